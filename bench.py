@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark one data-parallel worker's full SGD step on one MI355X.
+
+A step is compute_gradient (forward, softmax-CE, backward through every
+layer) + accumulate_grad into an empty GradBuf + apply_update, all through the
+C ABI on one stream, with inputs already resident in HBM.  The default
+workload is the 5000-unit MLP (fc 3072-5000x5-10, ReLU, softmax-CE, batch 512,
+momentum SGD mu = 0.9, eta = 0.01), synthetic inputs from the seeded
+generators, He-normal weights.
+
+Printed: one JSON line with images/s (value), the roofline of the dominant
+kernel (HIP-event durations of every launch inside the timed region,
+algorithmic flops per launch), per-kernel totals, the parameter-server Adagrad
+apply in GB/s, and the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+    python bench.py [--steps 50] [--warmup 5] [--workload mlp5000] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix (MFMA) peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "images/sec per fwd+bwd+update SGD step (fp32); GEMM MFMA util %, update GB/s"
+
+
+def describe(wl):
+    arch = {"mlp5000": "fc 3072-5000x5-10, ReLU, softmax-CE",
+            "lenet5": "LeNet-5 (conv5x5 6, pool, conv5x5 16, pool, fc 400-120-84-10)",
+            "vgg_cifar": "VGG-style 13 conv3x3 + 5 pool + fc 512-512-10 at 3x32x32",
+            "vgg16": "VGG-16 (13 conv3x3 + 5 pool + fc 25088-4096-4096-1000) at 3x224x224"}[wl.name]
+    rule = {"plain": f"plain SGD eta={wl.eta}", "momentum": f"momentum SGD mu={wl.mu} eta={wl.eta}",
+            "adagrad": f"Adagrad eta={wl.eta}"}[wl.rule]
+    return f"{wl.name}: {arch}, batch {wl.batch}, {rule}"
+
+
+def gpu_step_bench(wl, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sgd_cnns_amd as S
+    import workloads
+
+    dev = torch.device("cuda")
+    X, y, W = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    n = net.param_count()
+    Wd = torch.from_numpy(W).to(dev)
+    Xd = torch.from_numpy(X).to(dev)
+    yd = torch.from_numpy(y).to(dev)
+    grad = torch.empty(n, device=dev)
+    loss = torch.empty(1, device=dev)
+    ws = net.workspace(dev)
+    gb = S.GradBuf(n, device=dev)
+    state = None
+    if wl.rule == "momentum":
+        state = torch.zeros(n, device=dev)
+    elif wl.rule == "adagrad":
+        state = torch.full((n,), 0.1, device=dev)
+    rule = S.Rule(wl.rule, wl.eta, wl.mu, wl.eps)
+    stream = torch.cuda.current_stream()
+
+    upd_events = []
+
+    def step(record=False):
+        net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            S.accumulate_grad(gb, grad, stream)
+            e[1].record(stream)
+            S.apply_update(Wd, gb, state, rule, stream)
+            e[2].record(stream)
+            upd_events.append(e)
+        else:
+            S.accumulate_grad(gb, grad, stream)
+            S.apply_update(Wd, gb, state, rule, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    net.profile(True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        step(record=True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    net.profile(False)
+    total_ms = t0.elapsed_time(t1)
+    recs = net.profile_read()
+    loss_v = float(loss.item())
+    if not np.isfinite(loss_v):
+        raise RuntimeError(f"non-finite loss {loss_v}")
+
+    # per-kernel totals over the timed region
+    kern = {}
+    for (name, layer, phase, ms, flops, nbytes) in recs:
+        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        k["launches"] += 1
+        k["ms"] += ms
+        k["flops"] += flops
+        k["bytes"] += nbytes
+    acc_b = 8.0 * n            # empty GradBuf: read grad, write buffer
+    upd_b = {"plain": 12.0, "momentum": 20.0, "adagrad": 20.0}[wl.rule] * n
+    acc_name, upd_name = "accumulate_copy", f"apply_{wl.rule}"
+    kern[acc_name] = {"launches": steps, "ms": sum(e[0].elapsed_time(e[1]) for e in upd_events), "flops": 0.0,
+                      "bytes": acc_b * steps}
+    kern[upd_name] = {"launches": steps, "ms": sum(e[1].elapsed_time(e[2]) for e in upd_events),
+                      "flops": {"plain": 2, "momentum": 4, "adagrad": 7}[wl.rule] * n * steps,
+                      "bytes": upd_b * steps}
+    return dict(total_ms=total_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n)
+
+
+def ps_apply_bench(steps=100, pool=16):
+    """Parameter-server apply: 138,357,544 params, K = 8 buffers left-folded + Adagrad, fresh buffers per step."""
+    import torch
+
+    import sgd_cnns_amd as S
+    import workloads
+
+    ps = workloads.PS_APPLY
+    n, k = ps["n"], ps["k"]
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(ps["seed"])
+    W = torch.randn(n, device=dev, generator=g)
+    A = torch.full((n,), ps["acc0"], device=dev)
+    bufs = [torch.randn(n, device=dev, generator=g) * ps["grad_std"] for _ in range(pool)]
+    rule = S.Rule("adagrad", ps["eta"], 0.0, ps["eps"])
+    stream = torch.cuda.current_stream()
+    evs = []
+    for s in range(steps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        S.apply_fused(W, A, [bufs[(k * s + i) % pool] for i in range(k)], rule, stream)
+        e1.record(stream)
+        if s >= 2:
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    nbytes = (k + 4) * 4.0 * n
+    del bufs
+    return {"workload": f"{n} params, K={k} gradient buffers (fresh each step, pool {pool}) left-folded + Adagrad",
+            "kernel": "apply_fused_adagrad", "ms_per_step": ms, "bytes_per_step": nbytes,
+            "GB/s": nbytes / ms / 1e6, "frac_of_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS, "steps": steps}
+
+
+def cpu_baseline(wl, sample):
+    """The CPU oracle on a bounded sample: gradient of `sample` images + a full accumulate + apply."""
+    import numpy as np
+
+    import oracle as O
+    import workloads
+
+    X, y, W = workloads.make_inputs(wl)
+    net = O.OracleNet(wl.chw, wl.layers)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    _, g = net.gradient(W, X[:sample], y[:sample])
+    t_grad = time.perf_counter() - t0
+    gb = O.GradBuf(W.size)
+    state = np.zeros_like(W) if wl.rule != "adagrad" else np.full_like(W, 0.1)
+    t0 = time.perf_counter()
+    gb.accumulate(g)
+    O.apply_rule(wl.rule, W, state, gb.data, wl.eta, wl.mu, wl.eps)
+    t_upd = time.perf_counter() - t0
+    t_step = t_grad * wl.batch / sample + t_upd
+    return {"value": wl.batch / t_step, "unit": "images/s", "cores": cores, "kind": "oracle",
+            "sample": (f"gradient of the first {sample} of {wl.batch} images ({t_grad:.1f} s) scaled per image to the "
+                       f"full batch, plus one accumulate+apply over all {W.size} parameters ({t_upd:.2f} s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mlp5000", choices=["mlp5000", "lenet5", "vgg_cifar", "vgg16"])
+    ap.add_argument("--cpu-sample", type=int, default=0, help="images in the oracle sample (0 = per workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ps-apply", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}); the multi-GPU path is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import workloads
+    wl = workloads.WORKLOADS[args.workload]
+    print(f"[bench] {describe(wl)}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    r = gpu_step_bench(wl, args.steps, args.warmup)
+    ms_step = r["total_ms"] / args.steps
+    value = wl.batch * args.steps / (r["total_ms"] / 1e3)
+    kern = r["kern"]
+    gemms = {k: v for k, v in kern.items() if k.startswith("gemm_")}
+    dom = max(gemms, key=lambda k: gemms[k]["ms"])
+    d = gemms[dom]
+    achieved = d["flops"] / (d["ms"] / 1e3) / 1e12
+    g_flops = sum(v["flops"] for v in gemms.values())
+    g_ms = sum(v["ms"] for v in gemms.values())
+    upd = kern[f"apply_{wl.rule}"]
+    kernels = []
+    for name, v in sorted(kern.items(), key=lambda kv: -kv[1]["ms"]):
+        e = {"kernel": name, "launches": v["launches"], "avg_us": 1e3 * v["ms"] / v["launches"],
+             "share_of_step": v["ms"] / r["total_ms"]}
+        if v["flops"] and name.startswith("gemm_"):
+            e["TFLOP/s"] = v["flops"] / (v["ms"] / 1e3) / 1e12
+            e["frac_fp32_peak"] = e["TFLOP/s"] / PEAK_FP32_TFLOPS
+        if v["bytes"]:
+            e["GB/s"] = v["bytes"] / (v["ms"] / 1e3) / 1e9
+            e["frac_hbm_peak"] = e["GB/s"] / PEAK_HBM_GBS
+        kernels.append(e)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox inputs of the workload's shape; He-normal random-init weights)",
+        "config": {"workload": describe(wl), "global_batch": wl.batch, "params": r["n_params"],
+                   "update": wl.rule},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "launches": d["launches"], "avg_launch_us": 1e3 * d["ms"] / d["launches"],
+                     "flops_per_launch": d["flops"] / d["launches"]},
+        "gemm_mfma_util": {"achieved_TFLOP/s": g_flops / (g_ms / 1e3) / 1e12,
+                           "frac_fp32_peak": g_flops / (g_ms / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
+                           "share_of_step": g_ms / r["total_ms"]},
+        "update_GB/s": {"kernel": f"apply_{wl.rule}", "GB/s": upd["bytes"] / (upd["ms"] / 1e3) / 1e9,
+                        "frac_hbm_peak": upd["bytes"] / (upd["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "kernels": kernels,
+        "loss_last_step": r["loss"],
+    }
+    if not args.no_ps_apply:
+        print("[bench] parameter-server apply", file=sys.stderr, flush=True)
+        out["ps_apply"] = ps_apply_bench()
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or {"mlp5000": 96, "lenet5": 16, "vgg_cifar": 8, "vgg16": 1}[wl.name]
+        print(f"[bench] CPU oracle baseline on {sample} images", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, sample)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

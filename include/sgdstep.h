@@ -1,0 +1,249 @@
+/*
+ * sgdstep.h -- C ABI of one data-parallel worker's minibatch SGD step on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step follows the SPRINT report (IPSJ SIG Technical Report
+ * Vol.2016-HPC-155 No.8): a worker computes the gradient of one sub-batch
+ * (Algorithm 1, ComputeGradient, realised as im2col plus matrix products per
+ * the section 3.3 SGEMM table), adds it into its gradient buffer GradBuf, and
+ * the buffers are summed and applied to the weights (Algorithm 2, with
+ * momentum), or applied by a parameter server with a per-parameter Adagrad
+ * rate (DistBelief review: w' = w - eta_i * dw).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are caller-owned device memory (float32 unless stated).  The
+ *    library allocates no device memory; it owns only the host-side net
+ *    handle.  Pointers are plain device addresses.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    kernels on it and return after launch; they never synchronise.  The
+ *    caller synchronises before reading results.
+ *  - Return value: SGD_OK (0) or a negative SGD_E* code.  The status covers
+ *    argument, shape and launch errors only.  sgd_last_error() returns a
+ *    thread-local message for the last failure.  Nothing throws across the ABI.
+ *  - Results are deterministic: no floating-point atomics; every reduction
+ *    has a fixed order, so two identical calls give bitwise-identical outputs.
+ *  - NaN in inputs or weights propagates to the loss and gradients (ReLU
+ *    passes NaN through); it is not an error.
+ */
+#ifndef SGDSTEP_H
+#define SGDSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define SGD_OK 0
+#define SGD_EINVAL (-1)       /* null pointer, bad enum, bad size            */
+#define SGD_ESHAPE (-2)       /* layer list does not describe a valid net   */
+#define SGD_EWORKSPACE (-3)   /* workspace smaller than sgd_workspace_bytes */
+#define SGD_EDEVICE (-4)      /* a HIP launch or query failed               */
+#define SGD_EUNSUPPORTED (-5) /* valid request outside what is implemented  */
+
+/* ---- layer kinds ---- */
+#define SGD_CONV 1       /* out = out channels, kernel = c, pad = zero padding P; stride 1 */
+#define SGD_RELU 2       /* must directly follow SGD_CONV or SGD_FC                        */
+#define SGD_MAXPOOL 3    /* pool = p: p x p windows, stride p; p must divide H and W       */
+#define SGD_FC 4         /* out = output width                                             */
+#define SGD_SOFTMAX_CE 5 /* last layer; must directly follow an SGD_FC without ReLU        */
+
+/* ---- loss reduction over the sub-batch ---- */
+#define SGD_REDUCE_MEAN 0 /* loss and gradient scaled by 1/N (Chainer's softmax_cross_entropy) */
+#define SGD_REDUCE_SUM 1  /* unscaled sum over samples (SPRINT eq. (1) sums per-sample grads)  */
+
+/* ---- update rules ---- */
+#define SGD_PLAIN 0    /* W = W - eta*G                          (SPRINT eq. (1))           */
+#define SGD_MOMENTUM 1 /* V = mu*V - eta*G; W = W + V            (SPRINT Algorithm 2, nu=mu) */
+#define SGD_ADAGRAD 2  /* A = A + G*G; W = W - (eta/(sqrt(A)+eps))*G  (DistBelief review)   */
+
+/* ---- tensor-info selectors (sgd_tensor_info) ---- */
+#define SGD_T_OUT 0    /* forward output of the layer                                  */
+#define SGD_T_DOUT 1   /* gradient of the loss: for conv/fc w.r.t. the pre-activation  */
+                       /* (ReLU derivative applied), for maxpool w.r.t. its output     */
+#define SGD_T_COL 2    /* conv only: im2col matrix (overwritten by dCol in backward)   */
+#define SGD_T_WREP 3   /* conv only: weights repacked to [Co][ky][kx][ci]               */
+#define SGD_T_ARGMAX 4 /* maxpool only: uint8 window-local argmax ky*p+kx              */
+
+/* ---- tensor layouts reported by sgd_tensor_info ---- */
+#define SGD_LAYOUT_NHWC 1 /* dims = {N, H, W, C}                                      */
+#define SGD_LAYOUT_NCHW 2 /* dims = {N, C, H, W}                                      */
+#define SGD_LAYOUT_ROWS 3 /* dims = {rows, cols, row stride, 1}, row-major             */
+
+typedef struct sgd_layer {
+  int kind;   /* SGD_CONV ... SGD_SOFTMAX_CE                 */
+  int out;    /* conv: output channels; fc: output width     */
+  int kernel; /* conv: filter width c                        */
+  int pad;    /* conv: zero padding P on each side           */
+  int pool;   /* maxpool: window p                           */
+} sgd_layer;
+
+typedef struct sgd_input {
+  int batch;    /* N_Subbatch                                 */
+  int channels; /* m_0 (an MLP input is channels=width, h=w=1) */
+  int height;
+  int width;
+} sgd_input;
+
+typedef struct sgd_net sgd_net;
+
+/*
+ * Plan a network (host only; no device call).  Shapes follow SPRINT section
+ * 3.2 eq. (2), generalised to zero padding: a conv layer maps H to
+ * H + 2P - c + 1, a pool layer divides by p, an fc layer flattens its input in
+ * (c, h, w) order.  `layers` is copied.  On success *out receives a handle to
+ * free with sgd_destroy_net.  Errors: SGD_EINVAL (null pointer, n_layers < 2,
+ * bad reduction), SGD_ESHAPE (non-positive sizes, pool not dividing the map,
+ * conv output < 1, no final SGD_SOFTMAX_CE), SGD_EUNSUPPORTED (ReLU not after
+ * conv/fc, conv after fc, softmax not after an fc).
+ */
+int sgd_create_net(const sgd_input* input, const sgd_layer* layers, int n_layers, int reduction,
+                   sgd_net** out);
+void sgd_destroy_net(sgd_net* net);
+
+/*
+ * Number of parameters, SPRINT section 3.2 eq. (3):
+ *   sum over conv layers of m_l (c^2 m_{l-1} + 1) + sum over fc layers of
+ *   m_l (x_{l-1}^2 m_{l-1} + 1).
+ * The flat parameter vector W (and every gradient) has this length and holds,
+ * per weighted layer in network order, the weight (conv [Co][Ci][c][c], fc
+ * [out][in]) followed by the bias.  Returns -1 for a null net.
+ */
+int64_t sgd_param_count(const sgd_net* net);
+
+/*
+ * Element offsets of each weighted layer's weight and bias inside the flat
+ * vector, in network order.  Writes min(count, max_layers) entries and
+ * returns the number of weighted layers (or a negative error).
+ */
+int sgd_param_offsets(const sgd_net* net, int64_t* w_off, int64_t* b_off, int max_layers);
+
+/* Bytes of device workspace sgd_compute_gradient needs (0 for a null net). */
+size_t sgd_workspace_bytes(const sgd_net* net);
+
+/*
+ * Where a layer's intermediate tensor lives inside the workspace after
+ * sgd_compute_gradient: byte offset, dims (see SGD_LAYOUT_*) and layout.
+ * `layer` indexes the layer list given to sgd_create_net (a ReLU entry
+ * reports the tensors of the conv/fc it follows).  Returns SGD_OK, or
+ * SGD_EINVAL if that layer has no such tensor.  For inspection and tests.
+ */
+int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offset, int64_t dims[4],
+                    int* layout);
+
+/*
+ * One sub-batch gradient (SPRINT Algorithm 1, Grad = ComputeGradient(Weights)).
+ *  W     [param_count] weights, flat layout above.
+ *  X     [N][C][H][W] images, float32, NCHW.
+ *  y     [N] int32 labels in [0, classes); out-of-range labels are caller error
+ *        (not checked on the device).
+ *  grad  [param_count] output: the full gradient (every element written).
+ *  loss  device float scalar output: softmax cross-entropy, reduced per the
+ *        net's reduction.
+ *  ws    device workspace of at least sgd_workspace_bytes(net) bytes,
+ *        256-byte aligned; its contents on entry do not matter.
+ * The kernel sequence is: forward (im2col + GEMM + bias/ReLU + maxpool per
+ * conv layer, GEMM + bias/ReLU per fc layer), softmax-CE, then backward in
+ * reverse layer order with the dedw, dedb, dedx_fc and dedx_conv products of
+ * SPRINT's section 3.3 table (dedx_conv followed by col2im).  No dedx is
+ * computed for the first weighted layer.  Errors: SGD_EINVAL (null pointer),
+ * SGD_EWORKSPACE, SGD_EDEVICE.
+ */
+int sgd_compute_gradient(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad,
+                         float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A worker's gradient buffer with SPRINT's empty state (Algorithms 1 and 2).
+ * `data` is device memory of n floats; `empty` is kept on the host.
+ */
+typedef struct sgd_gradbuf {
+  float* data;
+  int64_t n;
+  int empty;
+} sgd_gradbuf;
+
+/*
+ * GradBuf <- grad if the buffer is empty, else GradBuf + grad (SPRINT
+ * Algorithm 1, the GradBuf update).  Clears `empty`.  grad has gb->n floats.
+ * Errors: SGD_EINVAL, SGD_EDEVICE.
+ */
+int sgd_accumulate_grad(sgd_gradbuf* gb, const float* grad, void* stream);
+
+/*
+ * Fold k gradients into the buffer in index order, as SPRINT Algorithm 2
+ * folds GradBuf_1..GradBuf_N into SendBuf: the first is copied if the buffer
+ * is empty, every later one added, one rounding per addition.  `grads` is a
+ * host array of k device pointers; 1 <= k <= 16.  Errors: SGD_EINVAL,
+ * SGD_EDEVICE.
+ */
+int sgd_accumulate_grads(sgd_gradbuf* gb, const float* const* grads, int k, void* stream);
+
+typedef struct sgd_rule {
+  int rule;  /* SGD_PLAIN, SGD_MOMENTUM or SGD_ADAGRAD */
+  float eta; /* learning rate                          */
+  float mu;  /* momentum coefficient (SGD_MOMENTUM)    */
+  float eps; /* Adagrad denominator offset             */
+} sgd_rule;
+
+/*
+ * Apply the buffered gradient G to W in place, elementwise, one rounding per
+ * statement in this order (no fused multiply-add; correctly rounded sqrt and
+ * division):
+ *   plain:    t = eta*G;  W = W - t
+ *   momentum: t1 = mu*V; t2 = eta*G; V = t1 - t2; W = W + V
+ *   adagrad:  A = A + G*G; d = sqrt(A) + eps; r = eta/d; t = r*G; W = W - t
+ * `state` is V (momentum) or A (Adagrad), n = gb->n floats; NULL for plain.
+ * An empty GradBuf is a zero gradient (SPRINT Algorithm 2 sends 0 when the
+ * first buffer is empty): plain and Adagrad then leave W unchanged, momentum
+ * still decays V.  Marks the buffer empty afterwards.  Errors: SGD_EINVAL,
+ * SGD_EDEVICE.
+ */
+int sgd_apply_update(float* W, sgd_gradbuf* gb, float* state, const sgd_rule* rule, void* stream);
+
+/*
+ * One pass that sums k gradient buffers in index order (a left fold, one
+ * rounding per addition) and applies the rule, as the parameter server's
+ * SumGradient + update of SPRINT Algorithm 2; bitwise equal to
+ * sgd_accumulate_grads into an empty buffer followed by sgd_apply_update.
+ * `grads` is a host array of k device pointers, 1 <= k <= 16, each n floats.
+ * Errors: SGD_EINVAL, SGD_EDEVICE.
+ */
+int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, int64_t n,
+                    const sgd_rule* rule, void* stream);
+
+/*
+ * Per-launch kernel timing, for measurement.  While enabled, every kernel
+ * sgd_compute_gradient launches is bracketed by a HIP event pair on the
+ * caller's stream, and its algorithmic work is recorded: flops of the
+ * arithmetic the method needs (2mnk for a product of the SPRINT section 3.3
+ * table, with k the unpadded reduction length) and bytes it must move
+ * through HBM (each operand read once, each result written once).
+ *
+ * sgd_profile(net, 1) clears the records and starts recording; (net, 0)
+ * stops.  sgd_profile_read waits for the recorded events, copies up to
+ * max_records entries to `out` (in launch order) and returns the number of
+ * records.  `kernel` points to a static string.  Errors: SGD_EINVAL,
+ * SGD_EDEVICE.
+ */
+typedef struct sgd_kernel_time {
+  const char* kernel; /* e.g. "gemm_64x128_nt", "im2col", "softmax_ce"     */
+  int layer;          /* index in the layer list, -1 for an inserted stage */
+  int phase;          /* 0 forward, 1 backward                              */
+  double ms;          /* event-measured duration of the launch              */
+  double flops;       /* algorithmic floating-point operations              */
+  double bytes;       /* algorithmic HBM bytes                              */
+} sgd_kernel_time;
+
+int sgd_profile(sgd_net* net, int enable);
+int sgd_profile_read(sgd_net* net, sgd_kernel_time* out, int max_records);
+
+/* Thread-local message describing the last failed call ("" if none). */
+const char* sgd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGDSTEP_H */

@@ -200,11 +200,13 @@ double or_conv_dx_point(int N, int Ci, int H, int W, int Co, int c, int P,
 
 /* ------------------------------------------------------------------------ */
 /* ReLU, as used after every hidden layer (the Chainer MLP applies F.relu   */
-/* after each Linear but the last).  Derivative taken as 0 at 0.            */
+/* after each Linear but the last).  Derivative taken as 0 at 0.  The pages */
+/* define it on numbers only; here a NaN input stays NaN (it is not <= 0),  */
+/* so a diverged step shows up in the loss instead of being zeroed.         */
 /* ------------------------------------------------------------------------ */
 void or_relu_fwd(int64_t n, const real* y, real* a) {
 #pragma omp parallel for
-  for (int64_t i = 0; i < n; ++i) a[i] = y[i] > (real)0 ? y[i] : (real)0;
+  for (int64_t i = 0; i < n; ++i) a[i] = y[i] <= (real)0 ? (real)0 : y[i];
 }
 
 /* dy = da where the forward output a was positive, else 0. */

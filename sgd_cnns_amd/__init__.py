@@ -1,0 +1,269 @@
+"""Python binding of libsgdstep (include/sgdstep.h): argument marshalling only.
+
+Every step of the SGD step runs in the HIP library; this module converts
+torch device tensors to raw pointers and calls the C ABI through ctypes.
+PyTorch provides device memory and streams only.  If the library is not
+built, or no GPU is present, the compute entry points raise: there is no CPU
+fallback.
+
+    import sgd_cnns_amd as S
+    net = S.Net((N, C, H, W), layers)           # layers as in workloads/
+    ws = net.workspace()                        # torch.uint8 device buffer
+    net.compute_gradient(W, X, y, grad, loss, ws)
+    gb = S.GradBuf(grad.numel(), device="cuda")
+    S.accumulate_grad(gb, grad)
+    S.apply_update(W, gb, state, S.Rule("momentum", eta=0.01, mu=0.9))
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgdstep.so")
+
+# Constants of include/sgdstep.h
+OK, EINVAL, ESHAPE, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+CONV, RELU, MAXPOOL, FC, SOFTMAX_CE = 1, 2, 3, 4, 5
+REDUCE_MEAN, REDUCE_SUM = 0, 1
+PLAIN, MOMENTUM, ADAGRAD = 0, 1, 2
+T_OUT, T_DOUT, T_COL, T_WREP, T_ARGMAX = 0, 1, 2, 3, 4
+LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
+
+EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
+           "sgd_tensor_info", "sgd_compute_gradient", "sgd_accumulate_grad", "sgd_accumulate_grads",
+           "sgd_apply_update", "sgd_apply_fused", "sgd_profile", "sgd_profile_read", "sgd_last_error"]
+
+
+class SgdLayer(C.Structure):
+    _fields_ = [("kind", C.c_int), ("out", C.c_int), ("kernel", C.c_int), ("pad", C.c_int), ("pool", C.c_int)]
+
+
+class SgdInput(C.Structure):
+    _fields_ = [("batch", C.c_int), ("channels", C.c_int), ("height", C.c_int), ("width", C.c_int)]
+
+
+class SgdGradBuf(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("n", C.c_int64), ("empty", C.c_int)]
+
+
+class SgdRule(C.Structure):
+    _fields_ = [("rule", C.c_int), ("eta", C.c_float), ("mu", C.c_float), ("eps", C.c_float)]
+
+
+class SgdKernelTime(C.Structure):
+    _fields_ = [("kernel", C.c_char_p), ("layer", C.c_int), ("phase", C.c_int), ("ms", C.c_double),
+                ("flops", C.c_double), ("bytes", C.c_double)]
+
+
+class SgdError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libsgdstep.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or sgd_cnns_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        P, i, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+        sig = {
+            "sgd_create_net": (i, [C.POINTER(SgdInput), C.POINTER(SgdLayer), i, i, C.POINTER(P)]),
+            "sgd_destroy_net": (None, [P]),
+            "sgd_param_count": (i64, [P]),
+            "sgd_param_offsets": (i, [P, C.POINTER(i64), C.POINTER(i64), i]),
+            "sgd_workspace_bytes": (sz, [P]),
+            "sgd_tensor_info": (i, [P, i, i, C.POINTER(i64), C.POINTER(i64), C.POINTER(i)]),
+            "sgd_compute_gradient": (i, [P, P, P, P, P, P, P, sz, P]),
+            "sgd_accumulate_grad": (i, [C.POINTER(SgdGradBuf), P, P]),
+            "sgd_accumulate_grads": (i, [C.POINTER(SgdGradBuf), C.POINTER(P), i, P]),
+            "sgd_apply_update": (i, [P, C.POINTER(SgdGradBuf), P, C.POINTER(SgdRule), P]),
+            "sgd_apply_fused": (i, [P, P, C.POINTER(P), i, i64, C.POINTER(SgdRule), P]),
+            "sgd_profile": (i, [P, i]),
+            "sgd_profile_read": (i, [P, C.POINTER(SgdKernelTime), i]),
+            "sgd_last_error": (C.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != OK:
+        raise SgdError(rc, lib().sgd_last_error().decode())
+    return rc
+
+
+def _require_cuda(*tensors):
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("sgd_cnns_amd compute calls need a ROCm GPU (no CPU fallback)")
+    for t in tensors:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+_KIND = {"conv": CONV, "relu": RELU, "pool": MAXPOOL, "fc": FC, "softmax_ce": SOFTMAX_CE}
+
+
+def to_layers(layers):
+    """Convert ("conv", out, c, pad) / ("relu",) / ("pool", p) / ("fc", out) / ("softmax_ce",) tuples."""
+    arr = (SgdLayer * len(layers))()
+    for j, L in enumerate(layers):
+        k = _KIND[L[0]]
+        a = arr[j]
+        a.kind = k
+        if k == CONV:
+            a.out, a.kernel, a.pad = L[1], L[2], L[3]
+        elif k == MAXPOOL:
+            a.pool = L[1]
+        elif k == FC:
+            a.out = L[1]
+    return arr
+
+
+class Net:
+    """A planned network (sgd_create_net)."""
+
+    def __init__(self, nchw, layers, reduce_sum=False):
+        L = lib()
+        inp = SgdInput(*[int(v) for v in nchw])
+        arr = to_layers(layers)
+        h = C.c_void_p()
+        _check(L.sgd_create_net(C.byref(inp), arr, len(layers), REDUCE_SUM if reduce_sum else REDUCE_MEAN,
+                                C.byref(h)))
+        self._h = h
+        self.nchw = tuple(nchw)
+        self.layers = list(layers)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.sgd_destroy_net(h)
+            self._h = None
+
+    def param_count(self):
+        return lib().sgd_param_count(self._h)
+
+    def param_offsets(self):
+        n = lib().sgd_param_offsets(self._h, None, None, 0)
+        if n < 0:
+            _check(n)
+        w = (C.c_int64 * n)()
+        b = (C.c_int64 * n)()
+        lib().sgd_param_offsets(self._h, w, b, n)
+        return list(w), list(b)
+
+    def workspace_bytes(self):
+        return lib().sgd_workspace_bytes(self._h)
+
+    def tensor_info(self, layer, which):
+        off = C.c_int64()
+        dims = (C.c_int64 * 4)()
+        lay = C.c_int()
+        _check(lib().sgd_tensor_info(self._h, layer, which, C.byref(off), dims, C.byref(lay)))
+        return off.value, tuple(dims), lay.value
+
+    def workspace(self, device="cuda"):
+        import torch
+        return torch.empty(self.workspace_bytes(), dtype=torch.uint8, device=device)
+
+    def view(self, ws, layer, which):
+        """A torch view of a workspace tensor (float32, or uint8 for T_ARGMAX)."""
+        import torch
+        off, dims, lay = self.tensor_info(layer, which)
+        if lay == LAYOUT_ROWS:
+            shape = (dims[0], dims[2])   # rows x row stride; logical columns are dims[1]
+        else:
+            shape = dims
+        n = 1
+        for d in shape:
+            n *= d
+        if which == T_ARGMAX:
+            return ws[off:off + n].view(shape)
+        return ws[off:off + 4 * n].view(torch.float32).view(shape)
+
+    def profile(self, enable):
+        """Start (clearing old records) or stop per-launch kernel timing."""
+        _check(lib().sgd_profile(self._h, 1 if enable else 0))
+
+    def profile_read(self):
+        """[(kernel, layer, phase, ms, flops, bytes)] for every recorded launch."""
+        n = lib().sgd_profile_read(self._h, None, 0)
+        if n < 0:
+            _check(n)
+        arr = (SgdKernelTime * max(n, 1))()
+        m = lib().sgd_profile_read(self._h, arr, n)
+        if m < 0:
+            _check(m)
+        return [(r.kernel.decode(), r.layer, r.phase, r.ms, r.flops, r.bytes) for r in arr[:n]]
+
+    def compute_gradient(self, W, X, y, grad, loss, ws, stream=None):
+        _require_cuda(W, X, y, grad, loss, ws)
+        _check(lib().sgd_compute_gradient(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(grad), _ptr(loss), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class GradBuf:
+    """A device gradient buffer with the host-side empty flag."""
+
+    def __init__(self, n, device="cuda", data=None):
+        import torch
+        self.data = data if data is not None else torch.empty(n, dtype=torch.float32, device=device)
+        self._c = SgdGradBuf(self.data.data_ptr(), n, 1)
+
+    @property
+    def empty(self):
+        return bool(self._c.empty)
+
+    @empty.setter
+    def empty(self, v):
+        self._c.empty = 1 if v else 0
+
+
+def accumulate_grad(gb, grad, stream=None):
+    _require_cuda(gb.data, grad)
+    _check(lib().sgd_accumulate_grad(C.byref(gb._c), _ptr(grad), _stream(stream)))
+
+
+def accumulate_grads(gb, grads, stream=None):
+    _require_cuda(gb.data, *grads)
+    arr = (C.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
+    _check(lib().sgd_accumulate_grads(C.byref(gb._c), arr, len(grads), _stream(stream)))
+
+
+_RULES = {"plain": PLAIN, "momentum": MOMENTUM, "adagrad": ADAGRAD}
+
+
+def Rule(rule, eta, mu=0.0, eps=0.0):
+    return SgdRule(_RULES[rule] if isinstance(rule, str) else rule, eta, mu, eps)
+
+
+def apply_update(W, gb, state, rule, stream=None):
+    _require_cuda(W, gb.data, state)
+    _check(lib().sgd_apply_update(_ptr(W), C.byref(gb._c), _ptr(state), C.byref(rule), _stream(stream)))
+
+
+def apply_fused(W, state, grads, rule, stream=None):
+    _require_cuda(W, state, *grads)
+    arr = (C.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
+    _check(lib().sgd_apply_fused(_ptr(W), _ptr(state), arr, len(grads), W.numel(), C.byref(rule), _stream(stream)))

@@ -1,0 +1,75 @@
+// Internal helpers shared by the HIP sources of libsgdstep (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "sgdstep.h"
+
+namespace sgd {
+
+// Thread-local error text behind sgd_last_error().
+void set_error(const std::string& msg);
+
+// Records `what` plus the pending HIP error (if any) and returns SGD_EDEVICE,
+// or returns 0 when the last launch succeeded.
+int check_launch(const char* what);
+
+// Optional per-launch timing (sgd_profile).  When a profiler is active on
+// the calling thread, every launcher brackets its kernel with a HIP event
+// pair and records the launch's algorithmic flops and HBM bytes.
+void prof_begin(const char* kernel, double flops, double bytes, hipStream_t s);
+void prof_end(hipStream_t s);
+void prof_set_layer(int layer, int phase);
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// ---------------------------------------------------------------- GEMM ----
+// C[M][N] = op(A) * op(B) in fp32 on the matrix cores.
+//   a_t == false: A stored [M][K] (row stride lda);  true: stored [K][M].
+//   b_t == false: B stored [N][K] (row stride ldb);  true: stored [K][N].
+// The epilogue is applied to each fp32 result v at (row, col):
+enum Epilogue : int {
+  EPI_STORE = 0,      // C = v
+  EPI_BIAS = 1,       // C = v + bias[col]
+  EPI_BIAS_RELU = 2,  // C = max(v + bias[col], 0)
+  EPI_MASK = 3,       // C = mask[row*ldm + col] > 0 ? v : 0   (ReLU derivative)
+  EPI_ACCUM = 4,      // C = C + v
+};
+
+struct GemmDesc {
+  const float* A;
+  const float* B;
+  float* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  bool a_t, b_t;
+  int epi;
+  const float* bias;
+  const float* mask;
+  int64_t ldm;
+  // Split-K: when splits > 1 the products of each K slice go to
+  // partial[s][M][N] (row stride N) and a second pass sums the slices in
+  // order s = 0..splits-1 before the epilogue.  `partial` must then hold
+  // splits*M*N floats.
+  int splits;
+  float* partial;
+  // Conv weight-gradient store: when perm_c > 0 the final value for
+  // (row = co, col = kk) with kk = (ky*c + kx)*Ci + ci is written to
+  // C[co*ldc + ci*c*c + ky*c + kx] (only kk < perm_k are stored).
+  int perm_c, perm_ci, perm_k;
+  // Algorithmic flops for profiling (0: 2*M*N*K).  Conv products pass the
+  // unpadded reduction length here.
+  double flops;
+};
+
+int gemm(const GemmDesc& d, hipStream_t s);
+
+// Heuristic split count for a product (>= 1), given the slice floor.
+int gemm_pick_splits(int M, int N, int K);
+
+}  // namespace sgd

@@ -1,0 +1,29 @@
+// Host launchers of the layer kernels (internal; see layers.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sgd {
+
+int im2col(const float* x, bool x_nchw, float* col, int N, int Ci, int H, int W, int c, int P, int Ho, int Wo,
+           int ldk, hipStream_t s);
+int col2im(const float* dcol, const float* mask_act, float* dx, int N, int Ci, int H, int W, int c, int P, int Ho,
+           int Wo, int ldk, hipStream_t s);
+int repack_weight(const float* w, float* wrep, int Co, int Ci, int c, int ldk, hipStream_t s);
+int maxpool_fwd(const float* x, float* y, uint8_t* argmax, int N, int C, int H, int W, int p, bool out_nchw,
+                hipStream_t s);
+int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, float* dx, int N, int C, int H, int W,
+                int p, bool out_nchw, hipStream_t s);
+int64_t colsum_scratch_floats(int64_t rows, int cols);
+int colsum(const float* dy, float* db, float* scratch, int64_t rows, int cols, hipStream_t s);
+int softmax_ce(const float* z, const int32_t* y, float* dz, float* row_loss, float* loss, int N, int C,
+               float scale, hipStream_t s);
+
+// update.hip
+int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy, int64_t n, hipStream_t s);
+int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t n, int rule, float eta, float mu,
+               float eps, hipStream_t s);
+
+}  // namespace sgd

@@ -1,0 +1,410 @@
+// Bandwidth-bound layer kernels of the SGD step: im2col / col2im, weight
+// repacking, max-pooling forward and backward, the bias-gradient (dedb)
+// column reduction and softmax cross-entropy.
+//
+// Activation layout.  Every activation the library produces is NHWC
+// (channels fastest), which is the natural row layout of the conv forward
+// product (rows = pixels, columns = output channels).  Only the caller's
+// images are NCHW, and the tensor feeding the first fc layer is written in
+// NCHW order so that the fc input is flattened in (c, h, w) order.
+//
+// im2col column order is (ky, kx, ci): a row of the im2col matrix is c*c runs
+// of Ci contiguous channels, so both its reads (NHWC) and writes are
+// contiguous.  The weights are repacked to the same order once per step.
+#include "common.h"
+#include "layers.h"
+
+namespace sgd {
+namespace {
+
+constexpr int kBlock = 256;
+
+int grid_for(int64_t work) { return (int)std::min<int64_t>(std::max<int64_t>(ceil_div(work, kBlock), 1), 65536); }
+
+#define GRID_STRIDE(i, n) \
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (n); i += (int64_t)gridDim.x * blockDim.x)
+
+// ---------------------------------------------------------------- im2col ----
+// Col[p][kk] = x[n][iy][ix][ci] with p = (n, oy, ox), kk = (ky*c + kx)*Ci + ci,
+// iy = oy + ky - P, ix = ox + kx - P; 0 outside the image and for the pad
+// columns K <= kk < ldk.
+__global__ void im2col_nhwc_vec4(const float* __restrict__ x, float* __restrict__ col, int N, int Ci, int H,
+                                 int W, int c, int P, int Ho, int Wo, int ldk) {
+  const int cq = Ci / 4;
+  const int64_t per_row = (int64_t)c * c * cq;
+  const int64_t total = (int64_t)N * Ho * Wo * per_row;
+  GRID_STRIDE(i, total) {
+    const int64_t p = i / per_row;
+    const int r = (int)(i - p * per_row);
+    const int tap = r / cq, q = r - tap * cq;
+    const int ky = tap / c, kx = tap - ky * c;
+    const int ox = (int)(p % Wo);
+    const int64_t t = p / Wo;
+    const int oy = (int)(t % Ho);
+    const int n = (int)(t / Ho);
+    const int iy = oy + ky - P, ix = ox + kx - P;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (iy >= 0 && iy < H && ix >= 0 && ix < W)
+      v = *reinterpret_cast<const float4*>(x + (((int64_t)n * H + iy) * W + ix) * Ci + 4 * q);
+    *reinterpret_cast<float4*>(col + p * ldk + (int64_t)tap * Ci + 4 * q) = v;
+  }
+}
+
+template <bool NCHW>
+__global__ void im2col_scalar(const float* __restrict__ x, float* __restrict__ col, int N, int Ci, int H, int W,
+                              int c, int P, int Ho, int Wo, int ldk) {
+  const int K = c * c * Ci;
+  const int64_t total = (int64_t)N * Ho * Wo * ldk;
+  GRID_STRIDE(i, total) {
+    const int64_t p = i / ldk;
+    const int kk = (int)(i - p * ldk);
+    float v = 0.f;
+    if (kk < K) {
+      const int tap = kk / Ci, ci = kk - tap * Ci;
+      const int ky = tap / c, kx = tap - ky * c;
+      const int ox = (int)(p % Wo);
+      const int64_t t = p / Wo;
+      const int oy = (int)(t % Ho);
+      const int n = (int)(t / Ho);
+      const int iy = oy + ky - P, ix = ox + kx - P;
+      if (iy >= 0 && iy < H && ix >= 0 && ix < W)
+        v = NCHW ? x[(((int64_t)n * Ci + ci) * H + iy) * W + ix] : x[(((int64_t)n * H + iy) * W + ix) * Ci + ci];
+    }
+    col[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------- col2im ----
+// dx[n][iy][ix][ci] = sum over (ky, kx) in row-major order of
+// dcol[(n, iy - ky + P, ix - kx + P)][(ky*c + kx)*Ci + ci] (taps outside the
+// output map skipped), then multiplied by the ReLU derivative [a > 0] of the
+// conv's input activation when `a` is given.  A gather: each output is
+// written once, no atomics.
+__global__ void col2im_nhwc_vec4(const float* __restrict__ dcol, const float* __restrict__ a,
+                                 float* __restrict__ dx, int N, int Ci, int H, int W, int c, int P, int Ho, int Wo,
+                                 int ldk) {
+  const int cq = Ci / 4;
+  const int64_t total = (int64_t)N * H * W * cq;
+  GRID_STRIDE(i, total) {
+    const int q = (int)(i % cq);
+    const int64_t pix = i / cq;
+    const int ix = (int)(pix % W);
+    const int64_t t = pix / W;
+    const int iy = (int)(t % H);
+    const int n = (int)(t / H);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ky = 0; ky < c; ++ky) {
+      const int oy = iy - ky + P;
+      if (oy < 0 || oy >= Ho) continue;
+      for (int kx = 0; kx < c; ++kx) {
+        const int ox = ix - kx + P;
+        if (ox < 0 || ox >= Wo) continue;
+        const float4 v = *reinterpret_cast<const float4*>(
+            dcol + (((int64_t)n * Ho + oy) * Wo + ox) * ldk + (int64_t)(ky * c + kx) * Ci + 4 * q);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+    }
+    if (a) {
+      const float4 m = *reinterpret_cast<const float4*>(a + i * 4);
+      s.x = m.x > 0.f ? s.x : 0.f;
+      s.y = m.y > 0.f ? s.y : 0.f;
+      s.z = m.z > 0.f ? s.z : 0.f;
+      s.w = m.w > 0.f ? s.w : 0.f;
+    }
+    *reinterpret_cast<float4*>(dx + i * 4) = s;
+  }
+}
+
+__global__ void col2im_nhwc_scalar(const float* __restrict__ dcol, const float* __restrict__ a,
+                                   float* __restrict__ dx, int N, int Ci, int H, int W, int c, int P, int Ho,
+                                   int Wo, int ldk) {
+  const int64_t total = (int64_t)N * H * W * Ci;
+  GRID_STRIDE(i, total) {
+    const int ci = (int)(i % Ci);
+    const int64_t pix = i / Ci;
+    const int ix = (int)(pix % W);
+    const int64_t t = pix / W;
+    const int iy = (int)(t % H);
+    const int n = (int)(t / H);
+    float s = 0.f;
+    for (int ky = 0; ky < c; ++ky) {
+      const int oy = iy - ky + P;
+      if (oy < 0 || oy >= Ho) continue;
+      for (int kx = 0; kx < c; ++kx) {
+        const int ox = ix - kx + P;
+        if (ox < 0 || ox >= Wo) continue;
+        s += dcol[(((int64_t)n * Ho + oy) * Wo + ox) * ldk + (int64_t)(ky * c + kx) * Ci + ci];
+      }
+    }
+    if (a) s = a[i] > 0.f ? s : 0.f;
+    dx[i] = s;
+  }
+}
+
+// ------------------------------------------------------- weight repacking ----
+// wrep[co][(ky*c + kx)*Ci + ci] = w[co][ci][ky][kx]; pad columns set to 0.
+__global__ void repack_conv_weight(const float* __restrict__ w, float* __restrict__ wrep, int Co, int Ci, int c,
+                                   int ldk) {
+  const int K = c * c * Ci;
+  const int64_t total = (int64_t)Co * ldk;
+  GRID_STRIDE(i, total) {
+    const int co = (int)(i / ldk), kk = (int)(i - (int64_t)co * ldk);
+    float v = 0.f;
+    if (kk < K) {
+      const int tap = kk / Ci, ci = kk - tap * Ci;
+      v = w[((int64_t)co * Ci + ci) * c * c + tap];
+    }
+    wrep[i] = v;
+  }
+}
+
+// --------------------------------------------------------------- max pool ----
+// p x p windows, stride p, over NHWC input.  The window is scanned row-major
+// and a strict '>' keeps the first maximum; a NaN in the window makes the
+// output NaN.  argmax stores the window-local index ky*p + kx.  The output
+// (and argmax) is NHWC, or NCHW when out_nchw is set.
+__global__ void maxpool_fwd_kernel(const float* __restrict__ x, float* __restrict__ y,
+                                   uint8_t* __restrict__ argmax, int N, int C, int H, int W, int p, int out_nchw) {
+  const int Ho = H / p, Wo = W / p;
+  const int64_t total = (int64_t)N * Ho * Wo * C;
+  GRID_STRIDE(i, total) {
+    const int ch = (int)(i % C);
+    const int64_t t = i / C;
+    const int ox = (int)(t % Wo);
+    const int64_t t2 = t / Wo;
+    const int oy = (int)(t2 % Ho);
+    const int n = (int)(t2 / Ho);
+    const float* base = x + (((int64_t)n * H + oy * p) * W + ox * p) * C + ch;
+    float best = base[0];
+    int bi = 0;
+    bool nan = false;
+    for (int ky = 0; ky < p; ++ky)
+      for (int kx = 0; kx < p; ++kx) {
+        const float v = base[((int64_t)ky * W + kx) * C];
+        if (v != v) nan = true;
+        if (v > best) {
+          best = v;
+          bi = ky * p + kx;
+        }
+      }
+    const int64_t o = out_nchw ? (((int64_t)n * C + ch) * Ho + oy) * Wo + ox : i;
+    y[o] = nan ? __builtin_nanf("") : best;
+    argmax[o] = (uint8_t)bi;
+  }
+}
+
+// Gather form of the pooling backward pass: each input position takes the
+// window's gradient if it is the window's argmax, else 0.  When `pooled` is
+// given (the pool follows a ReLU) the result is also multiplied by the ReLU
+// derivative, which at the argmax equals [pooled > 0].  dx is NHWC; dy,
+// argmax and pooled use the forward output layout.
+__global__ void maxpool_bwd_kernel(const float* __restrict__ dy, const uint8_t* __restrict__ argmax,
+                                   const float* __restrict__ pooled, float* __restrict__ dx, int N, int C, int H,
+                                   int W, int p, int out_nchw) {
+  const int Ho = H / p, Wo = W / p;
+  const int64_t total = (int64_t)N * H * W * C;
+  GRID_STRIDE(i, total) {
+    const int ch = (int)(i % C);
+    const int64_t t = i / C;
+    const int ix = (int)(t % W);
+    const int64_t t2 = t / W;
+    const int iy = (int)(t2 % H);
+    const int n = (int)(t2 / H);
+    const int oy = iy / p, ox = ix / p;
+    const int local = (iy - oy * p) * p + (ix - ox * p);
+    const int64_t o = out_nchw ? (((int64_t)n * C + ch) * Ho + oy) * Wo + ox
+                               : (((int64_t)n * Ho + oy) * Wo + ox) * C + ch;
+    float g = 0.f;
+    if (argmax[o] == local) {
+      g = dy[o];
+      if (pooled && !(pooled[o] > 0.f)) g = 0.f;
+    }
+    dx[i] = g;
+  }
+}
+
+// -------------------------------------------------- bias gradient (dedb) ----
+// db[col] = sum over rows of dy[row][col], as two fixed-order passes: each
+// thread of pass 1 sums one column over a chunk of `chunk` rows; pass 2 adds
+// the chunk sums in chunk order.
+__global__ void colsum_partial(const float* __restrict__ dy, float* __restrict__ part, int64_t rows, int cols,
+                               int64_t chunk) {
+  const int64_t nchunks = ceil_div(rows, chunk);
+  const int64_t total = nchunks * cols;
+  GRID_STRIDE(i, total) {
+    const int64_t ch = i / cols;
+    const int col = (int)(i - ch * cols);
+    const int64_t r0 = ch * chunk, r1 = std::min<int64_t>(rows, r0 + chunk);
+    float s = 0.f;
+    for (int64_t r = r0; r < r1; ++r) s += dy[r * cols + col];
+    part[i] = s;
+  }
+}
+
+__global__ void colsum_final(const float* __restrict__ part, float* __restrict__ db, int64_t nchunks, int cols) {
+  GRID_STRIDE(col, (int64_t)cols) {
+    float s = part[col];
+    for (int64_t c = 1; c < nchunks; ++c) s += part[c * cols + col];
+    db[col] = s;
+  }
+}
+
+// ------------------------------------------------------ softmax + CE loss ----
+// One wavefront per sample row.  lse = m + log(sum exp(z - m)), the row loss
+// lse - z[y], and dz = scale * (exp(z - lse) - [j == y]).  Wavefront
+// reductions use a fixed butterfly, so results are deterministic.
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ void softmax_ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ y,
+                                  float* __restrict__ dz, float* __restrict__ row_loss, int N, int C, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float* zr = z + (int64_t)row * C;
+  float m = -INFINITY;
+  bool nan = false;
+  for (int j = lane; j < C; j += 64) {
+    const float v = zr[j];
+    nan |= (v != v);
+    m = fmaxf(m, v);
+  }
+  m = wave_max(m);
+  float se = 0.f;
+  for (int j = lane; j < C; j += 64) se += expf(zr[j] - m);
+  se = wave_sum(se);
+  nan = __any(nan);
+  const float lse = nan ? __builtin_nanf("") : m + logf(se);
+  const int lbl = y[row];
+  for (int j = lane; j < C; j += 64) dz[(int64_t)row * C + j] = scale * (expf(zr[j] - lse) - (j == lbl ? 1.f : 0.f));
+  if (lane == 0) row_loss[row] = lse - zr[lbl];
+}
+
+// loss = scale * sum of row losses, one block, fixed reduction tree.
+__global__ void loss_sum_kernel(const float* __restrict__ row_loss, float* __restrict__ loss, int N, float scale) {
+  __shared__ float sh[kBlock];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < N; i += kBlock) s += row_loss[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = kBlock / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = scale * sh[0];
+}
+
+}  // namespace
+
+int im2col(const float* x, bool x_nchw, float* col, int N, int Ci, int H, int W, int c, int P, int Ho, int Wo,
+           int ldk, hipStream_t s) {
+  const bool vec = !x_nchw && Ci % 4 == 0 && ldk == c * c * Ci;
+  prof_begin("im2col", 0, 4.0 * ((double)N * Ho * Wo * ldk + (double)N * Ci * H * W), s);
+  if (vec) {
+    const int64_t total = (int64_t)N * Ho * Wo * c * c * (Ci / 4);
+    hipLaunchKernelGGL(im2col_nhwc_vec4, dim3(grid_for(total)), dim3(kBlock), 0, s, x, col, N, Ci, H, W, c, P, Ho,
+                       Wo, ldk);
+  } else {
+    const int64_t total = (int64_t)N * Ho * Wo * ldk;
+    if (x_nchw)
+      hipLaunchKernelGGL(im2col_scalar<true>, dim3(grid_for(total)), dim3(kBlock), 0, s, x, col, N, Ci, H, W, c, P,
+                         Ho, Wo, ldk);
+    else
+      hipLaunchKernelGGL(im2col_scalar<false>, dim3(grid_for(total)), dim3(kBlock), 0, s, x, col, N, Ci, H, W, c,
+                         P, Ho, Wo, ldk);
+  }
+  prof_end(s);
+  return check_launch("im2col");
+}
+
+int col2im(const float* dcol, const float* mask_act, float* dx, int N, int Ci, int H, int W, int c, int P, int Ho,
+           int Wo, int ldk, hipStream_t s) {
+  prof_begin("col2im", (double)N * Ho * Wo * c * c * Ci,
+             4.0 * ((double)N * Ho * Wo * c * c * Ci + (mask_act ? 2.0 : 1.0) * N * H * W * Ci), s);
+  if (Ci % 4 == 0 && ldk % 4 == 0) {
+    const int64_t total = (int64_t)N * H * W * (Ci / 4);
+    hipLaunchKernelGGL(col2im_nhwc_vec4, dim3(grid_for(total)), dim3(kBlock), 0, s, dcol, mask_act, dx, N, Ci, H,
+                       W, c, P, Ho, Wo, ldk);
+  } else {
+    const int64_t total = (int64_t)N * H * W * Ci;
+    hipLaunchKernelGGL(col2im_nhwc_scalar, dim3(grid_for(total)), dim3(kBlock), 0, s, dcol, mask_act, dx, N, Ci,
+                       H, W, c, P, Ho, Wo, ldk);
+  }
+  prof_end(s);
+  return check_launch("col2im");
+}
+
+int repack_weight(const float* w, float* wrep, int Co, int Ci, int c, int ldk, hipStream_t s) {
+  prof_begin("repack_weight", 0, 4.0 * ((double)Co * c * c * Ci + (double)Co * ldk), s);
+  hipLaunchKernelGGL(repack_conv_weight, dim3(grid_for((int64_t)Co * ldk)), dim3(kBlock), 0, s, w, wrep, Co, Ci, c,
+                     ldk);
+  prof_end(s);
+  return check_launch("repack_weight");
+}
+
+int maxpool_fwd(const float* x, float* y, uint8_t* argmax, int N, int C, int H, int W, int p, bool out_nchw,
+                hipStream_t s) {
+  const int64_t total = (int64_t)N * (H / p) * (W / p) * C;
+  prof_begin("maxpool_fwd", (double)N * H * W * C, 4.0 * N * H * W * C + 5.0 * total, s);
+  hipLaunchKernelGGL(maxpool_fwd_kernel, dim3(grid_for(total)), dim3(kBlock), 0, s, x, y, argmax, N, C, H, W, p,
+                     (int)out_nchw);
+  prof_end(s);
+  return check_launch("maxpool_fwd");
+}
+
+int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, float* dx, int N, int C, int H, int W,
+                int p, bool out_nchw, hipStream_t s) {
+  const int64_t total = (int64_t)N * H * W * C;
+  const double pooled_n = (double)total / ((double)p * p);
+  prof_begin("maxpool_bwd", 0, 4.0 * total + pooled_n * (pooled ? 9.0 : 5.0), s);
+  hipLaunchKernelGGL(maxpool_bwd_kernel, dim3(grid_for(total)), dim3(kBlock), 0, s, dy, argmax, pooled, dx, N, C,
+                     H, W, p, (int)out_nchw);
+  prof_end(s);
+  return check_launch("maxpool_bwd");
+}
+
+int64_t colsum_chunk(int64_t rows, int cols) {
+  (void)cols;
+  return rows <= 4096 ? rows : 1024;
+}
+
+int64_t colsum_scratch_floats(int64_t rows, int cols) { return ceil_div(rows, colsum_chunk(rows, cols)) * cols; }
+
+int colsum(const float* dy, float* db, float* scratch, int64_t rows, int cols, hipStream_t s) {
+  const int64_t chunk = colsum_chunk(rows, cols);
+  const int64_t nchunks = ceil_div(rows, chunk);
+  prof_begin("colsum_partial", (double)rows * cols, 4.0 * ((double)rows * cols + (double)nchunks * cols), s);
+  hipLaunchKernelGGL(colsum_partial, dim3(grid_for(nchunks * cols)), dim3(kBlock), 0, s, dy, scratch, rows, cols,
+                     chunk);
+  prof_end(s);
+  if (int e = check_launch("colsum_partial")) return e;
+  prof_begin("colsum_final", (double)nchunks * cols, 4.0 * ((double)nchunks * cols + cols), s);
+  hipLaunchKernelGGL(colsum_final, dim3(grid_for(cols)), dim3(kBlock), 0, s, scratch, db, nchunks, cols);
+  prof_end(s);
+  return check_launch("colsum_final");
+}
+
+int softmax_ce(const float* z, const int32_t* y, float* dz, float* row_loss, float* loss, int N, int C,
+               float scale, hipStream_t s) {
+  const int rows_per_block = kBlock / 64;
+  prof_begin("softmax_ce", 6.0 * N * C, 4.0 * (2.0 * N * C + 2.0 * N), s);
+  hipLaunchKernelGGL(softmax_ce_kernel, dim3((int)ceil_div(N, rows_per_block)), dim3(kBlock), 0, s, z, y, dz,
+                     row_loss, N, C, scale);
+  prof_end(s);
+  if (int e = check_launch("softmax_ce")) return e;
+  prof_begin("loss_sum", N, 4.0 * (N + 1), s);
+  hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(kBlock), 0, s, row_loss, loss, N, scale);
+  prof_end(s);
+  return check_launch("loss_sum");
+}
+
+}  // namespace sgd

@@ -1,0 +1,695 @@
+// Network planner, step orchestration and the C ABI of libsgdstep.
+//
+// sgd_create_net walks the layer list once on the host: it infers every
+// shape (SPRINT report section 3.2 eq. (2), generalised to zero padding),
+// lays out the flat parameter vector (eq. (3)), chooses the matrix-product
+// split factors and assigns every intermediate tensor a fixed offset in the
+// caller's workspace.  sgd_compute_gradient then only enqueues kernels: the
+// forward pass layer by layer, softmax cross-entropy, and the backward pass
+// in reverse layer order (the dependency order of backpropagation described
+// in "Pipelined training with stale weights of deep CNNs", section 2), with
+// each layer's dedw / dedb / dedx products as listed in the SPRINT report's
+// section 3.3 SGEMM table.
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "layers.h"
+
+namespace sgd {
+
+thread_local std::string g_error;
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return SGD_EDEVICE;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------- profiler
+struct ProfRec {
+  const char* kernel;
+  int layer, phase;
+  double flops, bytes;
+  hipEvent_t beg, end;
+};
+
+struct Profiler {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;  // events reused across recordings
+  size_t used = 0;
+  int layer = -1, phase = 0;
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+  ~Profiler() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+thread_local Profiler* g_prof = nullptr;
+
+void prof_set_layer(int layer, int phase) {
+  if (g_prof) {
+    g_prof->layer = layer;
+    g_prof->phase = phase;
+  }
+}
+
+void prof_begin(const char* kernel, double flops, double bytes, hipStream_t s) {
+  if (!g_prof || !g_prof->on) return;
+  ProfRec r{kernel, g_prof->layer, g_prof->phase, flops, bytes, g_prof->get(), g_prof->get()};
+  if (!r.beg || !r.end) return;
+  (void)hipEventRecord(r.beg, s);
+  g_prof->recs.push_back(r);
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof || !g_prof->on || g_prof->recs.empty()) return;
+  (void)hipEventRecord(g_prof->recs.back().end, s);
+}
+
+namespace {
+
+struct Tensor {
+  int64_t off = -1;  // byte offset in the workspace
+  int64_t dims[4] = {0, 0, 0, 0};
+  int layout = 0;
+};
+
+// One planned stage.  ReLU entries of the layer list are folded into the
+// conv/fc stage they follow; an fc fed by a conv map without pooling gets a
+// p = 1 "pool" stage that only reorders NHWC to NCHW (the (c, h, w) flatten).
+struct Stage {
+  int kind = 0;   // SGD_CONV, SGD_MAXPOOL, SGD_FC, SGD_SOFTMAX_CE
+  int spec = -1;  // index in the caller's layer list (-1: inserted flatten)
+  int input = -1; // producing stage, -1 = the images
+  bool relu = false;
+  bool first_weighted = false;
+  int N = 0, Ci = 0, H = 0, W = 0;   // input shape (fc: Ci = input width, H = W = 1)
+  int Co = 0, Ho = 0, Wo = 0;        // output shape (fc: Co = output width)
+  int c = 0, P = 0, p = 1;           // conv filter / padding, pool window
+  int K = 0, ldk = 0;                // conv: c*c*Ci and its padded row length
+  bool out_nchw = false;             // pool: output written NCHW (feeds an fc)
+  int64_t w_off = -1, b_off = -1;    // parameter offsets (elements)
+  int split_fwd = 1, split_dw = 1, split_dx = 1;
+  Tensor out, dout, col, wrep, argmax;
+};
+
+}  // namespace
+}  // namespace sgd
+
+struct sgd_net {
+  sgd_input input{};
+  int reduction = SGD_REDUCE_MEAN;
+  int classes = 0;
+  std::vector<sgd_layer> spec;
+  std::vector<sgd::Stage> stages;
+  std::vector<int> spec_to_stage;  // layer-list index -> stage (ReLU -> its conv/fc)
+  int64_t n_params = 0;
+  std::vector<int64_t> w_offs, b_offs;
+  int64_t ws_bytes = 0;
+  sgd::Tensor row_loss;
+  int64_t partial_off = 0, partial_floats = 0;
+  int64_t colsum_off = 0, colsum_floats = 0;
+  sgd::Profiler prof;
+};
+
+namespace sgd {
+namespace {
+
+struct Bump {
+  int64_t top = 0;
+  int64_t take(int64_t bytes) {
+    const int64_t o = top;
+    top += round_up(std::max<int64_t>(bytes, 1), 256);
+    return o;
+  }
+};
+
+// dims follow the SGD_LAYOUT_* conventions; a row-major matrix is
+// {rows, cols, row stride, 1} and occupies rows * stride elements.
+Tensor make_tensor(Bump& b, int64_t elem_bytes, int layout, int64_t d0, int64_t d1, int64_t d2, int64_t d3) {
+  Tensor t;
+  t.layout = layout;
+  t.dims[0] = d0;
+  t.dims[1] = d1;
+  t.dims[2] = d2;
+  t.dims[3] = d3;
+  const int64_t elems = layout == SGD_LAYOUT_ROWS ? d0 * d2 : d0 * d1 * d2 * d3;
+  t.off = b.take(elem_bytes * elems);
+  return t;
+}
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+int plan(sgd_net* net) {
+  const sgd_input in = net->input;
+  if (in.batch <= 0 || in.channels <= 0 || in.height <= 0 || in.width <= 0)
+    return fail(SGD_ESHAPE, "input sizes must be positive");
+  auto& st = net->stages;
+  const int n_layers = (int)net->spec.size();
+  net->spec_to_stage.assign(n_layers, -1);
+  // current activation: producing stage (-1 = images), shape, whether flat
+  int cur = -1, C = in.channels, H = in.height, W = in.width;
+  bool flat = false;
+  int64_t off = 0;
+  bool seen_weighted = false;
+  for (int i = 0; i < n_layers; ++i) {
+    const sgd_layer& L = net->spec[i];
+    if (L.kind == SGD_CONV) {
+      if (flat) return fail(SGD_EUNSUPPORTED, "layer " + std::to_string(i) + ": conv after fc");
+      if (L.out <= 0 || L.kernel <= 0 || L.pad < 0)
+        return fail(SGD_ESHAPE, "layer " + std::to_string(i) + ": bad conv parameters");
+      Stage s;
+      s.kind = SGD_CONV;
+      s.spec = i;
+      s.input = cur;
+      s.N = in.batch;
+      s.Ci = C;
+      s.H = H;
+      s.W = W;
+      s.c = L.kernel;
+      s.P = L.pad;
+      s.Co = L.out;
+      s.Ho = H + 2 * L.pad - L.kernel + 1;
+      s.Wo = W + 2 * L.pad - L.kernel + 1;
+      if (s.Ho < 1 || s.Wo < 1) return fail(SGD_ESHAPE, "layer " + std::to_string(i) + ": conv output is empty");
+      s.K = s.c * s.c * s.Ci;
+      s.ldk = (int)round_up(s.K, 4);
+      s.first_weighted = !seen_weighted;
+      seen_weighted = true;
+      s.w_off = off;
+      off += (int64_t)s.Co * s.K;
+      s.b_off = off;
+      off += s.Co;
+      st.push_back(s);
+      cur = (int)st.size() - 1;
+      C = s.Co;
+      H = s.Ho;
+      W = s.Wo;
+      net->spec_to_stage[i] = cur;
+    } else if (L.kind == SGD_RELU) {
+      if (cur < 0 || (st[cur].kind != SGD_CONV && st[cur].kind != SGD_FC) || st[cur].relu ||
+          net->spec_to_stage[i - 1] != cur)
+        return fail(SGD_EUNSUPPORTED, "layer " + std::to_string(i) + ": ReLU must directly follow a conv or fc");
+      st[cur].relu = true;
+      net->spec_to_stage[i] = cur;
+    } else if (L.kind == SGD_MAXPOOL) {
+      if (flat || cur < 0) return fail(SGD_EUNSUPPORTED, "layer " + std::to_string(i) + ": pool needs a conv map");
+      if (L.pool <= 0 || L.pool > 15 || H % L.pool || W % L.pool)
+        return fail(SGD_ESHAPE, "layer " + std::to_string(i) + ": pool window must divide the feature map");
+      Stage s;
+      s.kind = SGD_MAXPOOL;
+      s.spec = i;
+      s.input = cur;
+      s.N = in.batch;
+      s.Ci = s.Co = C;
+      s.H = H;
+      s.W = W;
+      s.p = L.pool;
+      s.Ho = H / L.pool;
+      s.Wo = W / L.pool;
+      st.push_back(s);
+      cur = (int)st.size() - 1;
+      H = s.Ho;
+      W = s.Wo;
+      net->spec_to_stage[i] = cur;
+    } else if (L.kind == SGD_FC) {
+      if (L.out <= 0) return fail(SGD_ESHAPE, "layer " + std::to_string(i) + ": fc width must be positive");
+      if (!flat && cur >= 0 && H * W > 1) {
+        if (st[cur].kind == SGD_MAXPOOL) {
+          st[cur].out_nchw = true;
+        } else {  // conv map without pooling: insert the NHWC -> NCHW flatten
+          Stage f;
+          f.kind = SGD_MAXPOOL;
+          f.input = cur;
+          f.N = in.batch;
+          f.Ci = f.Co = C;
+          f.H = f.Ho = H;
+          f.W = f.Wo = W;
+          f.p = 1;
+          f.out_nchw = true;
+          st.push_back(f);
+          cur = (int)st.size() - 1;
+        }
+      }
+      Stage s;
+      s.kind = SGD_FC;
+      s.spec = i;
+      s.input = cur;
+      s.N = in.batch;
+      s.Ci = flat ? C : C * H * W;
+      s.H = s.W = 1;
+      s.Co = L.out;
+      s.Ho = s.Wo = 1;
+      s.first_weighted = !seen_weighted;
+      seen_weighted = true;
+      s.w_off = off;
+      off += (int64_t)s.Co * s.Ci;
+      s.b_off = off;
+      off += s.Co;
+      st.push_back(s);
+      cur = (int)st.size() - 1;
+      C = s.Co;
+      H = W = 1;
+      flat = true;
+      net->spec_to_stage[i] = cur;
+    } else if (L.kind == SGD_SOFTMAX_CE) {
+      if (i != n_layers - 1) return fail(SGD_ESHAPE, "softmax_ce must be the last layer");
+      if (cur < 0 || st[cur].kind != SGD_FC || st[cur].relu || net->spec_to_stage[i - 1] != cur)
+        return fail(SGD_EUNSUPPORTED, "softmax_ce must directly follow an fc layer without ReLU");
+      Stage s;
+      s.kind = SGD_SOFTMAX_CE;
+      s.spec = i;
+      s.input = cur;
+      s.N = in.batch;
+      s.Ci = s.Co = C;
+      st.push_back(s);
+      net->classes = C;
+      net->spec_to_stage[i] = (int)st.size() - 1;
+    } else {
+      return fail(SGD_EINVAL, "layer " + std::to_string(i) + ": unknown kind " + std::to_string(L.kind));
+    }
+  }
+  if (st.empty() || st.back().kind != SGD_SOFTMAX_CE) return fail(SGD_ESHAPE, "last layer must be softmax_ce");
+  net->n_params = off;
+
+  // Workspace layout and product split factors.
+  Bump b;
+  int64_t partial = 0, colsum_sc = 0;
+  for (Stage& s : st) {
+    const int64_t N = s.N;
+    if (s.kind == SGD_CONV) {
+      const int64_t P = N * s.Ho * s.Wo;
+      s.wrep = make_tensor(b, 4, SGD_LAYOUT_ROWS, s.Co, s.K, s.ldk, 1);
+      s.col = make_tensor(b, 4, SGD_LAYOUT_ROWS, P, s.K, s.ldk, 1);
+      s.out = make_tensor(b, 4, SGD_LAYOUT_NHWC, N, s.Ho, s.Wo, s.Co);
+      s.dout = make_tensor(b, 4, SGD_LAYOUT_NHWC, N, s.Ho, s.Wo, s.Co);
+      s.split_fwd = gemm_pick_splits((int)P, s.Co, s.ldk);
+      s.split_dw = gemm_pick_splits(s.Co, s.ldk, (int)P);
+      s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)P, s.ldk, s.Co);
+      if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * P * s.Co);
+      partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * s.ldk);
+      if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * P * s.ldk);
+      colsum_sc = std::max<int64_t>(colsum_sc, colsum_scratch_floats(P, s.Co));
+    } else if (s.kind == SGD_MAXPOOL) {
+      const int lay = s.out_nchw ? SGD_LAYOUT_NCHW : SGD_LAYOUT_NHWC;
+      if (s.out_nchw) {
+        s.out = make_tensor(b, 4, lay, N, s.Co, s.Ho, s.Wo);
+        s.argmax = make_tensor(b, 1, lay, N, s.Co, s.Ho, s.Wo);
+        s.dout = make_tensor(b, 4, lay, N, s.Co, s.Ho, s.Wo);
+      } else {
+        s.out = make_tensor(b, 4, lay, N, s.Ho, s.Wo, s.Co);
+        s.argmax = make_tensor(b, 1, lay, N, s.Ho, s.Wo, s.Co);
+        s.dout = make_tensor(b, 4, lay, N, s.Ho, s.Wo, s.Co);
+      }
+    } else if (s.kind == SGD_FC) {
+      s.out = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, s.Co, s.Co, 1);
+      s.dout = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, s.Co, s.Co, 1);
+      s.split_fwd = gemm_pick_splits((int)N, s.Co, s.Ci);
+      s.split_dw = gemm_pick_splits(s.Co, s.Ci, (int)N);
+      s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)N, s.Ci, s.Co);
+      if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * N * s.Co);
+      if (s.split_dw > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * s.Ci);
+      if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * N * s.Ci);
+      colsum_sc = std::max<int64_t>(colsum_sc, colsum_scratch_floats(N, s.Co));
+    } else if (s.kind == SGD_SOFTMAX_CE) {
+      // the logits' gradient lives in the last fc stage's dout
+      net->row_loss = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, 1, 1, 1);
+      s.out = net->row_loss;
+      s.dout = st[s.input].dout;
+    }
+  }
+  net->partial_floats = partial;
+  net->partial_off = b.take(4 * std::max<int64_t>(partial, 1));
+  net->colsum_floats = colsum_sc;
+  net->colsum_off = b.take(4 * std::max<int64_t>(colsum_sc, 1));
+  net->ws_bytes = b.top;
+  for (const Stage& s : st)
+    if (s.kind == SGD_CONV || s.kind == SGD_FC) {
+      net->w_offs.push_back(s.w_off);
+      net->b_offs.push_back(s.b_off);
+    }
+  return SGD_OK;
+}
+
+template <typename T>
+T* at(void* ws, const Tensor& t) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + t.off);
+}
+
+// Forward output of the stage feeding `s` (nullptr = the images).
+const float* input_of(const sgd_net* net, const Stage& s, void* ws, const float* X) {
+  return s.input < 0 ? X : at<float>(ws, net->stages[s.input].out);
+}
+
+int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y, float* loss, void* ws,
+                hipStream_t st) {
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
+  for (Stage& s : net->stages) {
+    const float* xin = input_of(net, s, ws, X);
+    int e = 0;
+    prof_set_layer(s.spec, 0);
+    if (s.kind == SGD_CONV) {
+      float* wrep = at<float>(ws, s.wrep);
+      float* col = at<float>(ws, s.col);
+      if ((e = repack_weight(Wt + s.w_off, wrep, s.Co, s.Ci, s.c, s.ldk, st))) return e;
+      if ((e = im2col(xin, s.input < 0, col, s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st))) return e;
+      GemmDesc g{};
+      g.A = col;
+      g.lda = s.ldk;
+      g.B = wrep;
+      g.ldb = s.ldk;
+      g.C = at<float>(ws, s.out);
+      g.ldc = s.Co;
+      g.M = s.N * s.Ho * s.Wo;
+      g.N = s.Co;
+      g.K = s.ldk;
+      g.flops = 2.0 * g.M * g.N * (double)s.K;
+      g.epi = s.relu ? EPI_BIAS_RELU : EPI_BIAS;
+      g.bias = Wt + s.b_off;
+      g.splits = s.split_fwd;
+      g.partial = partial;
+      if ((e = gemm(g, st))) return e;
+    } else if (s.kind == SGD_MAXPOOL) {
+      if ((e = maxpool_fwd(xin, at<float>(ws, s.out), at<uint8_t>(ws, s.argmax), s.N, s.Ci, s.H, s.W, s.p,
+                           s.out_nchw, st)))
+        return e;
+    } else if (s.kind == SGD_FC) {
+      GemmDesc g{};
+      g.A = xin;
+      g.lda = s.Ci;
+      g.B = Wt + s.w_off;
+      g.ldb = s.Ci;
+      g.C = at<float>(ws, s.out);
+      g.ldc = s.Co;
+      g.M = s.N;
+      g.N = s.Co;
+      g.K = s.Ci;
+      g.epi = s.relu ? EPI_BIAS_RELU : EPI_BIAS;
+      g.bias = Wt + s.b_off;
+      g.splits = s.split_fwd;
+      g.partial = partial;
+      if ((e = gemm(g, st))) return e;
+    } else if (s.kind == SGD_SOFTMAX_CE) {
+      const float scale = net->reduction == SGD_REDUCE_SUM ? 1.f : 1.f / (float)s.N;
+      if ((e = softmax_ce(xin, y, at<float>(ws, s.dout), at<float>(ws, s.out), loss, s.N, s.Ci, scale, st)))
+        return e;
+    }
+  }
+  return 0;
+}
+
+int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, void* ws, hipStream_t st) {
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
+  float* colsum_sc = reinterpret_cast<float*>(static_cast<char*>(ws) + net->colsum_off);
+  auto& stages = net->stages;
+  for (int si = (int)stages.size() - 1; si >= 0; --si) {
+    Stage& s = stages[si];
+    const float* xin = input_of(net, s, ws, X);
+    int e = 0;
+    prof_set_layer(s.spec, 1);
+    if (s.kind == SGD_FC) {
+      const float* dout = at<float>(ws, s.dout);
+      GemmDesc g{};  // dedw: dW[out][in] = dout^T * input
+      g.A = dout;
+      g.lda = s.Co;
+      g.a_t = true;
+      g.B = xin;
+      g.ldb = s.Ci;
+      g.b_t = true;
+      g.C = grad + s.w_off;
+      g.ldc = s.Ci;
+      g.M = s.Co;
+      g.N = s.Ci;
+      g.K = s.N;
+      g.epi = EPI_STORE;
+      g.splits = s.split_dw;
+      g.partial = partial;
+      if ((e = gemm(g, st))) return e;
+      if ((e = colsum(dout, grad + s.b_off, colsum_sc, s.N, s.Co, st))) return e;  // dedb
+      if (!s.first_weighted) {
+        const Stage& src = stages[s.input];
+        GemmDesc d{};  // dedx_fc: d_input[N][in] = dout * W
+        d.A = dout;
+        d.lda = s.Co;
+        d.B = Wt + s.w_off;
+        d.ldb = s.Ci;
+        d.b_t = true;
+        d.C = at<float>(ws, src.dout);
+        d.ldc = s.Ci;
+        d.M = s.N;
+        d.N = s.Ci;
+        d.K = s.Co;
+        const bool mask = src.relu && src.kind != SGD_MAXPOOL;
+        d.epi = mask ? EPI_MASK : EPI_STORE;
+        d.mask = mask ? at<float>(ws, src.out) : nullptr;
+        d.ldm = s.Ci;
+        d.splits = s.split_dx;
+        d.partial = partial;
+        if ((e = gemm(d, st))) return e;
+      }
+    } else if (s.kind == SGD_MAXPOOL) {
+      const Stage& src = stages[s.input];
+      const float* pooled = src.relu ? at<float>(ws, s.out) : nullptr;
+      if ((e = maxpool_bwd(at<float>(ws, s.dout), at<uint8_t>(ws, s.argmax), pooled, at<float>(ws, src.dout), s.N,
+                           s.Ci, s.H, s.W, s.p, s.out_nchw, st)))
+        return e;
+    } else if (s.kind == SGD_CONV) {
+      const float* dout = at<float>(ws, s.dout);
+      float* col = at<float>(ws, s.col);
+      const int64_t P = (int64_t)s.N * s.Ho * s.Wo;
+      GemmDesc g{};  // dedw: dW'[co][kk] = dout^T * col, stored permuted to [co][ci][ky][kx]
+      g.A = dout;
+      g.lda = s.Co;
+      g.a_t = true;
+      g.B = col;
+      g.ldb = s.ldk;
+      g.b_t = true;
+      g.C = grad + s.w_off;
+      g.ldc = s.K;
+      g.M = s.Co;
+      g.N = s.ldk;
+      g.K = (int)P;
+      g.flops = 2.0 * s.Co * (double)s.K * (double)P;
+      g.epi = EPI_STORE;
+      g.splits = s.split_dw;
+      g.partial = partial;
+      g.perm_c = s.c;
+      g.perm_ci = s.Ci;
+      g.perm_k = s.K;
+      if ((e = gemm(g, st))) return e;
+      if ((e = colsum(dout, grad + s.b_off, colsum_sc, P, s.Co, st))) return e;  // dedb
+      if (!s.first_weighted) {
+        GemmDesc d{};  // dedx_conv: dcol[P][kk] = dout * W' (written over the im2col matrix)
+        d.A = dout;
+        d.lda = s.Co;
+        d.B = at<float>(ws, s.wrep);
+        d.ldb = s.ldk;
+        d.b_t = true;
+        d.C = col;
+        d.ldc = s.ldk;
+        d.M = (int)P;
+        d.N = s.ldk;
+        d.K = s.Co;
+        d.flops = 2.0 * (double)P * s.K * (double)s.Co;
+        d.epi = EPI_STORE;
+        d.splits = s.split_dx;
+        d.partial = partial;
+        if ((e = gemm(d, st))) return e;
+        const Stage& src = stages[s.input];
+        const float* mask = (src.relu && src.kind != SGD_MAXPOOL) ? at<float>(ws, src.out) : nullptr;
+        if ((e = col2im(col, mask, at<float>(ws, src.dout), s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st)))
+          return e;
+      }
+    }
+  }
+  return 0;
+}
+
+}  // namespace
+}  // namespace sgd
+
+// ======================================================================= ABI
+using sgd::fail;
+
+extern "C" {
+
+const char* sgd_last_error(void) { return sgd::g_error.c_str(); }
+
+int sgd_create_net(const sgd_input* input, const sgd_layer* layers, int n_layers, int reduction, sgd_net** out) {
+  if (!input || !layers || !out) return fail(SGD_EINVAL, "sgd_create_net: null pointer");
+  *out = nullptr;
+  if (n_layers < 2) return fail(SGD_EINVAL, "sgd_create_net: need at least an fc and softmax_ce layer");
+  if (reduction != SGD_REDUCE_MEAN && reduction != SGD_REDUCE_SUM)
+    return fail(SGD_EINVAL, "sgd_create_net: bad reduction");
+  sgd_net* net = new (std::nothrow) sgd_net();
+  if (!net) return fail(SGD_EINVAL, "sgd_create_net: out of host memory");
+  net->input = *input;
+  net->reduction = reduction;
+  net->spec.assign(layers, layers + n_layers);
+  const int rc = sgd::plan(net);
+  if (rc != SGD_OK) {
+    delete net;
+    return rc;
+  }
+  *out = net;
+  return SGD_OK;
+}
+
+void sgd_destroy_net(sgd_net* net) { delete net; }
+
+int64_t sgd_param_count(const sgd_net* net) { return net ? net->n_params : -1; }
+
+int sgd_param_offsets(const sgd_net* net, int64_t* w_off, int64_t* b_off, int max_layers) {
+  if (!net) return fail(SGD_EINVAL, "sgd_param_offsets: null net");
+  const int n = (int)net->w_offs.size();
+  for (int i = 0; i < n && i < max_layers; ++i) {
+    if (w_off) w_off[i] = net->w_offs[i];
+    if (b_off) b_off[i] = net->b_offs[i];
+  }
+  return n;
+}
+
+size_t sgd_workspace_bytes(const sgd_net* net) { return net ? (size_t)net->ws_bytes : 0; }
+
+int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offset, int64_t dims[4], int* layout) {
+  if (!net || !byte_offset || !dims || !layout) return fail(SGD_EINVAL, "sgd_tensor_info: null pointer");
+  if (layer < 0 || layer >= (int)net->spec_to_stage.size()) return fail(SGD_EINVAL, "sgd_tensor_info: bad layer");
+  const sgd::Stage& s = net->stages[net->spec_to_stage[layer]];
+  const sgd::Tensor* t = nullptr;
+  switch (which) {
+    case SGD_T_OUT: t = &s.out; break;
+    case SGD_T_DOUT: t = &s.dout; break;
+    case SGD_T_COL: t = s.kind == SGD_CONV ? &s.col : nullptr; break;
+    case SGD_T_WREP: t = s.kind == SGD_CONV ? &s.wrep : nullptr; break;
+    case SGD_T_ARGMAX: t = s.kind == SGD_MAXPOOL ? &s.argmax : nullptr; break;
+    default: break;
+  }
+  if (!t || t->off < 0) return fail(SGD_EINVAL, "sgd_tensor_info: layer has no such tensor");
+  *byte_offset = t->off;
+  for (int i = 0; i < 4; ++i) dims[i] = t->dims[i];
+  *layout = t->layout;
+  return SGD_OK;
+}
+
+int sgd_compute_gradient(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, float* loss,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, "sgd_compute_gradient: null pointer");
+  if ((int64_t)ws_bytes < net->ws_bytes)
+    return fail(SGD_EWORKSPACE, "sgd_compute_gradient: workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                    std::to_string(net->ws_bytes));
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SGD_EINVAL, "sgd_compute_gradient: workspace not 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error from an unrelated earlier call
+  sgd::g_prof = &net->prof;
+  int e = sgd::run_forward(net, W, X, y, loss, ws, st);
+  if (!e) e = sgd::run_backward(net, W, X, grad, ws, st);
+  sgd::g_prof = nullptr;
+  return e;
+}
+
+int sgd_profile(sgd_net* net, int enable) {
+  if (!net) return fail(SGD_EINVAL, "sgd_profile: null net");
+  if (enable) {
+    net->prof.recs.clear();
+    net->prof.used = 0;
+  }
+  net->prof.on = enable != 0;
+  return SGD_OK;
+}
+
+int sgd_profile_read(sgd_net* net, sgd_kernel_time* out, int max_records) {
+  if (!net) return fail(SGD_EINVAL, "sgd_profile_read: null net");
+  const int n = (int)net->prof.recs.size();
+  for (int i = 0; i < n && i < max_records && out; ++i) {
+    const sgd::ProfRec& r = net->prof.recs[i];
+    float ms = 0.f;
+    if (hipEventSynchronize(r.end) != hipSuccess || hipEventElapsedTime(&ms, r.beg, r.end) != hipSuccess)
+      return fail(SGD_EDEVICE, "sgd_profile_read: event query failed");
+    out[i].kernel = r.kernel;
+    out[i].layer = r.layer;
+    out[i].phase = r.phase;
+    out[i].ms = ms;
+    out[i].flops = r.flops;
+    out[i].bytes = r.bytes;
+  }
+  return n;
+}
+
+int sgd_accumulate_grad(sgd_gradbuf* gb, const float* grad, void* stream) {
+  if (!gb || !gb->data || !grad) return fail(SGD_EINVAL, "sgd_accumulate_grad: null pointer");
+  if (gb->n <= 0) return fail(SGD_EINVAL, "sgd_accumulate_grad: n must be positive");
+  const float* g[1] = {grad};
+  const int e = sgd::accumulate(gb->data, g, 1, gb->empty != 0, gb->n, static_cast<hipStream_t>(stream));
+  if (!e) gb->empty = 0;
+  return e;
+}
+
+int sgd_accumulate_grads(sgd_gradbuf* gb, const float* const* grads, int k, void* stream) {
+  if (!gb || !gb->data || !grads) return fail(SGD_EINVAL, "sgd_accumulate_grads: null pointer");
+  if (gb->n <= 0) return fail(SGD_EINVAL, "sgd_accumulate_grads: n must be positive");
+  if (k < 1 || k > 16) return fail(SGD_EINVAL, "sgd_accumulate_grads: k must be in 1..16");
+  for (int j = 0; j < k; ++j)
+    if (!grads[j]) return fail(SGD_EINVAL, "sgd_accumulate_grads: null gradient pointer");
+  const int e = sgd::accumulate(gb->data, grads, k, gb->empty != 0, gb->n, static_cast<hipStream_t>(stream));
+  if (!e) gb->empty = 0;
+  return e;
+}
+
+static int check_rule(const sgd_rule* rule, const float* state, const char* who) {
+  if (!rule) return fail(SGD_EINVAL, std::string(who) + ": null rule");
+  if (rule->rule != SGD_PLAIN && rule->rule != SGD_MOMENTUM && rule->rule != SGD_ADAGRAD)
+    return fail(SGD_EINVAL, std::string(who) + ": unknown rule");
+  if (rule->rule != SGD_PLAIN && !state) return fail(SGD_EINVAL, std::string(who) + ": rule needs a state buffer");
+  return SGD_OK;
+}
+
+int sgd_apply_update(float* W, sgd_gradbuf* gb, float* state, const sgd_rule* rule, void* stream) {
+  if (!W || !gb || !gb->data) return fail(SGD_EINVAL, "sgd_apply_update: null pointer");
+  if (gb->n <= 0) return fail(SGD_EINVAL, "sgd_apply_update: n must be positive");
+  if (int e = check_rule(rule, state, "sgd_apply_update")) return e;
+  int e = SGD_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gb->empty) {
+    // zero gradient: plain and Adagrad leave W (and A) unchanged; momentum decays V
+    if (rule->rule == SGD_MOMENTUM)
+      e = sgd::apply_rule(W, state, nullptr, 0, gb->n, rule->rule, rule->eta, rule->mu, rule->eps, st);
+  } else {
+    const float* g[1] = {gb->data};
+    e = sgd::apply_rule(W, state, g, 1, gb->n, rule->rule, rule->eta, rule->mu, rule->eps, st);
+  }
+  if (!e) gb->empty = 1;
+  return e;
+}
+
+int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, int64_t n, const sgd_rule* rule,
+                    void* stream) {
+  if (!W || !grads) return fail(SGD_EINVAL, "sgd_apply_fused: null pointer");
+  if (n <= 0) return fail(SGD_EINVAL, "sgd_apply_fused: n must be positive");
+  if (k < 1 || k > 16) return fail(SGD_EINVAL, "sgd_apply_fused: k must be in 1..16");
+  for (int j = 0; j < k; ++j)
+    if (!grads[j]) return fail(SGD_EINVAL, "sgd_apply_fused: null gradient pointer");
+  if (int e = check_rule(rule, state, "sgd_apply_fused")) return e;
+  return sgd::apply_rule(W, state, grads, k, n, rule->rule, rule->eta, rule->mu, rule->eps,
+                         static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

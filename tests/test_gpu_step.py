@@ -1,0 +1,120 @@
+"""GPU parity of sgd_compute_gradient against the CPU oracle (end to end).
+
+Loss to |dL| <= 1e-5 |L|; every layer's weight and bias gradient to
+max|d| <= 1e-4 max|g| (fp32 products with fp32 accumulation on the GPU, the
+oracle rounding to float after each layer with double sums).  Sizes are ones
+the oracle finishes in seconds, chosen to span several GEMM tiles and leave
+ragged tails (odd channel counts, widths not divisible by 4, 16, 64 or 128).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads
+from tests._util import LOSS_RTOL, per_tensor_grad_check
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sgd_cnns_amd as S  # noqa: E402
+
+
+def run_gpu(chw, layers, X, y, W, reduce_sum=False, keep_ws=False):
+    N = X.shape[0]
+    net = S.Net((N,) + tuple(chw), layers, reduce_sum=reduce_sum)
+    dev = torch.device("cuda")
+    Wd = torch.from_numpy(W).to(dev)
+    Xd = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
+    yd = torch.from_numpy(y).to(dev)
+    grad = torch.full((net.param_count(),), float("nan"), device=dev)
+    loss = torch.full((1,), float("nan"), device=dev)
+    ws = net.workspace()
+    net.compute_gradient(Wd, Xd, yd, grad, loss, ws)
+    torch.cuda.synchronize()
+    out = (float(loss.item()), grad.cpu().numpy())
+    if keep_ws:
+        return out + (net, ws)
+    return out
+
+
+def check(chw, layers, N, seed, classes, x_dist="uniform", reduce_sum=False, w_scale=None):
+    print(f"[parity] chw={chw} N={N} seed={seed} layers={layers}", flush=True)
+    shape = (N,) + tuple(chw)
+    X = workloads.uniform01(seed, 0, shape) if x_dist == "uniform" else workloads.normal(seed, 0, shape)
+    y = workloads.labels(seed, 1, N, classes)
+    W = workloads.he_normal_params(seed, chw, layers)
+    onet = O.OracleNet(chw, layers, reduce_sum=reduce_sum)
+    assert onet.param_count() == W.size
+    l_ref, g_ref = onet.gradient(W, X, y)
+    l_gpu, g_gpu = run_gpu(chw, layers, X, y, W, reduce_sum)
+    assert np.isfinite(g_gpu).all()
+    assert abs(l_gpu - l_ref) <= LOSS_RTOL * abs(l_ref), (l_gpu, l_ref)
+    wo = [onet.params[i][0] for i in sorted(onet.params)]
+    bo = [onet.params[i][2] for i in sorted(onet.params)]
+    worst = per_tensor_grad_check(g_gpu, g_ref, wo, bo, W.size)
+    print(f"[parity] loss {l_gpu:.7f} vs {l_ref:.7f}; worst grad ratio {worst:.2e}", flush=True)
+
+
+def test_lenet5_config():
+    wl = workloads.WORKLOADS["lenet5"]
+    check(wl.chw, wl.layers, wl.batch, wl.seed, wl.classes)
+
+
+def test_tiny_cnn_ragged():
+    layers = [("conv", 5, 3, 1), ("relu",), ("pool", 2), ("conv", 7, 3, 0), ("relu",), ("pool", 3),
+              ("fc", 13), ("relu",), ("fc", 6), ("softmax_ce",)]
+    check((3, 16, 16), layers, 3, 101, 6, x_dist="normal")
+
+
+def test_cnn_unpooled_conv_into_fc_and_sum_reduction():
+    layers = [("conv", 4, 3, 1), ("relu",), ("conv", 6, 5, 2), ("fc", 11), ("relu",), ("fc", 5), ("softmax_ce",)]
+    check((2, 9, 7), layers, 5, 102, 5, x_dist="normal", reduce_sum=True)
+
+
+def test_mlp_ragged_tiles():
+    layers = [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)]
+    check((3072, 1, 1), layers, 70, 103, 10)
+
+
+def test_conv_channels_multiple_of_4_vector_paths():
+    # Ci % 4 == 0 takes the float4 im2col / col2im paths; 3 pools; 2 tiles in M
+    layers = [("conv", 8, 3, 1), ("relu",), ("conv", 16, 3, 1), ("relu",), ("pool", 2),
+              ("conv", 32, 3, 1), ("relu",), ("pool", 2), ("fc", 40), ("relu",), ("fc", 10), ("softmax_ce",)]
+    check((4, 16, 16), layers, 6, 104, 10, x_dist="normal")
+
+
+def test_vgg_cifar_reduced_batch():
+    wl = workloads.WORKLOADS["vgg_cifar"]
+    check(wl.chw, wl.layers, 2, 105, wl.classes, x_dist="normal")
+
+
+def test_deterministic_bitwise():
+    wl = workloads.WORKLOADS["lenet5"]
+    X, y, W = workloads.make_inputs(wl)
+    a = run_gpu(wl.chw, wl.layers, X, y, W)
+    b = run_gpu(wl.chw, wl.layers, X, y, W)
+    assert a[0] == b[0]
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_zero_weights_closed_form():
+    # W = 0: loss = ln C; only the last bias has a gradient, 1/C - count(y=j)/N
+    wl = workloads.WORKLOADS["lenet5"]
+    X, y, W = workloads.make_inputs(wl)
+    W[:] = 0
+    l, g = run_gpu(wl.chw, wl.layers, X, y, W)
+    assert l == pytest.approx(np.log(10), rel=1e-6)
+    net = S.Net((wl.batch,) + wl.chw, wl.layers)
+    wo, bo = net.param_offsets()
+    expect = 1.0 / 10 - np.bincount(y, minlength=10) / wl.batch
+    np.testing.assert_allclose(g[bo[-1]:], expect, atol=1e-7)
+    assert np.all(g[:bo[-1]] == 0)
+
+
+def test_nan_input_propagates_without_error():
+    wl = workloads.WORKLOADS["lenet5"]
+    X, y, W = workloads.make_inputs(wl)
+    X[3, 0, 10, 10] = np.nan
+    l, g = run_gpu(wl.chw, wl.layers, X, y, W)
+    assert np.isnan(l)
+    assert np.isnan(O.OracleNet(wl.chw, wl.layers).gradient(W, X, y)[0])

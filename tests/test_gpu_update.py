@@ -1,0 +1,158 @@
+"""GPU parity of GradBuf accumulation and the update rules against the oracle.
+
+The update arithmetic is one rounding per statement in a fixed order on both
+sides, so results are expected bitwise equal (the contract is <= 1 ulp).
+Sizes include a ragged tail (n % 4 != 0) and misaligned pointers (views
+starting one float in), which take the scalar paths.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sgd_cnns_amd as S  # noqa: E402
+
+
+def ulp_diff(a, b):
+    a = a.astype(np.float32).view(np.int32).astype(np.int64)
+    b = b.astype(np.float32).view(np.int32).astype(np.int64)
+    a = np.where(a < 0, -(a & 0x7FFFFFFF), a)
+    b = np.where(b < 0, -(b & 0x7FFFFFFF), b)
+    return np.abs(a - b)
+
+
+def dev(a, offset=0):
+    """Device copy; with offset=1 the tensor starts 4 bytes into its allocation (misaligned)."""
+    t = torch.empty(a.size + offset, dtype=torch.float32, device="cuda")
+    v = t[offset:]
+    v.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    return v
+
+
+@pytest.mark.parametrize("n,offset", [(1000003, 0), (4099, 1), (7, 0)])
+@pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad"])
+def test_accumulate_then_apply_matches_oracle(n, offset, rule):
+    print(f"[update] rule={rule} n={n} offset={offset}", flush=True)
+    W0 = workloads.normal(11, 2, n)
+    st0 = np.abs(workloads.normal(11, 3, n)) + np.float32(0.1) if rule == "adagrad" else \
+        workloads.normal(11, 3, n, 1e-3)
+    gs = [workloads.normal(11, 100 + j, n, 1e-3) for j in range(3)]
+    eta, mu, eps = 0.01, 0.9, 1e-8
+    # oracle
+    gb = O.GradBuf(n)
+    for g in gs:
+        gb.accumulate(g)
+    Wr, sr = W0.copy(), st0.copy()
+    O.apply_rule(rule, Wr, sr, gb.data, eta, mu, eps)
+    # GPU: accumulate one by one, then apply
+    gbd = S.GradBuf(n, data=dev(np.zeros(n, np.float32), offset))
+    gds = [dev(g, offset) for g in gs]
+    for g in gds:
+        S.accumulate_grad(gbd, g)
+    Wd, sd = dev(W0, offset), dev(st0, offset)
+    S.apply_update(Wd, gbd, sd if rule != "plain" else None, S.Rule(rule, eta, mu, eps))
+    torch.cuda.synchronize()
+    assert gbd.empty
+    np.testing.assert_array_equal(gbd.data.cpu().numpy(), gb.data)
+    assert ulp_diff(Wd.cpu().numpy(), Wr).max() <= 1
+    assert np.array_equal(Wd.cpu().numpy(), Wr), "expected bitwise equality"
+    if rule != "plain":
+        assert np.array_equal(sd.cpu().numpy(), sr)
+
+
+@pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad"])
+def test_fused_equals_accumulate_plus_apply(rule):
+    n, k = 333_335, 8
+    gs = [workloads.normal(12, 100 + j, n, 1e-3) for j in range(k)]
+    W0 = workloads.normal(12, 2, n)
+    st0 = np.full(n, 0.1, np.float32) if rule == "adagrad" else np.zeros(n, np.float32)
+    gds = [dev(g) for g in gs]
+    # fused
+    Wf, sf = dev(W0), dev(st0)
+    S.apply_fused(Wf, sf, gds, S.Rule(rule, 0.01, 0.9, 1e-8))
+    # unfused: fold k buffers then apply
+    gb = S.GradBuf(n)
+    S.accumulate_grads(gb, gds)
+    Wu, su = dev(W0), dev(st0)
+    S.apply_update(Wu, gb, su, S.Rule(rule, 0.01, 0.9, 1e-8))
+    # oracle
+    ob = O.GradBuf(n)
+    for g in gs:
+        ob.accumulate(g)
+    Wr, sr = W0.copy(), st0.copy()
+    O.apply_rule(rule, Wr, sr, ob.data, 0.01, 0.9, 1e-8)
+    torch.cuda.synchronize()
+    for t in (Wf, Wu):
+        assert np.array_equal(t.cpu().numpy(), Wr)
+    for t in (sf, su):
+        assert np.array_equal(t.cpu().numpy(), sr)
+
+
+def test_empty_gradbuf_is_zero_gradient():
+    n = 1001
+    W0 = workloads.normal(13, 2, n)
+    V0 = workloads.normal(13, 3, n)
+    gb = S.GradBuf(n)
+    gb.data.fill_(123.0)
+    for rule in ("plain", "adagrad", "momentum"):
+        Wd, sd = dev(W0), dev(np.abs(V0) if rule == "adagrad" else V0)
+        S.apply_update(Wd, gb, sd, S.Rule(rule, 0.01, 0.9, 1e-8))
+        Wr, sr = W0.copy(), (np.abs(V0) if rule == "adagrad" else V0).copy()
+        O.apply_rule(rule, Wr, sr, None, 0.01, 0.9, 1e-8)
+        torch.cuda.synchronize()
+        assert np.array_equal(Wd.cpu().numpy(), Wr)
+        assert np.array_equal(sd.cpu().numpy(), sr)
+
+
+def test_dyadic_permutations_bitwise_equal():
+    n, k = 4096 + 3, 4
+    r = np.random.default_rng(3)
+    gs = [(r.integers(-2 ** 12, 2 ** 12, n) * 2.0 ** -20).astype(np.float32) for _ in range(k)]
+    gds = [dev(g) for g in gs]
+    outs = []
+    for perm in ([0, 1, 2, 3], [3, 2, 1, 0], [2, 0, 3, 1]):
+        gb = S.GradBuf(n)
+        S.accumulate_grads(gb, [gds[j] for j in perm])
+        outs.append(gb.data.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_parameter_server_workload_full_size():
+    # 138,357,544 parameters, K = 8 buffers N(0, 1e-3^2), Adagrad eta 0.01, eps 1e-8, A0 = 0.1:
+    # full-array check at step 1, strided subset at steps 2-3 with fresh buffers.
+    ps = workloads.PS_APPLY
+    n, k = ps["n"], ps["k"]
+    print(f"[update] parameter-server n={n} k={k}", flush=True)
+    W0 = workloads.normal(ps["seed"], 2, n)
+    A0 = np.full(n, ps["acc0"], np.float32)
+    pool = [workloads.ps_gradient(ps["seed"], j, n, ps["grad_std"]) for j in range(10)]
+    Wd, Ad = dev(W0), dev(A0)
+    gd = [dev(g) for g in pool]
+    Wr, Ar = W0, A0
+    sub = slice(0, n, 61)
+    rule = S.Rule("adagrad", ps["eta"], 0.0, ps["eps"])
+    for step in range(3):
+        idx = [(k * step + i) % len(pool) for i in range(k)]
+        S.apply_fused(Wd, Ad, [gd[i] for i in idx], rule)
+        if step == 0:
+            ob = O.GradBuf(n)
+            for i in idx:
+                ob.accumulate(pool[i])
+            O.apply_adagrad(Wr, Ar, ob.data, ps["eta"], ps["eps"])
+            torch.cuda.synchronize()
+            assert np.array_equal(Wd.cpu().numpy(), Wr)
+            assert np.array_equal(Ad.cpu().numpy(), Ar)
+            Wr, Ar = Wr[sub].copy(), Ar[sub].copy()
+        else:
+            ob = O.GradBuf(Wr.size)
+            for i in idx:
+                ob.accumulate(pool[i][sub])
+            O.apply_adagrad(Wr, Ar, ob.data, ps["eta"], ps["eps"])
+            torch.cuda.synchronize()
+            assert np.array_equal(Wd.cpu().numpy()[sub], Wr)
+            assert np.array_equal(Ad.cpu().numpy()[sub], Ar)

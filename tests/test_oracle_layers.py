@@ -175,6 +175,7 @@ def test_relu():
     y = np.array([-1.0, 0.0, 2.5, -0.0, 3.0], np.float32)
     a = O.relu_fwd(y)
     np.testing.assert_array_equal(a, [0, 0, 2.5, 0, 3.0])
+    assert np.isnan(O.relu_fwd(np.array([np.nan], np.float32))[0])   # NaN passes through
     dy = O.relu_bwd(a, np.ones(5, np.float32))
     np.testing.assert_array_equal(dy, [0, 0, 1, 0, 1])   # derivative 0 at 0
 
