@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark one data-parallel worker's full SGD step on one MI355X.
 
-A step is compute_gradient (forward, softmax-CE, backward through every
-layer) + accumulate_grad into an empty GradBuf + apply_update, all through the
-C ABI on one stream, with inputs already resident in HBM.  The default
+A step is the gradient (forward, softmax-CE, backward through every layer)
+written into the worker's empty GradBuf (sgd_compute_gradient_into) +
+apply_update, all through the C ABI on one stream, with inputs already
+resident in HBM.  The default
 workload is the 5000-unit MLP (fc 3072-5000x5-10, ReLU, softmax-CE, batch 512,
 momentum SGD mu = 0.9, eta = 0.01), synthetic inputs from the seeded
 generators, He-normal weights.
@@ -69,17 +70,15 @@ def gpu_step_bench(wl, steps, warmup):
     upd_events = []
 
     def step(record=False):
-        net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+        # worker: gradient straight into its (empty) GradBuf; then the apply
+        net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws, stream)
         if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
-            S.accumulate_grad(gb, grad, stream)
-            e[1].record(stream)
             S.apply_update(Wd, gb, state, rule, stream)
-            e[2].record(stream)
+            e[1].record(stream)
             upd_events.append(e)
         else:
-            S.accumulate_grad(gb, grad, stream)
             S.apply_update(Wd, gb, state, rule, stream)
 
     for _ in range(warmup):
@@ -110,12 +109,9 @@ def gpu_step_bench(wl, steps, warmup):
         k["ms"] += ms
         k["flops"] += flops
         k["bytes"] += nbytes
-    acc_b = 8.0 * n            # empty GradBuf: read grad, write buffer
     upd_b = {"plain": 12.0, "momentum": 20.0, "adagrad": 20.0}[wl.rule] * n
-    acc_name, upd_name = "accumulate_copy", f"apply_{wl.rule}"
-    kern[acc_name] = {"launches": steps, "ms": sum(e[0].elapsed_time(e[1]) for e in upd_events), "flops": 0.0,
-                      "bytes": acc_b * steps}
-    kern[upd_name] = {"launches": steps, "ms": sum(e[1].elapsed_time(e[2]) for e in upd_events),
+    upd_name = f"apply_{wl.rule}"
+    kern[upd_name] = {"launches": steps, "ms": sum(e[0].elapsed_time(e[1]) for e in upd_events),
                       "flops": {"plain": 2, "momentum": 4, "adagrad": 7}[wl.rule] * n * steps,
                       "bytes": upd_b * steps}
     return dict(total_ms=total_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n)
@@ -252,7 +248,7 @@ def main():
         print("[bench] parameter-server apply", file=sys.stderr, flush=True)
         out["ps_apply"] = ps_apply_bench()
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mlp5000": 96, "lenet5": 16, "vgg_cifar": 8, "vgg16": 1}[wl.name]
+        sample = args.cpu_sample or {"mlp5000": 512, "lenet5": 16, "vgg_cifar": 16, "vgg16": 1}[wl.name]
         print(f"[bench] CPU oracle baseline on {sample} images", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, sample)
     print(json.dumps(out))

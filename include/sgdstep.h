@@ -165,6 +165,19 @@ typedef struct sgd_gradbuf {
 } sgd_gradbuf;
 
 /*
+ * The same gradient computation written straight into a gradient buffer:
+ * stored if the buffer is empty, added element by element (one rounding per
+ * addition, after the gradient is formed in fp32) if not -- SPRINT Algorithm
+ * 1's ComputeGradient followed by its GradBuf update, without the separate
+ * gradient array.  Bitwise equal to sgd_compute_gradient followed by
+ * sgd_accumulate_grad.  gb->n must equal the parameter count; clears
+ * gb->empty.  Errors as sgd_compute_gradient, and SGD_EINVAL for a buffer of
+ * the wrong length.
+ */
+int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, const int32_t* y, sgd_gradbuf* gb,
+                              float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * GradBuf <- grad if the buffer is empty, else GradBuf + grad (SPRINT
  * Algorithm 1, the GradBuf update).  Clears `empty`.  grad has gb->n floats.
  * Errors: SGD_EINVAL, SGD_EDEVICE.

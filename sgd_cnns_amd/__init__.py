@@ -31,7 +31,8 @@ T_OUT, T_DOUT, T_COL, T_WREP, T_ARGMAX = 0, 1, 2, 3, 4
 LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
-           "sgd_tensor_info", "sgd_compute_gradient", "sgd_accumulate_grad", "sgd_accumulate_grads",
+           "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_accumulate_grad",
+           "sgd_accumulate_grads",
            "sgd_apply_update", "sgd_apply_fused", "sgd_profile", "sgd_profile_read", "sgd_last_error"]
 
 
@@ -81,6 +82,7 @@ def lib():
             "sgd_workspace_bytes": (sz, [P]),
             "sgd_tensor_info": (i, [P, i, i, C.POINTER(i64), C.POINTER(i64), C.POINTER(i)]),
             "sgd_compute_gradient": (i, [P, P, P, P, P, P, P, sz, P]),
+            "sgd_compute_gradient_into": (i, [P, P, P, P, C.POINTER(SgdGradBuf), P, P, sz, P]),
             "sgd_accumulate_grad": (i, [C.POINTER(SgdGradBuf), P, P]),
             "sgd_accumulate_grads": (i, [C.POINTER(SgdGradBuf), C.POINTER(P), i, P]),
             "sgd_apply_update": (i, [P, C.POINTER(SgdGradBuf), P, C.POINTER(SgdRule), P]),
@@ -221,6 +223,13 @@ class Net:
         _require_cuda(W, X, y, grad, loss, ws)
         _check(lib().sgd_compute_gradient(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(grad), _ptr(loss), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)))
+
+
+    def compute_gradient_into(self, W, X, y, gb, loss, ws, stream=None):
+        """Gradient stored into an empty GradBuf, or added into a non-empty one."""
+        _require_cuda(W, X, y, gb.data, loss, ws)
+        _check(lib().sgd_compute_gradient_into(self._h, _ptr(W), _ptr(X), _ptr(y), C.byref(gb._c), _ptr(loss),
+                                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 class GradBuf:

@@ -65,11 +65,25 @@ struct GemmDesc {
   // Algorithmic flops for profiling (0: 2*M*N*K).  Conv products pass the
   // unpadded reduction length here.
   double flops;
+  // When set (dedw form only), B gets an implicit column of ones after its
+  // last column and that column's results -- the row sums of op(A), i.e. the
+  // bias gradient -- are written to ones_out[0..M).  Partial buffers then
+  // hold splits*M*(N+1) floats.
+  float* ones_out;
+  // Add every final result into its destination instead of storing it
+  // (with EPI_STORE only; used to accumulate a gradient into a GradBuf).
+  bool accum = false;
+  // Tile configuration override (-1: chosen from the shape).
+  int cfg = -1;
 };
+
+constexpr int kGemmConfigs = 5;
 
 int gemm(const GemmDesc& d, hipStream_t s);
 
-// Heuristic split count for a product (>= 1), given the slice floor.
-int gemm_pick_splits(int M, int N, int K);
+// Tile configuration and split count the shape (M x Nt output, reduction K)
+// will use; Nt counts the ones column when there is one.
+int gemm_pick_cfg(int M, int Nt);
+int gemm_pick_splits(int M, int Nt, int K);
 
 }  // namespace sgd

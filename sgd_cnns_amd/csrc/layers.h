@@ -16,8 +16,6 @@ int maxpool_fwd(const float* x, float* y, uint8_t* argmax, int N, int C, int H, 
                 hipStream_t s);
 int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, float* dx, int N, int C, int H, int W,
                 int p, bool out_nchw, hipStream_t s);
-int64_t colsum_scratch_floats(int64_t rows, int cols);
-int colsum(const float* dy, float* db, float* scratch, int64_t rows, int cols, hipStream_t s);
 int softmax_ce(const float* z, const int32_t* y, float* dz, float* row_loss, float* loss, int N, int C,
                float scale, hipStream_t s);
 

@@ -1,6 +1,5 @@
 // Bandwidth-bound layer kernels of the SGD step: im2col / col2im, weight
-// repacking, max-pooling forward and backward, the bias-gradient (dedb)
-// column reduction and softmax cross-entropy.
+// repacking, max-pooling forward and backward and softmax cross-entropy.
 //
 // Activation layout.  Every activation the library produces is NHWC
 // (channels fastest), which is the natural row layout of the conv forward
@@ -226,32 +225,6 @@ __global__ void maxpool_bwd_kernel(const float* __restrict__ dy, const uint8_t* 
   }
 }
 
-// -------------------------------------------------- bias gradient (dedb) ----
-// db[col] = sum over rows of dy[row][col], as two fixed-order passes: each
-// thread of pass 1 sums one column over a chunk of `chunk` rows; pass 2 adds
-// the chunk sums in chunk order.
-__global__ void colsum_partial(const float* __restrict__ dy, float* __restrict__ part, int64_t rows, int cols,
-                               int64_t chunk) {
-  const int64_t nchunks = ceil_div(rows, chunk);
-  const int64_t total = nchunks * cols;
-  GRID_STRIDE(i, total) {
-    const int64_t ch = i / cols;
-    const int col = (int)(i - ch * cols);
-    const int64_t r0 = ch * chunk, r1 = std::min<int64_t>(rows, r0 + chunk);
-    float s = 0.f;
-    for (int64_t r = r0; r < r1; ++r) s += dy[r * cols + col];
-    part[i] = s;
-  }
-}
-
-__global__ void colsum_final(const float* __restrict__ part, float* __restrict__ db, int64_t nchunks, int cols) {
-  GRID_STRIDE(col, (int64_t)cols) {
-    float s = part[col];
-    for (int64_t c = 1; c < nchunks; ++c) s += part[c * cols + col];
-    db[col] = s;
-  }
-}
-
 // ------------------------------------------------------ softmax + CE loss ----
 // One wavefront per sample row.  lse = m + log(sum exp(z - m)), the row loss
 // lse - z[y], and dz = scale * (exp(z - lse) - [j == y]).  Wavefront
@@ -370,27 +343,6 @@ int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, flo
                      H, W, p, (int)out_nchw);
   prof_end(s);
   return check_launch("maxpool_bwd");
-}
-
-int64_t colsum_chunk(int64_t rows, int cols) {
-  (void)cols;
-  return rows <= 4096 ? rows : 1024;
-}
-
-int64_t colsum_scratch_floats(int64_t rows, int cols) { return ceil_div(rows, colsum_chunk(rows, cols)) * cols; }
-
-int colsum(const float* dy, float* db, float* scratch, int64_t rows, int cols, hipStream_t s) {
-  const int64_t chunk = colsum_chunk(rows, cols);
-  const int64_t nchunks = ceil_div(rows, chunk);
-  prof_begin("colsum_partial", (double)rows * cols, 4.0 * ((double)rows * cols + (double)nchunks * cols), s);
-  hipLaunchKernelGGL(colsum_partial, dim3(grid_for(nchunks * cols)), dim3(kBlock), 0, s, dy, scratch, rows, cols,
-                     chunk);
-  prof_end(s);
-  if (int e = check_launch("colsum_partial")) return e;
-  prof_begin("colsum_final", (double)nchunks * cols, 4.0 * ((double)nchunks * cols + cols), s);
-  hipLaunchKernelGGL(colsum_final, dim3(grid_for(cols)), dim3(kBlock), 0, s, scratch, db, nchunks, cols);
-  prof_end(s);
-  return check_launch("colsum_final");
 }
 
 int softmax_ce(const float* z, const int32_t* y, float* dz, float* row_loss, float* loss, int N, int C,

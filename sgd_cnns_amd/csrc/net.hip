@@ -124,7 +124,6 @@ struct sgd_net {
   int64_t ws_bytes = 0;
   sgd::Tensor row_loss;
   int64_t partial_off = 0, partial_floats = 0;
-  int64_t colsum_off = 0, colsum_floats = 0;
   sgd::Profiler prof;
 };
 
@@ -293,7 +292,7 @@ int plan(sgd_net* net) {
 
   // Workspace layout and product split factors.
   Bump b;
-  int64_t partial = 0, colsum_sc = 0;
+  int64_t partial = 0;
   for (Stage& s : st) {
     const int64_t N = s.N;
     if (s.kind == SGD_CONV) {
@@ -303,12 +302,11 @@ int plan(sgd_net* net) {
       s.out = make_tensor(b, 4, SGD_LAYOUT_NHWC, N, s.Ho, s.Wo, s.Co);
       s.dout = make_tensor(b, 4, SGD_LAYOUT_NHWC, N, s.Ho, s.Wo, s.Co);
       s.split_fwd = gemm_pick_splits((int)P, s.Co, s.ldk);
-      s.split_dw = gemm_pick_splits(s.Co, s.ldk, (int)P);
+      s.split_dw = gemm_pick_splits(s.Co, s.ldk + 1, (int)P);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)P, s.ldk, s.Co);
       if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * P * s.Co);
-      partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * s.ldk);
+      partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * (s.ldk + 1));  // permuted store
       if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * P * s.ldk);
-      colsum_sc = std::max<int64_t>(colsum_sc, colsum_scratch_floats(P, s.Co));
     } else if (s.kind == SGD_MAXPOOL) {
       const int lay = s.out_nchw ? SGD_LAYOUT_NCHW : SGD_LAYOUT_NHWC;
       if (s.out_nchw) {
@@ -324,12 +322,11 @@ int plan(sgd_net* net) {
       s.out = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, s.Co, s.Co, 1);
       s.dout = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, s.Co, s.Co, 1);
       s.split_fwd = gemm_pick_splits((int)N, s.Co, s.Ci);
-      s.split_dw = gemm_pick_splits(s.Co, s.Ci, (int)N);
+      s.split_dw = gemm_pick_splits(s.Co, s.Ci + 1, (int)N);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)N, s.Ci, s.Co);
       if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * N * s.Co);
-      if (s.split_dw > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * s.Ci);
+      if (s.split_dw > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * (s.Ci + 1));
       if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * N * s.Ci);
-      colsum_sc = std::max<int64_t>(colsum_sc, colsum_scratch_floats(N, s.Co));
     } else if (s.kind == SGD_SOFTMAX_CE) {
       // the logits' gradient lives in the last fc stage's dout
       net->row_loss = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, 1, 1, 1);
@@ -339,8 +336,6 @@ int plan(sgd_net* net) {
   }
   net->partial_floats = partial;
   net->partial_off = b.take(4 * std::max<int64_t>(partial, 1));
-  net->colsum_floats = colsum_sc;
-  net->colsum_off = b.take(4 * std::max<int64_t>(colsum_sc, 1));
   net->ws_bytes = b.top;
   for (const Stage& s : st)
     if (s.kind == SGD_CONV || s.kind == SGD_FC) {
@@ -417,9 +412,10 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
   return 0;
 }
 
-int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, void* ws, hipStream_t st) {
+// accum: add the weight and bias gradients into `grad` instead of storing
+// them (the GradBuf update of SPRINT Algorithm 1 for a non-empty buffer).
+int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, bool accum, void* ws, hipStream_t st) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
-  float* colsum_sc = reinterpret_cast<float*>(static_cast<char*>(ws) + net->colsum_off);
   auto& stages = net->stages;
   for (int si = (int)stages.size() - 1; si >= 0; --si) {
     Stage& s = stages[si];
@@ -428,7 +424,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, voi
     prof_set_layer(s.spec, 1);
     if (s.kind == SGD_FC) {
       const float* dout = at<float>(ws, s.dout);
-      GemmDesc g{};  // dedw: dW[out][in] = dout^T * input
+      GemmDesc g{};  // dedw: dW[out][in] = dout^T * input; dedb via the ones column
       g.A = dout;
       g.lda = s.Co;
       g.a_t = true;
@@ -443,8 +439,9 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, voi
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
       g.partial = partial;
+      g.ones_out = grad + s.b_off;
+      g.accum = accum;
       if ((e = gemm(g, st))) return e;
-      if ((e = colsum(dout, grad + s.b_off, colsum_sc, s.N, s.Co, st))) return e;  // dedb
       if (!s.first_weighted) {
         const Stage& src = stages[s.input];
         GemmDesc d{};  // dedx_fc: d_input[N][in] = dout * W
@@ -476,7 +473,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, voi
       const float* dout = at<float>(ws, s.dout);
       float* col = at<float>(ws, s.col);
       const int64_t P = (int64_t)s.N * s.Ho * s.Wo;
-      GemmDesc g{};  // dedw: dW'[co][kk] = dout^T * col, stored permuted to [co][ci][ky][kx]
+      GemmDesc g{};  // dedw: dW'[co][kk] = dout^T * col, stored permuted to [co][ci][ky][kx]; dedb via ones
       g.A = dout;
       g.lda = s.Co;
       g.a_t = true;
@@ -495,8 +492,9 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, voi
       g.perm_c = s.c;
       g.perm_ci = s.Ci;
       g.perm_k = s.K;
+      g.ones_out = grad + s.b_off;
+      g.accum = accum;
       if ((e = gemm(g, st))) return e;
-      if ((e = colsum(dout, grad + s.b_off, colsum_sc, P, s.Co, st))) return e;  // dedb
       if (!s.first_weighted) {
         GemmDesc d{};  // dedx_conv: dcol[P][kk] = dout * W' (written over the im2col matrix)
         d.A = dout;
@@ -590,19 +588,35 @@ int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offs
   return SGD_OK;
 }
 
-int sgd_compute_gradient(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, float* loss,
-                         void* ws, size_t ws_bytes, void* stream) {
-  if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, "sgd_compute_gradient: null pointer");
+static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, bool accum, float* loss,
+                void* ws, size_t ws_bytes, void* stream, const char* who) {
+  if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, std::string(who) + ": null pointer");
   if ((int64_t)ws_bytes < net->ws_bytes)
-    return fail(SGD_EWORKSPACE, "sgd_compute_gradient: workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+    return fail(SGD_EWORKSPACE, std::string(who) + ": workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
                                     std::to_string(net->ws_bytes));
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SGD_EINVAL, "sgd_compute_gradient: workspace not 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SGD_EINVAL, std::string(who) + ": workspace not 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error from an unrelated earlier call
   sgd::g_prof = &net->prof;
   int e = sgd::run_forward(net, W, X, y, loss, ws, st);
-  if (!e) e = sgd::run_backward(net, W, X, grad, ws, st);
+  if (!e) e = sgd::run_backward(net, W, X, grad, accum, ws, st);
   sgd::g_prof = nullptr;
+  return e;
+}
+
+int sgd_compute_gradient(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, float* loss,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return step(net, W, X, y, grad, false, loss, ws, ws_bytes, stream, "sgd_compute_gradient");
+}
+
+int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, const int32_t* y, sgd_gradbuf* gb,
+                              float* loss, void* ws, size_t ws_bytes, void* stream) {
+  if (!gb || !gb->data) return fail(SGD_EINVAL, "sgd_compute_gradient_into: null gradient buffer");
+  if (net && gb->n != net->n_params)
+    return fail(SGD_EINVAL, "sgd_compute_gradient_into: buffer length " + std::to_string(gb->n) + " != parameter count " +
+                                std::to_string(net->n_params));
+  const int e = step(net, W, X, y, gb->data, gb->empty == 0, loss, ws, ws_bytes, stream, "sgd_compute_gradient_into");
+  if (!e) gb->empty = 0;
   return e;
 }
 

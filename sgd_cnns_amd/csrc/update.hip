@@ -14,8 +14,10 @@
 // (SPRINT Algorithm 2's SumGradient order); k = 0 is an empty GradBuf, i.e.
 // a zero gradient.
 //
-// Each thread handles float4 groups (16-byte loads and stores); a scalar path
-// covers misaligned pointers and the n % 4 tail.
+// Each thread handles two float4 groups per iteration (16-byte loads and
+// stores, all issued before the arithmetic so more bytes are in flight); the
+// data are streamed with non-temporal loads and stores, since every byte is
+// touched once.  A scalar path covers misaligned pointers and the n % 4 tail.
 #include "common.h"
 #include "layers.h"
 
@@ -24,84 +26,87 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kBlock = 256;
+constexpr int kUnroll = 2;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 struct Ptrs {
   const float* g[kMaxK];
 };
 
-__device__ __forceinline__ float fold(const Ptrs& P, int k, int64_t i) {
+__device__ __forceinline__ v4f ld4(const float* p, int64_t i) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p) + i);
+}
+__device__ __forceinline__ void st4(float* p, int64_t i, v4f v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p) + i);
+}
+
+// Left fold g_0 + g_1 + ... + g_{k-1} (k >= 1), one rounding per addition.
+__device__ __forceinline__ v4f fold4(const Ptrs& P, int k, int64_t i) {
+  v4f s = ld4(P.g[0], i);
+  for (int j = 1; j < k; ++j) s = s + ld4(P.g[j], i);
+  return s;
+}
+__device__ __forceinline__ float fold1(const Ptrs& P, int k, int64_t i) {
   float s = P.g[0][i];
   for (int j = 1; j < k; ++j) s = s + P.g[j][i];
   return s;
 }
 
-__device__ __forceinline__ float4 fold4(const Ptrs& P, int k, int64_t i) {
-  float4 s = reinterpret_cast<const float4*>(P.g[0])[i];
-  for (int j = 1; j < k; ++j) {
-    const float4 v = reinterpret_cast<const float4*>(P.g[j])[i];
-    s.x = s.x + v.x;
-    s.y = s.y + v.y;
-    s.z = s.z + v.z;
-    s.w = s.w + v.w;
-  }
-  return s;
-}
-
-// buf = (first_is_copy ? 0-term : buf) + g_0 + ... + g_{k-1}, left to right.
+// buf = (first_is_copy ? g_0 : buf + g_0) + g_1 + ... + g_{k-1}, left to right.
 __global__ void accumulate_kernel(float* __restrict__ buf, Ptrs P, int k, int first_is_copy, int64_t n, int vec) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t done = 0;
   if (vec) {
     const int64_t n4 = n / 4;
-    for (int64_t i = t0; i < n4; i += stride) {
-      float4 s;
-      if (first_is_copy) {
-        s = fold4(P, k, i);
-      } else {
-        s = reinterpret_cast<const float4*>(buf)[i];
-        for (int j = 0; j < k; ++j) {
-          const float4 v = reinterpret_cast<const float4*>(P.g[j])[i];
-          s.x = s.x + v.x;
-          s.y = s.y + v.y;
-          s.z = s.z + v.z;
-          s.w = s.w + v.w;
-        }
-      }
-      reinterpret_cast<float4*>(buf)[i] = s;
+    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+      v4f s[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) s[u] = first_is_copy ? ld4(P.g[0], i + u * stride) : ld4(buf, i + u * stride);
+      for (int j = first_is_copy ? 1 : 0; j < k; ++j)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) s[u] = s[u] + ld4(P.g[j], i + u * stride);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) st4(buf, i + u * stride, s[u]);
+    }
+    for (; i < n4; i += stride) {
+      v4f s = first_is_copy ? ld4(P.g[0], i) : ld4(buf, i);
+      for (int j = first_is_copy ? 1 : 0; j < k; ++j) s = s + ld4(P.g[j], i);
+      st4(buf, i, s);
     }
     done = n4 * 4;
+    i = done + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   }
-  for (int64_t i = done + t0; i < n; i += stride) {
-    float s;
-    if (first_is_copy) {
-      s = fold(P, k, i);
-    } else {
-      s = buf[i];
-      for (int j = 0; j < k; ++j) s = s + P.g[j][i];
-    }
+  for (; i < n; i += stride) {
+    float s = first_is_copy ? P.g[0][i] : buf[i];
+    for (int j = first_is_copy ? 1 : 0; j < k; ++j) s = s + P.g[j][i];
     buf[i] = s;
   }
 }
 
-template <int RULE>
-__device__ __forceinline__ void rule1(float& w, float* st, float g, float eta, float mu, float eps) {
+// One parameter: the rule's statements in order, each rounded once.
+template <int RULE, typename T>
+__device__ __forceinline__ void rule1(T& w, T& st, T g, float eta, float mu, float eps) {
   if (RULE == SGD_PLAIN) {
-    const float t = eta * g;
+    const T t = eta * g;
     w = w - t;
   } else if (RULE == SGD_MOMENTUM) {
-    const float t1 = mu * *st;
-    const float t2 = eta * g;
-    const float v = t1 - t2;
-    *st = v;
-    w = w + v;
+    const T t1 = mu * st;
+    const T t2 = eta * g;
+    st = t1 - t2;
+    w = w + st;
   } else {
-    const float gg = g * g;
-    const float a = *st + gg;
-    *st = a;
-    const float d = sqrtf(a) + eps;
-    const float r = eta / d;
-    const float t = r * g;
+    const T gg = g * g;
+    st = st + gg;
+    T d;
+    if constexpr (sizeof(T) == sizeof(float)) {
+      d = sqrtf(st) + eps;
+    } else {
+      d = T{sqrtf(st.x), sqrtf(st.y), sqrtf(st.z), sqrtf(st.w)} + eps;
+    }
+    const T r = eta / d;
+    const T t = r * g;
     w = w - t;
   }
 }
@@ -110,41 +115,52 @@ template <int RULE>
 __global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, Ptrs P, int k, int64_t n, float eta,
                              float mu, float eps, int vec) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t done = 0;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr bool kState = RULE != SGD_PLAIN;
   if (vec) {
     const int64_t n4 = n / 4;
-    for (int64_t i = t0; i < n4; i += stride) {
-      const float4 g = k > 0 ? fold4(P, k, i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      float4 w = reinterpret_cast<const float4*>(W)[i];
-      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (RULE != SGD_PLAIN) s = reinterpret_cast<const float4*>(state)[i];
-      rule1<RULE>(w.x, &s.x, g.x, eta, mu, eps);
-      rule1<RULE>(w.y, &s.y, g.y, eta, mu, eps);
-      rule1<RULE>(w.z, &s.z, g.z, eta, mu, eps);
-      rule1<RULE>(w.w, &s.w, g.w, eta, mu, eps);
-      reinterpret_cast<float4*>(W)[i] = w;
-      if (RULE != SGD_PLAIN) reinterpret_cast<float4*>(state)[i] = s;
+    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+      v4f w[kUnroll], st[kUnroll], g[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        g[u] = k > 0 ? fold4(P, k, i + u * stride) : v4f{0.f, 0.f, 0.f, 0.f};
+        w[u] = ld4(W, i + u * stride);
+        st[u] = kState ? ld4(state, i + u * stride) : v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        rule1<RULE>(w[u], st[u], g[u], eta, mu, eps);
+        st4(W, i + u * stride, w[u]);
+        if (kState) st4(state, i + u * stride, st[u]);
+      }
     }
-    done = n4 * 4;
+    for (; i < n4; i += stride) {
+      v4f g = k > 0 ? fold4(P, k, i) : v4f{0.f, 0.f, 0.f, 0.f};
+      v4f w = ld4(W, i);
+      v4f st = kState ? ld4(state, i) : v4f{0.f, 0.f, 0.f, 0.f};
+      rule1<RULE>(w, st, g, eta, mu, eps);
+      st4(W, i, w);
+      if (kState) st4(state, i, st);
+    }
+    i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   }
-  for (int64_t i = done + t0; i < n; i += stride) {
-    const float g = k > 0 ? fold(P, k, i) : 0.f;
+  for (; i < n; i += stride) {
+    const float g = k > 0 ? fold1(P, k, i) : 0.f;
     float w = W[i];
-    float s = RULE != SGD_PLAIN ? state[i] : 0.f;
-    rule1<RULE>(w, &s, g, eta, mu, eps);
+    float st = kState ? state[i] : 0.f;
+    rule1<RULE>(w, st, g, eta, mu, eps);
     W[i] = w;
-    if (RULE != SGD_PLAIN) state[i] = s;
+    if (kState) state[i] = st;
   }
 }
 
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// About one unrolled iteration per thread: many waves in flight per CU hide
+// HBM latency better than a few long-running ones.
 int grid_for(int64_t n) {
-  // Enough workgroups to fill 256 CUs several times over; each thread then
-  // loops over float4 groups.
-  const int64_t want = ceil_div(ceil_div(n, 4), kBlock);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, 256 * 16));
+  const int64_t want = ceil_div(ceil_div(n, 4), (int64_t)kBlock * kUnroll);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, 1 << 16));
 }
 
 }  // namespace
@@ -156,8 +172,12 @@ int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy,
     P.g[j] = grads[j];
     vec = vec && a16(grads[j]);
   }
+  const double streams = k + (first_is_copy ? 1 : 2);
+  prof_begin(first_is_copy ? "accumulate_copy" : "accumulate_add", (double)(k - (first_is_copy ? 1 : 0)) * n,
+             4.0 * streams * n, s);
   hipLaunchKernelGGL(accumulate_kernel, dim3(grid_for(n)), dim3(kBlock), 0, s, buf, P, k, (int)first_is_copy, n,
                      (int)vec);
+  prof_end(s);
   return check_launch("accumulate");
 }
 
@@ -170,6 +190,9 @@ int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t
     vec = vec && a16(grads[j]);
   }
   const dim3 g(grid_for(n)), b(kBlock);
+  static const char* const names[3] = {"apply_plain", "apply_momentum", "apply_adagrad"};
+  const double streams = k + (rule == SGD_PLAIN ? 2 : 4);
+  prof_begin(names[rule], (double)n * (k + 4), 4.0 * streams * n, s);
   switch (rule) {
     case SGD_PLAIN:
       hipLaunchKernelGGL(apply_kernel<SGD_PLAIN>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, (int)vec);
@@ -181,6 +204,7 @@ int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t
       hipLaunchKernelGGL(apply_kernel<SGD_ADAGRAD>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, (int)vec);
       break;
   }
+  prof_end(s);
   return check_launch("apply_rule");
 }
 

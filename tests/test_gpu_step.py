@@ -118,3 +118,53 @@ def test_nan_input_propagates_without_error():
     l, g = run_gpu(wl.chw, wl.layers, X, y, W)
     assert np.isnan(l)
     assert np.isnan(O.OracleNet(wl.chw, wl.layers).gradient(W, X, y)[0])
+
+
+def test_compute_gradient_into_matches_compute_plus_accumulate():
+    # empty buffer: bitwise the gradient; non-empty: bitwise g0 + gradient
+    wl = workloads.WORKLOADS["lenet5"]
+    X, y, W = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + wl.chw, wl.layers)
+    n = net.param_count()
+    dev = torch.device("cuda")
+    Wd, Xd, yd = (torch.from_numpy(a).to(dev) for a in (W, X, y))
+    ws = net.workspace()
+    loss = torch.empty(1, device=dev)
+    grad = torch.empty(n, device=dev)
+    net.compute_gradient(Wd, Xd, yd, grad, loss, ws)
+    gb = S.GradBuf(n)
+    gb.data.fill_(7.0)
+    net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws)
+    assert not gb.empty
+    torch.cuda.synchronize()
+    g = grad.cpu().numpy()
+    np.testing.assert_array_equal(gb.data.cpu().numpy(), g)
+    g0 = workloads.normal(7, 3, n, 1e-2)
+    gb.data.copy_(torch.from_numpy(g0))
+    net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gb.data.cpu().numpy(), (g0 + g).astype(np.float32))
+    bad = S.GradBuf(n - 1)
+    with pytest.raises(S.SgdError):
+        net.compute_gradient_into(Wd, Xd, yd, bad, loss, ws)
+
+
+def test_compute_gradient_into_vgg_split_k_paths():
+    # conv dedw with split-K and permuted store, fc dedw direct store: both accumulate
+    wl = workloads.WORKLOADS["vgg_cifar"]
+    X, y, W = workloads.make_inputs(wl.with_batch(2))
+    net = S.Net((2,) + wl.chw, wl.layers)
+    n = net.param_count()
+    dev = torch.device("cuda")
+    Wd, Xd, yd = (torch.from_numpy(a).to(dev) for a in (W, X, y))
+    ws = net.workspace()
+    loss = torch.empty(1, device=dev)
+    grad = torch.empty(n, device=dev)
+    net.compute_gradient(Wd, Xd, yd, grad, loss, ws)
+    g0 = workloads.normal(8, 3, n, 1e-3)
+    gb = S.GradBuf(n)
+    gb.data.copy_(torch.from_numpy(g0))
+    gb.empty = False
+    net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gb.data.cpu().numpy(), (g0 + grad.cpu().numpy()).astype(np.float32))
