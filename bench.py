@@ -185,6 +185,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="images in the oracle sample (0 = per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ps-apply", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size kernel for counter scaling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -194,6 +196,15 @@ def main():
 
     import workloads
     wl = workloads.WORKLOADS[args.workload]
+    if args.copy_calibration_mib:
+        import torch
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] {describe(wl)}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     r = gpu_step_bench(wl, args.steps, args.warmup)
     ms_step = r["total_ms"] / args.steps

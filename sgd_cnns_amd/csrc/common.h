@@ -73,17 +73,14 @@ struct GemmDesc {
   // Add every final result into its destination instead of storing it
   // (with EPI_STORE only; used to accumulate a gradient into a GradBuf).
   bool accum = false;
-  // Tile configuration override (-1: chosen from the shape).
+  // Kernel/tile override (-1: chosen from the shape and the operands).
   int cfg = -1;
 };
 
-constexpr int kGemmConfigs = 5;
-
 int gemm(const GemmDesc& d, hipStream_t s);
 
-// Tile configuration and split count the shape (M x Nt output, reduction K)
-// will use; Nt counts the ones column when there is one.
-int gemm_pick_cfg(int M, int Nt);
+// Split count for a product with an M x Nt output (Nt counts the ones
+// column when there is one) and reduction length K.
 int gemm_pick_splits(int M, int Nt, int K);
 
 }  // namespace sgd
