@@ -252,6 +252,20 @@ typedef struct sgd_kernel_time {
 int sgd_profile(sgd_net* net, int enable);
 int sgd_profile_read(sgd_net* net, sgd_kernel_time* out, int max_records);
 
+/*
+ * One whole SGD step for the common case of one sub-batch per update: the
+ * gradient of (X, y) at W is computed and the rule applied to W in place,
+ * each layer's update issued as soon as that layer's gradient is final (in
+ * the epilogue of its dedw product), so no gradient array is written or read
+ * back.  Bitwise equal to sgd_compute_gradient_into into an empty GradBuf
+ * followed by sgd_apply_update with the same rule (SPRINT Algorithm 1's
+ * gradient into an empty GradBuf, then the apply).  `state` is V (momentum)
+ * or A (Adagrad), param_count floats, updated in place; NULL for plain.
+ * Errors as sgd_compute_gradient and sgd_apply_update.
+ */
+int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, float* state, const sgd_rule* rule,
+                   float* loss, void* ws, size_t ws_bytes, void* stream);
+
 /* Thread-local message describing the last failed call ("" if none). */
 const char* sgd_last_error(void);
 

@@ -33,7 +33,8 @@ LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
-           "sgd_apply_update", "sgd_apply_fused", "sgd_profile", "sgd_profile_read", "sgd_last_error"]
+           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_profile", "sgd_profile_read",
+           "sgd_last_error"]
 
 
 class SgdLayer(C.Structure):
@@ -87,6 +88,7 @@ def lib():
             "sgd_accumulate_grads": (i, [C.POINTER(SgdGradBuf), C.POINTER(P), i, P]),
             "sgd_apply_update": (i, [P, C.POINTER(SgdGradBuf), P, C.POINTER(SgdRule), P]),
             "sgd_apply_fused": (i, [P, P, C.POINTER(P), i, i64, C.POINTER(SgdRule), P]),
+            "sgd_train_step": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P, sz, P]),
             "sgd_profile": (i, [P, i]),
             "sgd_profile_read": (i, [P, C.POINTER(SgdKernelTime), i]),
             "sgd_last_error": (C.c_char_p, []),
@@ -230,6 +232,13 @@ class Net:
         _require_cuda(W, X, y, gb.data, loss, ws)
         _check(lib().sgd_compute_gradient_into(self._h, _ptr(W), _ptr(X), _ptr(y), C.byref(gb._c), _ptr(loss),
                                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+    def train_step(self, W, X, y, state, rule, loss, ws, stream=None):
+        """Gradient + update in one pass: W (and state) updated in place."""
+        _require_cuda(W, X, y, state, loss, ws)
+        _check(lib().sgd_train_step(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(state), C.byref(rule), _ptr(loss),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 class GradBuf:

@@ -73,6 +73,15 @@ struct GemmDesc {
   // Add every final result into its destination instead of storing it
   // (with EPI_STORE only; used to accumulate a gradient into a GradBuf).
   bool accum = false;
+  // Fused training step: when urule >= 0 the final values are gradients
+  // and the rule (SGD_PLAIN / SGD_MOMENTUM / SGD_ADAGRAD) is applied to the
+  // parameters at C (and the ones column's at ones_out) with state at the
+  // same offsets in ustate (ustate_b for the ones column); nothing else is
+  // stored.  Requires EPI_STORE and no accum.
+  int urule = -1;
+  float* ustate = nullptr;
+  float* ustate_b = nullptr;
+  float eta = 0.f, mu = 0.f, eps = 0.f;
   // Kernel/tile override (-1: chosen from the shape and the operands).
   int cfg = -1;
 };

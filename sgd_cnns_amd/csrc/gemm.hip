@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "rules.h"
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -68,6 +69,10 @@ struct KArgs {
   float* ones_out;   // bias-gradient output for the ones column (final store)
   int accum;         // final stores add into the destination (GradBuf += grad)
   int perm_c, perm_ci, perm_k;  // conv weight-gradient store (see GemmDesc)
+  int urule;         // >= 0: apply this update rule instead of storing the gradient
+  float* ustate;     // rule state at the same offsets as C
+  float* ustate_b;   // rule state of the ones column (bias)
+  float eta, mu, eps;
   int a_vec, b_vec;  // float4 global loads allowed (aligned base, ld % 4 == 0)
   int tiles_n;       // tiles along Nt
   int tiles;         // tiles per split
@@ -180,15 +185,23 @@ __device__ __forceinline__ float epilogue(float v, int epi, int row, int col, co
 // Final store of one result: the ones column to ones_out, the conv weight
 // gradient permuted from [co][(ky,kx,ci)] to [co][ci][ky][kx], anything else
 // through the epilogue.
+// With urule >= 0 (the fused training step) the value is the parameter's
+// final gradient and the update rule is applied to the parameter (and its
+// state) in place of storing it.
 __device__ __forceinline__ void finish(float v, int row, int col, const KArgs& p) {
   if (col == p.N) {
-    p.ones_out[row] = p.accum ? p.ones_out[row] + v : v;
+    if (p.urule >= 0) apply_one(p.urule, p.ones_out + row, p.ustate_b + row, v, p.eta, p.mu, p.eps);
+    else p.ones_out[row] = p.accum ? p.ones_out[row] + v : v;
   } else if (p.perm_c > 0) {
     if (col < p.perm_k) {
       const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
-      float* dst = p.C + (int64_t)row * p.ldc + (int64_t)ci * p.perm_c * p.perm_c + tap;
-      *dst = p.accum ? *dst + v : v;
+      const int64_t off = (int64_t)row * p.ldc + (int64_t)ci * p.perm_c * p.perm_c + tap;
+      if (p.urule >= 0) apply_one(p.urule, p.C + off, p.ustate + off, v, p.eta, p.mu, p.eps);
+      else p.C[off] = p.accum ? p.C[off] + v : v;
     }
+  } else if (p.urule >= 0) {
+    const int64_t off = (int64_t)row * p.ldc + col;
+    apply_one(p.urule, p.C + off, p.ustate + off, v, p.eta, p.mu, p.eps);
   } else {
     float* dst = p.C + (int64_t)row * p.ldc + col;
     *dst = epilogue(v, p.epi, row, col, p, p.epi == EPI_ACCUM ? *dst : 0.f);
@@ -197,9 +210,57 @@ __device__ __forceinline__ void finish(float v, int row, int col, const KArgs& p
 
 // Write a wavefront's accumulators.  Result layout of a 32x32 block: lane
 // (li, lh) holds column li and rows 8*(r/4) + 4*lh + r%4 for r = 0..15.
-template <int TM, int TN>
+// Fused update of one 32x32 accumulator block whose columns are plain
+// parameter columns: all 16 weight and state loads are issued before the
+// rule is applied, so their latencies overlap.
+template <int RULE>
+__device__ __forceinline__ void update_block(const f32x16& g, const KArgs& p, int rb, int col, int lh) {
+  float w[16], st[16];
+  bool ok[16];
+  int64_t off[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = rb + 8 * (r >> 2) + 4 * lh + (r & 3);
+    ok[r] = row < p.M && col < p.N;
+    off[r] = (int64_t)row * p.ldc + col;
+    w[r] = ok[r] ? p.C[off[r]] : 0.f;
+    st[r] = (ok[r] && RULE != SGD_PLAIN) ? p.ustate[off[r]] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) rule1<RULE>(w[r], st[r], g[r], p.eta, p.mu, p.eps);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (!ok[r]) continue;
+    p.C[off[r]] = w[r];
+    if (RULE != SGD_PLAIN) p.ustate[off[r]] = st[r];
+  }
+}
+
+// FUSED: the launch applies an update rule to plain parameter columns (no
+// split, no permutation); a separate instance so the other products keep
+// their smaller register budget.
+template <int TM, int TN, bool FUSED = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], const KArgs& p, int r0, int c0, int z, int li,
                                            int lh) {
+  if (FUSED) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int c = 0; c < TN; ++c) {
+        const int col = c0 + c * 32 + li;
+        if (p.urule == SGD_PLAIN) update_block<SGD_PLAIN>(acc[a][c], p, r0 + a * 32, col, lh);
+        else if (p.urule == SGD_MOMENTUM) update_block<SGD_MOMENTUM>(acc[a][c], p, r0 + a * 32, col, lh);
+        else update_block<SGD_ADAGRAD>(acc[a][c], p, r0 + a * 32, col, lh);
+        if (col == p.N) {  // the ones column: the bias
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = r0 + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            if (row < p.M) finish(acc[a][c][r], row, col, p);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -403,7 +464,7 @@ struct DmaT {
   }
 };
 
-template <int BM, int BN, bool AT, bool BT>
+template <int BM, int BN, bool AT, bool BT, bool FUSED = false>
 __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -478,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p) {
     }
   }
   wait_vmcnt<0>();  // the trailing zero-fill loads must land before the workgroup ends
-  store_tile<TM, TN>(acc, p, m0 + wm * WM, n0 + wn * WN, z, li, lh);
+  store_tile<TM, TN, FUSED>(acc, p, m0 + wm * WM, n0 + wn * WN, z, li, lh);
 }
 
 // Sum split-K partial tiles in slice order, then store: the ones column to
@@ -536,18 +597,18 @@ void launch_cfg(int cfg, const KArgs& a, int splits, hipStream_t s) {
   }
 }
 
-template <int BM, int BN, bool AT, bool BT>
+template <int BM, int BN, bool AT, bool BT, bool FUSED = false>
 void launch_dma(const KArgs& a, int splits, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_dma<BM, BN, AT, BT>), dim3(a.tiles * splits), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_dma<BM, BN, AT, BT, FUSED>), dim3(a.tiles * splits), dim3(kThreads), 0, s, a);
 }
 
-template <bool AT, bool BT>
+template <bool AT, bool BT, bool FUSED = false>
 void launch_dma_cfg(int cfg, const KArgs& a, int splits, hipStream_t s) {
   switch (cfg) {
-    case 0: launch_dma<128, 128, AT, BT>(a, splits, s); break;
-    case 1: launch_dma<256, 128, AT, BT>(a, splits, s); break;
-    case 2: launch_dma<128, 64, AT, BT>(a, splits, s); break;
-    default: launch_dma<64, 128, AT, BT>(a, splits, s); break;
+    case 0: launch_dma<128, 128, AT, BT, FUSED>(a, splits, s); break;
+    case 1: launch_dma<256, 128, AT, BT, FUSED>(a, splits, s); break;
+    case 2: launch_dma<128, 64, AT, BT, FUSED>(a, splits, s); break;
+    default: launch_dma<64, 128, AT, BT, FUSED>(a, splits, s); break;
   }
 }
 
@@ -618,6 +679,16 @@ int gemm(const GemmDesc& d, hipStream_t s) {
   a.perm_c = d.perm_c;
   a.perm_ci = d.perm_ci;
   a.perm_k = d.perm_k;
+  a.urule = d.urule;
+  a.ustate = d.ustate;
+  a.ustate_b = d.ustate_b;
+  a.eta = d.eta;
+  a.mu = d.mu;
+  a.eps = d.eps;
+  if (d.urule >= 0 && (d.epi != EPI_STORE || d.accum)) {
+    set_error("gemm: an update rule can only replace a plain store");
+    return SGD_EINVAL;
+  }
   a.a_vec = aligned16(d.A) && d.lda % 4 == 0;
   a.b_vec = aligned16(d.B) && d.ldb % 4 == 0;
   const int splits = d.splits < 1 ? 1 : d.splits;
@@ -664,6 +735,8 @@ int gemm(const GemmDesc& d, hipStream_t s) {
              4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * a.Nt), s);
   if (dma) {
     if (!d.a_t && !d.b_t) launch_dma_cfg<false, false>(cfg, a, splits, s);
+    else if (d.a_t && d.b_t && d.urule >= 0 && !via_partial && d.perm_c == 0)
+      launch_dma_cfg<true, true, true>(cfg, a, splits, s);
     else if (d.a_t && d.b_t) launch_dma_cfg<true, true>(cfg, a, splits, s);
     else if (!d.a_t && d.b_t) launch_dma_cfg<false, true>(cfg, a, splits, s);
     else launch_dma_cfg<true, false>(cfg, a, splits, s);

@@ -345,6 +345,18 @@ int plan(sgd_net* net) {
   return SGD_OK;
 }
 
+// Fused training step: the dedw product applies `rule` to the layer's
+// weights and bias (state at the same offsets) instead of storing gradients.
+void set_update(GemmDesc& g, const sgd_rule* rule, float* state, const Stage& s) {
+  if (!rule) return;
+  g.urule = rule->rule;
+  g.eta = rule->eta;
+  g.mu = rule->mu;
+  g.eps = rule->eps;
+  g.ustate = state ? state + s.w_off : nullptr;
+  g.ustate_b = state ? state + s.b_off : nullptr;
+}
+
 template <typename T>
 T* at(void* ws, const Tensor& t) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + t.off);
@@ -414,7 +426,11 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
 
 // accum: add the weight and bias gradients into `grad` instead of storing
 // them (the GradBuf update of SPRINT Algorithm 1 for a non-empty buffer).
-int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, bool accum, void* ws, hipStream_t st) {
+// rule (fused training step): `grad` is the weight vector itself and each
+// layer's update is applied as soon as its gradient is final; an fc layer's
+// dedx product, which reads that layer's weights, runs before its dedw.
+int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, bool accum, const sgd_rule* rule,
+                 float* state, void* ws, hipStream_t st) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
   auto& stages = net->stages;
   for (int si = (int)stages.size() - 1; si >= 0; --si) {
@@ -424,24 +440,6 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
     prof_set_layer(s.spec, 1);
     if (s.kind == SGD_FC) {
       const float* dout = at<float>(ws, s.dout);
-      GemmDesc g{};  // dedw: dW[out][in] = dout^T * input; dedb via the ones column
-      g.A = dout;
-      g.lda = s.Co;
-      g.a_t = true;
-      g.B = xin;
-      g.ldb = s.Ci;
-      g.b_t = true;
-      g.C = grad + s.w_off;
-      g.ldc = s.Ci;
-      g.M = s.Co;
-      g.N = s.Ci;
-      g.K = s.N;
-      g.epi = EPI_STORE;
-      g.splits = s.split_dw;
-      g.partial = partial;
-      g.ones_out = grad + s.b_off;
-      g.accum = accum;
-      if ((e = gemm(g, st))) return e;
       if (!s.first_weighted) {
         const Stage& src = stages[s.input];
         GemmDesc d{};  // dedx_fc: d_input[N][in] = dout * W
@@ -463,6 +461,25 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.partial = partial;
         if ((e = gemm(d, st))) return e;
       }
+      GemmDesc g{};  // dedw: dW[out][in] = dout^T * input; dedb via the ones column
+      g.A = dout;
+      g.lda = s.Co;
+      g.a_t = true;
+      g.B = xin;
+      g.ldb = s.Ci;
+      g.b_t = true;
+      g.C = grad + s.w_off;
+      g.ldc = s.Ci;
+      g.M = s.Co;
+      g.N = s.Ci;
+      g.K = s.N;
+      g.epi = EPI_STORE;
+      g.splits = s.split_dw;
+      g.partial = partial;
+      g.ones_out = grad + s.b_off;
+      g.accum = accum;
+      set_update(g, rule, state, s);
+      if ((e = gemm(g, st))) return e;
     } else if (s.kind == SGD_MAXPOOL) {
       const Stage& src = stages[s.input];
       const float* pooled = src.relu ? at<float>(ws, s.out) : nullptr;
@@ -494,6 +511,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.perm_k = s.K;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
+      set_update(g, rule, state, s);
       if ((e = gemm(g, st))) return e;
       if (!s.first_weighted) {
         GemmDesc d{};  // dedx_conv: dcol[P][kk] = dout * W' (written over the im2col matrix)
@@ -588,8 +606,9 @@ int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offs
   return SGD_OK;
 }
 
-static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, bool accum, float* loss,
-                void* ws, size_t ws_bytes, void* stream, const char* who) {
+static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, bool accum,
+                const sgd_rule* rule, float* state, float* loss, void* ws, size_t ws_bytes, void* stream,
+                const char* who) {
   if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, std::string(who) + ": null pointer");
   if ((int64_t)ws_bytes < net->ws_bytes)
     return fail(SGD_EWORKSPACE, std::string(who) + ": workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
@@ -599,14 +618,14 @@ static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, 
   (void)hipGetLastError();  // clear a stale error from an unrelated earlier call
   sgd::g_prof = &net->prof;
   int e = sgd::run_forward(net, W, X, y, loss, ws, st);
-  if (!e) e = sgd::run_backward(net, W, X, grad, accum, ws, st);
+  if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, ws, st);
   sgd::g_prof = nullptr;
   return e;
 }
 
 int sgd_compute_gradient(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, float* loss,
                          void* ws, size_t ws_bytes, void* stream) {
-  return step(net, W, X, y, grad, false, loss, ws, ws_bytes, stream, "sgd_compute_gradient");
+  return step(net, W, X, y, grad, false, nullptr, nullptr, loss, ws, ws_bytes, stream, "sgd_compute_gradient");
 }
 
 int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, const int32_t* y, sgd_gradbuf* gb,
@@ -615,7 +634,8 @@ int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, cons
   if (net && gb->n != net->n_params)
     return fail(SGD_EINVAL, "sgd_compute_gradient_into: buffer length " + std::to_string(gb->n) + " != parameter count " +
                                 std::to_string(net->n_params));
-  const int e = step(net, W, X, y, gb->data, gb->empty == 0, loss, ws, ws_bytes, stream, "sgd_compute_gradient_into");
+  const int e = step(net, W, X, y, gb->data, gb->empty == 0, nullptr, nullptr, loss, ws, ws_bytes, stream,
+                     "sgd_compute_gradient_into");
   if (!e) gb->empty = 0;
   return e;
 }
@@ -646,6 +666,14 @@ int sgd_profile_read(sgd_net* net, sgd_kernel_time* out, int max_records) {
     out[i].bytes = r.bytes;
   }
   return n;
+}
+
+static int check_rule(const sgd_rule* rule, const float* state, const char* who);
+
+int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, float* state, const sgd_rule* rule,
+                   float* loss, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_rule(rule, state, "sgd_train_step")) return e;
+  return step(net, W, X, y, W, false, rule, state, loss, ws, ws_bytes, stream, "sgd_train_step");
 }
 
 int sgd_accumulate_grad(sgd_gradbuf* gb, const float* grad, void* stream) {

@@ -1,15 +1,8 @@
 // GradBuf accumulation and the weight-update rules: streaming, HBM-bound
 // elementwise kernels over the flat parameter vector.
 //
-// The arithmetic is one rounding per statement in a fixed order (the library
-// is compiled with -ffp-contract=off, and HIP's default single-precision
-// division and square root are correctly rounded), so results are bitwise
-// reproducible and bitwise equal to a scalar loop written the same way:
-//   plain:    t = eta*g;  W = W - t                       (SPRINT eq. (1))
-//   momentum: t1 = mu*V; t2 = eta*g; V = t1 - t2; W = W + V
-//             (SPRINT Algorithm 2: new weights add nu times the last change)
-//   adagrad:  A = A + g*g; d = sqrt(A) + eps; r = eta/d; t = r*g; W = W - t
-//             (DistBelief review: a per-parameter adaptive rate on the server)
+// The rules themselves are in rules.h (one rounding per statement, shared with
+// the fused training-step epilogue).
 // The gradient g is the left fold of k buffers g_0 + g_1 + ... + g_{k-1}
 // (SPRINT Algorithm 2's SumGradient order); k = 0 is an empty GradBuf, i.e.
 // a zero gradient.
@@ -20,6 +13,7 @@
 // touched once.  A scalar path covers misaligned pointers and the n % 4 tail.
 #include "common.h"
 #include "layers.h"
+#include "rules.h"
 
 namespace sgd {
 namespace {
@@ -82,32 +76,6 @@ __global__ void accumulate_kernel(float* __restrict__ buf, Ptrs P, int k, int fi
     float s = first_is_copy ? P.g[0][i] : buf[i];
     for (int j = first_is_copy ? 1 : 0; j < k; ++j) s = s + P.g[j][i];
     buf[i] = s;
-  }
-}
-
-// One parameter: the rule's statements in order, each rounded once.
-template <int RULE, typename T>
-__device__ __forceinline__ void rule1(T& w, T& st, T g, float eta, float mu, float eps) {
-  if (RULE == SGD_PLAIN) {
-    const T t = eta * g;
-    w = w - t;
-  } else if (RULE == SGD_MOMENTUM) {
-    const T t1 = mu * st;
-    const T t2 = eta * g;
-    st = t1 - t2;
-    w = w + st;
-  } else {
-    const T gg = g * g;
-    st = st + gg;
-    T d;
-    if constexpr (sizeof(T) == sizeof(float)) {
-      d = sqrtf(st) + eps;
-    } else {
-      d = T{sqrtf(st.x), sqrtf(st.y), sqrtf(st.z), sqrtf(st.w)} + eps;
-    }
-    const T r = eta / d;
-    const T t = r * g;
-    w = w - t;
   }
 }
 

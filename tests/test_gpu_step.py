@@ -168,3 +168,49 @@ def test_compute_gradient_into_vgg_split_k_paths():
     net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(gb.data.cpu().numpy(), (g0 + grad.cpu().numpy()).astype(np.float32))
+
+
+@pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad"])
+@pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged", "mlp5000"])
+def test_train_step_equals_gradient_then_apply(rule, case):
+    # the fused step (update applied in the dedw epilogues / split-K reduction)
+    # must give bitwise the same W and optimizer state as gradient-into-GradBuf
+    # followed by the separate apply
+    if case == "lenet5":
+        wl = workloads.WORKLOADS["lenet5"]
+    elif case == "vgg_cifar_b2":
+        wl = workloads.WORKLOADS["vgg_cifar"].with_batch(2)
+    elif case == "mlp_ragged":
+        wl = workloads.Workload("mlp_ragged", 31, 70, (3072, 1, 1),
+                                [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)])
+    else:
+        wl = workloads.WORKLOADS["mlp5000"]
+    print(f"[train_step] {case} {rule}", flush=True)
+    X, y, W = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    n = net.param_count()
+    dev = torch.device("cuda")
+    Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+    st0 = workloads.normal(9, 3, n, 1e-3)
+    if rule == "adagrad":
+        st0 = np.abs(st0) + np.float32(0.1)
+    R = S.Rule(rule, 0.01, 0.9, 1e-8)
+    ws = net.workspace()
+    loss_a = torch.empty(1, device=dev)
+    loss_b = torch.empty(1, device=dev)
+    # reference: gradient into an empty GradBuf, then apply
+    Wa = torch.from_numpy(W).to(dev)
+    sa = torch.from_numpy(st0).to(dev)
+    gb = S.GradBuf(n)
+    net.compute_gradient_into(Wa, Xd, yd, gb, loss_a, ws)
+    S.apply_update(Wa, gb, sa if rule != "plain" else None, R)
+    # fused
+    Wb = torch.from_numpy(W).to(dev)
+    sb = torch.from_numpy(st0).to(dev)
+    net.train_step(Wb, Xd, yd, sb if rule != "plain" else None, R, loss_b, ws)
+    torch.cuda.synchronize()
+    assert loss_a.item() == loss_b.item()
+    assert torch.equal(Wa, Wb), f"max |dW| {(Wa - Wb).abs().max().item()}"
+    if rule != "plain":
+        assert torch.equal(sa, sb)
+    assert not torch.equal(Wb, torch.from_numpy(W).to(dev))
