@@ -5,6 +5,9 @@ linked into sgd_cnns_amd/libsgdstep.so (in-tree, so it travels with the
 source tree).  Flags:
   -ffp-contract=off     each statement of the update rules rounds once
   -packed-fp32-ops off  no packed-FP32 VALU instructions are generated
+  -amdgpu-mfma-vgpr-form  matrix-core accumulators stay in ordinary VGPRs, so
+                        the GEMM epilogues read them without a bulk copy out
+                        of the accumulation registers (which cost occupancy)
 """
 import concurrent.futures as cf
 import glob
@@ -20,7 +23,7 @@ LIB = os.path.join(HERE, "libsgdstep.so")
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-result"]
 
 

@@ -52,12 +52,15 @@ struct GemmDesc {
   const float* bias;
   const float* mask;
   int64_t ldm;
-  // Split-K: when splits > 1 the products of each K slice go to
-  // partial[s][M][N] (row stride N) and a second pass sums the slices in
-  // order s = 0..splits-1 before the epilogue.  `partial` must then hold
-  // splits*M*N floats.
+  // Scratch for partial products (partial_floats floats).  gemm_dma
+  // schedules work with stream-K and needs 2 * grid * tile floats when a
+  // tile is shared between blocks (gemm_scratch_floats gives the need of a
+  // shape).  gemm_staged splits K when splits > 1: the products of each K
+  // slice go to partial[s][M][N] (row stride N) and a second pass sums the
+  // slices in order s = 0..splits-1 before the epilogue.
   int splits;
   float* partial;
+  int64_t partial_floats = 0;
   // Conv weight-gradient store: when perm_c > 0 the final value for
   // (row = co, col = kk) with kk = (ky*c + kx)*Ci + ci is written to
   // C[co*ldc + ci*c*c + ky*c + kx] (only kk < perm_k are stored).
@@ -84,12 +87,20 @@ struct GemmDesc {
   float eta = 0.f, mu = 0.f, eps = 0.f;
   // Kernel/tile override (-1: chosen from the shape and the operands).
   int cfg = -1;
+  // gemm_dma schedule override: sk_grid > 0 forces that many blocks with
+  // the first sk_dp tiles done whole and the rest by stream-K.
+  int sk_grid = -1, sk_dp = 0;
 };
 
 int gemm(const GemmDesc& d, hipStream_t s);
 
-// Split count for a product with an M x Nt output (Nt counts the ones
-// column when there is one) and reduction length K.
+// Split count for gemm_staged for a product with an M x Nt output (Nt
+// counts the ones column when there is one) and reduction length K.
 int gemm_pick_splits(int M, int Nt, int K);
+
+// Scratch floats gemm() needs in GemmDesc::partial for such a product on the
+// current device (gemm_dma's stream-K slots, or gemm_staged's splits).
+// `fused`: the dedw form with an update rule in the epilogue.
+int64_t gemm_scratch_floats(int M, int Nt, int K, bool a_t, bool b_t, bool fused, int splits);
 
 }  // namespace sgd

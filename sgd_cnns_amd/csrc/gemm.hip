@@ -38,9 +38,19 @@
 // k = 8g + 4h + e in lane half h (the 32x32x2 instruction takes k = h from
 // lane half h).
 //
-// Large-K products (conv dedw has K = N*Ho*Wo, up to 1.6M) are split along K:
-// each slice writes its own partial tile and a second pass adds the slices in
-// a fixed order, so results stay deterministic and the fp32 sums stay short.
+// gemm_dma balances the machine with a stream-K schedule: its grid holds no
+// more blocks than fit on the GPU at once, blocks take whole tiles first and
+// then equal contiguous runs of the remaining tiles' k-slices, and tiles
+// shared between runs are finished by a fixup pass that adds the partial
+// products in k order -- deterministic, and the fp32 sums of large-K
+// products (conv dedw has K = N*Ho*Wo, up to 1.6M) stay short.  gemm_staged
+// splits large K into slices written as partial tiles and adds them in a
+// fixed order in a second pass.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -208,82 +218,242 @@ __device__ __forceinline__ void finish(float v, int row, int col, const KArgs& p
   }
 }
 
-// Write a wavefront's accumulators.  Result layout of a 32x32 block: lane
-// (li, lh) holds column li and rows 8*(r/4) + 4*lh + r%4 for r = 0..15.
-// Fused update of one 32x32 accumulator block whose columns are plain
-// parameter columns: all 16 weight and state loads are issued before the
-// rule is applied, so their latencies overlap.
-template <int RULE>
-__device__ __forceinline__ void update_block(const f32x16& g, const KArgs& p, int rb, int col, int lh) {
-  float w[16], st[16];
-  bool ok[16];
-  int64_t off[16];
+// finish() for rows row .. row + nrow - 1 (nrow <= 4) of one column: every
+// load the epilogue needs is issued before the first store.
+__device__ __forceinline__ void finish4(const float (&v)[4], int row, int nrow, int col, const KArgs& p) {
+  float *dst, *stt;
+  int64_t base, ld;
+  const bool plain = col != p.N && p.perm_c == 0;
+  if (col == p.N) {
+    dst = p.ones_out;
+    stt = p.ustate_b;
+    base = row;
+    ld = 1;
+  } else {
+    int64_t cb = col;
+    if (p.perm_c > 0) {
+      if (col >= p.perm_k) return;
+      const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
+      cb = (int64_t)ci * p.perm_c * p.perm_c + tap;
+    }
+    dst = p.C;
+    stt = p.ustate;
+    base = (int64_t)row * p.ldc + cb;
+    ld = p.ldc;
+  }
+  const bool old_c = p.urule >= 0 || (plain ? p.epi == EPI_ACCUM : p.accum);
+  float aux[4] = {0.f, 0.f, 0.f, 0.f}, sv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = rb + 8 * (r >> 2) + 4 * lh + (r & 3);
-    ok[r] = row < p.M && col < p.N;
-    off[r] = (int64_t)row * p.ldc + col;
-    w[r] = ok[r] ? p.C[off[r]] : 0.f;
-    st[r] = (ok[r] && RULE != SGD_PLAIN) ? p.ustate[off[r]] : 0.f;
+  for (int e = 0; e < 4; ++e) {
+    if (e >= nrow) break;
+    if (old_c) aux[e] = dst[base + e * ld];
+    else if (plain && p.epi == EPI_MASK) aux[e] = p.mask[(int64_t)(row + e) * p.ldm + col];
+    if (p.urule == SGD_MOMENTUM || p.urule == SGD_ADAGRAD) sv[e] = stt[base + e * ld];
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) rule1<RULE>(w[r], st[r], g[r], p.eta, p.mu, p.eps);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (!ok[r]) continue;
-    p.C[off[r]] = w[r];
-    if (RULE != SGD_PLAIN) p.ustate[off[r]] = st[r];
+  for (int e = 0; e < 4; ++e) {
+    if (e >= nrow) break;
+    float x = v[e];
+    if (p.urule >= 0) {
+      if (p.urule == SGD_PLAIN) rule1<SGD_PLAIN>(aux[e], sv[e], x, p.eta, p.mu, p.eps);
+      else if (p.urule == SGD_MOMENTUM) rule1<SGD_MOMENTUM>(aux[e], sv[e], x, p.eta, p.mu, p.eps);
+      else rule1<SGD_ADAGRAD>(aux[e], sv[e], x, p.eta, p.mu, p.eps);
+      dst[base + e * ld] = aux[e];
+      if (p.urule != SGD_PLAIN) stt[base + e * ld] = sv[e];
+      continue;
+    }
+    if (!plain) x = p.accum ? aux[e] + x : x;
+    else if (p.epi == EPI_MASK) x = aux[e] > 0.f ? x : 0.f;
+    else x = epilogue(x, p.epi, row + e, col, p, aux[e]);
+    dst[base + e * ld] = x;
   }
 }
 
-// FUSED: the launch applies an update rule to plain parameter columns (no
-// split, no permutation); a separate instance so the other products keep
-// their smaller register budget.
-template <int TM, int TN, bool FUSED = false>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], const KArgs& p, int r0, int c0, int z, int li,
+// Epilogue variants of gemm_dma, fixed at compile time so each instance
+// carries only the code (and registers) its products need:
+enum EpiMode : int {
+  EM_GENERIC = 0,  // finish() per element: any combination of the options
+  EM_STORE = 1,    // C = v
+  EM_BIAS = 2,     // C = v + bias[col], then ReLU when epi == EPI_BIAS_RELU
+  EM_MASK = 3,     // C = mask > 0 ? v : 0
+  EM_DW = 4,       // dedw: ones column to ones_out, permuted conv store, accum
+  EM_UPDATE = 5,   // dedw with the update rule applied in place of the store
+};
+
+// Row of result register r inside a lane's 32x32 block (the MFMA layout:
+// lane (li, lh) holds column li and rows 4*lh + 8*(r/4) + r%4).
+__device__ __forceinline__ int blk_row(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Epilogue memory goes through buffer instructions whose resource starts at
+// the wavefront's first row and ends after its last valid row: rows past M
+// fall outside the record range (loads read 0, stores are dropped) and lanes
+// past the last column use an out-of-range offset, so no per-element branch
+// is needed.  The host keeps 128 rows of any epilogue operand below 2^30
+// bytes, so adding a row offset to an out-of-range offset cannot wrap.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+constexpr uint32_t kOffOut = 0x80000000u;
+__device__ __forceinline__ brsrc brsrc_rows(const float* base, int rows, uint32_t ld) {
+  const int64_t bytes = rows > 0 ? (int64_t)rows * ld * 4 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
+                                           (int)std::min<int64_t>(bytes, 0x7ffffff0), 0x00020000);
+}
+__device__ __forceinline__ float bload(brsrc r, uint32_t vo) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, 0, 0));
+}
+__device__ __forceinline__ void bstore(float v, brsrc r, uint32_t vo) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)vo, 0, 0);
+}
+
+// Keeps the scheduler from hoisting the next group's loads and arithmetic
+// above this point, which bounds the values in flight (and the registers the
+// epilogue needs) to one group.
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
+// Specialised epilogues of one wavefront's TM x TN blocks; r0, c0 (its first
+// row and column) are wavefront-uniform.
+template <int TM, int TN, int EM>
+__device__ __forceinline__ void store_wave(const f32x16 (&acc)[TM][TN], const KArgs& p, int r0, int c0, int li,
                                            int lh) {
-  if (FUSED) {
+  const int rows = min(p.M - r0, TM * 32);
+  if (EM == EM_STORE || EM == EM_BIAS || EM == EM_MASK) {
+    const uint32_t ldc = (uint32_t)p.ldc, ldm = (uint32_t)p.ldm;
+    const brsrc rc = brsrc_rows(p.C + (int64_t)r0 * p.ldc + c0, rows, ldc);
+    const brsrc rm = brsrc_rows(EM == EM_MASK ? p.mask + (int64_t)r0 * p.ldm + c0 : p.C, EM == EM_MASK ? rows : 0, ldm);
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int c = 0; c < TN; ++c) {
+      const int col = c0 + c * 32 + li;
+      const bool ok = col < p.N;
+      const uint32_t vc = ok ? (4u * lh * ldc + c * 32 + li) * 4u : kOffOut;
+      const uint32_t vm = ok ? (4u * lh * ldm + c * 32 + li) * 4u : kOffOut;
+      const float bias = (EM == EM_BIAS && ok) ? p.bias[col] : 0.f;
 #pragma unroll
-      for (int c = 0; c < TN; ++c) {
-        const int col = c0 + c * 32 + li;
-        if (p.urule == SGD_PLAIN) update_block<SGD_PLAIN>(acc[a][c], p, r0 + a * 32, col, lh);
-        else if (p.urule == SGD_MOMENTUM) update_block<SGD_MOMENTUM>(acc[a][c], p, r0 + a * 32, col, lh);
-        else update_block<SGD_ADAGRAD>(acc[a][c], p, r0 + a * 32, col, lh);
-        if (col == p.N) {  // the ones column: the bias
+      for (int a = 0; a < TM; ++a) {
+        float m[16];
+        if (EM == EM_MASK) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = r0 + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (row < p.M) finish(acc[a][c][r], row, col, p);
-          }
+          for (int r = 0; r < 16; ++r) m[r] = bload(rm, vm + (a * 32 + blk_row(r)) * ldm * 4u);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = acc[a][c][r];
+          if (EM == EM_BIAS) {
+            x = x + bias;
+            if (p.epi == EPI_BIAS_RELU) x = x <= 0.f ? 0.f : x;  // NaN passes through
+          }
+          if (EM == EM_MASK) x = m[r] > 0.f ? x : 0.f;
+          bstore(x, rc, vc + (a * 32 + blk_row(r)) * ldc * 4u);
+        }
+        sched_fence();
       }
-    return;
+    }
+  } else if (EM == EM_DW || EM == EM_UPDATE) {
+    const uint32_t ldc = (uint32_t)p.ldc;
+    const brsrc rd = brsrc_rows(p.C + (int64_t)r0 * p.ldc, rows, ldc);
+    const bool st_on = EM == EM_UPDATE && p.ustate;
+    const brsrc rs = brsrc_rows(st_on ? p.ustate + (int64_t)r0 * p.ldc : p.C, st_on ? rows : 0, ldc);
+    const brsrc rdb = brsrc_rows(p.ones_out ? p.ones_out + r0 : p.C, p.ones_out ? rows : 0, 1);
+    const brsrc rsb = brsrc_rows(EM == EM_UPDATE && p.ustate_b ? p.ustate_b + r0 : p.C,
+                                 EM == EM_UPDATE && p.ustate_b ? rows : 0, 1);
+    // Blocks of 8 rows of one lane's column: parameter (and state) loads
+    // first, then the rule or the accumulation, then the stores.
+    auto rows8 = [&](auto rule_c, const f32x16& v, int h, int a, brsrc d, brsrc st_r, uint32_t vo, uint32_t ld) {
+      constexpr int RULE = decltype(rule_c)::value;  // -1: plain store (with accum)
+      float w[8], st[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t o = vo + (a * 32 + blk_row(8 * h + e)) * ld * 4u;
+        w[e] = (RULE >= 0 || p.accum) ? bload(d, o) : 0.f;
+        st[e] = (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD) ? bload(st_r, o) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (RULE >= 0) rule1<(RULE >= 0 ? RULE : 0)>(w[e], st[e], v[8 * h + e], p.eta, p.mu, p.eps);
+        else w[e] = p.accum ? w[e] + v[8 * h + e] : v[8 * h + e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t o = vo + (a * 32 + blk_row(8 * h + e)) * ld * 4u;
+        bstore(w[e], d, o);
+        if (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD) bstore(st[e], st_r, o);
+      }
+      sched_fence();
+    };
+    auto block = [&](const f32x16& v, int a, brsrc d, brsrc st_r, uint32_t vo, uint32_t ld) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (EM == EM_DW) rows8(std::integral_constant<int, -1>{}, v, h, a, d, st_r, vo, ld);
+        else if (p.urule == SGD_PLAIN) rows8(std::integral_constant<int, SGD_PLAIN>{}, v, h, a, d, st_r, vo, ld);
+        else if (p.urule == SGD_MOMENTUM) rows8(std::integral_constant<int, SGD_MOMENTUM>{}, v, h, a, d, st_r, vo, ld);
+        else rows8(std::integral_constant<int, SGD_ADAGRAD>{}, v, h, a, d, st_r, vo, ld);
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < TN; ++c) {
+      const int col = c0 + c * 32 + li;
+      // Plain or permuted conv weight columns.
+      bool ok = col < p.N;
+      uint32_t cb = (uint32_t)col;
+      if (p.perm_c > 0) {
+        ok = ok && col < p.perm_k;
+        const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
+        cb = (uint32_t)(ci * p.perm_c * p.perm_c + tap);
+      }
+      const uint32_t vo = ok ? (4u * lh * ldc + cb) * 4u : kOffOut;
+      if (c0 + c * 32 < p.N) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a) block(acc[a][c], a, rd, rs, vo, ldc);
+      }
+      // The ones column (bias) when it falls in this block.
+      if (p.ones_out && p.N >= c0 + c * 32 && p.N < c0 + c * 32 + 32) {
+        const uint32_t vb = col == p.N ? 4u * lh * 4u : kOffOut;
+#pragma unroll
+        for (int a = 0; a < TM; ++a) block(acc[a][c], a, rdb, rsb, vb, 1);
+      }
+    }
   }
+}
+
+// Generic epilogue: each 32x32 block of a wavefront is parked in the
+// wavefront's own 1024 floats of LDS (`wl`) and finished by a short loop, so
+// the code holds one finish() per block instead of one per element (an
+// unrolled per-element finish() runs to tens of KiB of instructions that
+// every wavefront fetches cold).  The caller makes sure no other wavefront
+// still reads that LDS.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile_generic(const f32x16 (&acc)[TM][TN], const KArgs& p, int r0, int c0, int z,
+                                                   int li, int lh, float* wl) {
+  const int lane = li + 32 * lh;
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int c = 0; c < TN; ++c)
+    for (int c = 0; c < TN; ++c) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = r0 + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int col = c0 + c * 32 + li;
-        if (row >= p.M || col >= p.Nt) continue;
-        const float v = acc[a][c][r];
-        if (p.split) p.C[(int64_t)z * p.M * p.Nt + (int64_t)row * p.Nt + col] = v;
-        else finish(v, row, col, p);
+      for (int r = 0; r < 16; ++r) wl[(4 * lh + blk_row(r)) * 32 + li] = acc[a][c][r];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the block is in LDS before any lane reads it
+#pragma unroll 1
+      for (int e = 0; e < 16; ++e) {
+        const int k = e * 64 + lane;  // rows 2e, 2e+1 of the block: lanes cover 32 consecutive columns
+        const int row = r0 + a * 32 + (k >> 5), col = c0 + c * 32 + (k & 31);
+        const float v = wl[k];
+        if (row < p.M && col < p.Nt) {
+          if (p.split) p.C[(int64_t)z * p.M * p.Nt + (int64_t)row * p.Nt + col] = v;
+          else finish(v, row, col, p);
+        }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next block is parked
+    }
 }
 
-template <int BM, int BN, int BK, bool AT, bool BT>
+template <int BM, int BN, int BK, bool AT, bool BT, int EM>
 __global__ __launch_bounds__(kThreads) void gemm_staged(KArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   using SA = Slice<BM, BK, AT>;
   using SB = Slice<BN, BK, BT>;
-  __shared__ __align__(16) float As[2][SA::SIZE];
-  __shared__ __align__(16) float Bs[2][SB::SIZE];
+  __shared__ __align__(16) float lds[2 * (SA::SIZE + SB::SIZE)];
+  static_assert(2 * (SA::SIZE + SB::SIZE) >= 4 * 1024, "LDS too small for the generic epilogue");
+  float(*As)[SA::SIZE] = reinterpret_cast<float(*)[SA::SIZE]>(lds);
+  float(*Bs)[SB::SIZE] = reinterpret_cast<float(*)[SB::SIZE]>(lds + 2 * SA::SIZE);
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber so each XCD
   // walks a contiguous run of tiles (neighbouring tiles share operand panels
@@ -300,7 +470,8 @@ __global__ __launch_bounds__(kThreads) void gemm_staged(KArgs p) {
   const bool ones = p.Nt > p.N;
   const bool interior = p.a_vec && p.b_vec && m0 + BM <= p.M && n0 + BN <= p.N;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform in the wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, lh = lane >> 5;
 
@@ -359,7 +530,8 @@ __global__ __launch_bounds__(kThreads) void gemm_staged(KArgs p) {
     cur ^= 1;
   }
 
-  store_tile<TM, TN>(acc, p, m0 + wm * WM, n0 + wn * WN, z, li, lh);
+  if (EM == EM_GENERIC) store_tile_generic<TM, TN>(acc, p, m0 + wm * WM, n0 + wn * WN, z, li, lh, lds + wave * 1024);
+  else store_wave<TM, TN, EM>(acc, p, m0 + wm * WM, n0 + wn * WN, li, lh);
 }
 
 // ------------------------------------------------------------ gemm_dma ----
@@ -398,28 +570,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // K-contiguous operand (stored [R][K]): LDS stage [R][16]; quad q of row r at
-// slot q ^ swz(r).
+// slot q ^ swz(r).  `rs` addresses the work item's first element; the host
+// keeps every offset inside an item below 2^31 bytes.
 template <int R>
 struct DmaK {
   static constexpr int SIZE = R * kDmaBK;
   static constexpr int NI = R * (kDmaBK / 4) / 256;  // 16-byte loads per thread per stage
   __device__ static __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-  // Stage of slice kk (relative to the block's first k); rows >= rvalid and
-  // k >= kvalid read zeros.
-  __device__ static __forceinline__ void load(i32x4 rs, float* S, int64_t ld, int rvalid, int kk, int kvalid) {
+  // Slice at k offset kk of the item; rows >= rvalid and k >= kvalid read zeros.
+  __device__ static __forceinline__ void load(i32x4 rs, float* S, uint32_t ld, int rvalid, int kk, int kvalid) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int qi = (wave * NI + j) * 64 + lane;
       const int r = qi >> 2, g = (qi & 3) ^ swz(r);
       const bool ok = r < rvalid && kk + 4 * g < kvalid;
-      dma16(rs, S + (wave * NI + j) * 256, ok ? (uint32_t)(((int64_t)r * ld + kk + 4 * g) * 4) : kOffBad);
+      dma16(rs, S + (wave * NI + j) * 256, ok ? ((uint32_t)r * ld + (uint32_t)(kk + 4 * g)) * 4u : kOffBad);
     }
   }
   __device__ static __forceinline__ float4 operand(const float* S, int row, int g, int h) {
     return *reinterpret_cast<const float4*>(&S[row * kDmaBK + 4 * ((2 * g + h) ^ swz(row))]);
   }
-  __device__ static __forceinline__ void ones_fixup(float*, int, int, int, int) {}
+  __device__ static __forceinline__ void ones_fixup(float*, int, int, int) {}
 };
 
 // Row-contiguous operand (stored [K][R]): LDS stage [16][R]; column quad c of
@@ -430,14 +602,14 @@ struct DmaT {
   static constexpr int SIZE = R * kDmaBK;
   static constexpr int NI = R * kDmaBK / 4 / 256;
   __device__ static __forceinline__ int swzT(int k) { return ((k >> 2) & 1) << 3; }
-  __device__ static __forceinline__ void load(i32x4 rs, float* S, int64_t ld, int rvalid, int kk, int kvalid) {
+  __device__ static __forceinline__ void load(i32x4 rs, float* S, uint32_t ld, int rvalid, int kk, int kvalid) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int qi = (wave * NI + j) * 64 + lane;
       const int k = qi / Q, c = (qi % Q) ^ swzT(k);
       const bool ok = kk + k < kvalid && 4 * c < rvalid;
-      dma16(rs, S + (wave * NI + j) * 256, ok ? (uint32_t)(((int64_t)(kk + k) * ld + 4 * c) * 4) : kOffBad);
+      dma16(rs, S + (wave * NI + j) * 256, ok ? ((uint32_t)(kk + k) * ld + (uint32_t)(4 * c)) * 4u : kOffBad);
     }
   }
   __device__ static __forceinline__ float4 operand(const float* S, int col, int g, int h) {
@@ -451,9 +623,9 @@ struct DmaT {
   }
   // The implicit ones column at tile-relative column `oc` (a multiple of 4, so
   // its quad was loaded as zeros): the lane that loaded that quad sets its
-  // first element to 1 for the valid k of the stage.  Called after the lane's
-  // own loads for the stage completed, before the barrier that publishes it.
-  __device__ static __forceinline__ void ones_fixup(float* S, int oc, int kk, int kvalid, int /*unused*/) {
+  // first element to 1 for the valid k of the slice.  Called after the lane's
+  // own loads for the slice completed, before the barrier that publishes it.
+  __device__ static __forceinline__ void ones_fixup(float* S, int oc, int kk, int kvalid) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -464,82 +636,233 @@ struct DmaT {
   }
 };
 
-template <int BM, int BN, bool AT, bool BT, bool FUSED = false>
-__global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p) {
+// Stream-K schedule of one gemm_dma launch.  Blocks first take whole tiles
+// round-robin (tiles [0, dp_tiles)); the k-slices of the remaining tiles,
+// flattened tile by tile, are then cut into gridDim.x equal contiguous
+// ranges, one per block, so every block ends after the same amount of work
+// however the tile count divides the machine.  A range that covers a whole
+// tile stores it directly; a tile shared by several ranges is written by
+// each as a partial product to that block's slot (2b for the tile its range
+// starts in, 2b + 1 for the tile it ends in) and gemm_sk_fixup adds the slots
+// in k order before the epilogue, so results do not depend on timing.
+struct SkArgs {
+  int ipt;           // k-slices per tile: ceil(K / 16)
+  int dp_tiles;      // tiles done whole before the stream-K part
+  int sk_iters;      // (tiles - dp_tiles) * ipt; 0 or >= gridDim.x, and
+                     // sk_iters * gridDim.x < 2^31 (32-bit range arithmetic)
+  float* part;       // 2 * gridDim.x slots of BM * BN floats
+};
+
+__host__ __device__ inline int sk_start(int b, int S, int G) { return (int)((uint32_t)b * (uint32_t)S / (uint32_t)G); }
+
+// The block whose range holds stream-K slice x.
+__host__ __device__ inline int sk_block_of(int x, int S, int G) {
+  int b = (int)(((uint32_t)x * (uint32_t)G + (uint32_t)G - 1u) / (uint32_t)S);
+  while (b > 0 && sk_start(b, S, G) > x) --b;
+  while (b + 1 < G && sk_start(b + 1, S, G) <= x) ++b;
+  return b;
+}
+
+// Partial-slot layout: float4 (wave, a, c, q) of lane l at
+// ((((wave * TM + a) * TN + c) * 4 + q) * 64 + l) * 4 -- every store and load
+// instruction covers 1 KiB contiguously.
+template <int TM, int TN>
+__device__ __forceinline__ int64_t slot_index(int wave, int a, int c, int q, int lane) {
+  return ((((int64_t)(wave * TM + a) * TN + c) * 4 + q) * 64 + lane) * 4;
+}
+
+template <int BM, int BN, bool AT, bool BT, int EM>
+__global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   using SA = typename std::conditional<AT, DmaT<BM>, DmaK<BM>>::type;
   using SB = typename std::conditional<BT, DmaT<BN>, DmaK<BN>>::type;
   constexpr int kLoads = SA::NI + SB::NI;
-  __shared__ __align__(16) float As[kDmaStages][SA::SIZE];
-  __shared__ __align__(16) float Bs[kDmaStages][SB::SIZE];
+  __shared__ __align__(16) float lds[kDmaStages * (SA::SIZE + SB::SIZE)];
+  static_assert(kDmaStages * (SA::SIZE + SB::SIZE) >= 4 * 1024, "LDS too small for the generic epilogue");
+  float(*As)[SA::SIZE] = reinterpret_cast<float(*)[SA::SIZE]>(lds);
+  float(*Bs)[SB::SIZE] = reinterpret_cast<float(*)[SB::SIZE]>(lds + kDmaStages * SA::SIZE);
 
-  // XCD-contiguous runs of tiles (see gemm_staged), tiles ordered along M
-  // first so a run shares B panels.
-  const int nblk = gridDim.x;
+  // Blocks are dealt round-robin to the 8 XCDs; renumber so each XCD holds a
+  // contiguous run of block indices, i.e. neighbouring tiles (which share
+  // operand panels in that XCD's L2).  Tiles are ordered along M first.
+  const int G = gridDim.x;
   int b = blockIdx.x;
-  if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
-  const int z = b / p.tiles;
-  const int t = b - z * p.tiles;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
   const int tiles_m = p.tiles / p.tiles_n;
-  const int tn_i = t / tiles_m, tm_i = t - tn_i * tiles_m;
-  const int m0 = tm_i * BM, n0 = tn_i * BN;
-  const int kbeg = z * p.k_per_split;
-  const int kval = max(0, min(p.K, kbeg + p.k_per_split) - kbeg);
-  const i32x4 ra = buffer_rsrc(AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
-  const i32x4 rb = buffer_rsrc(BT ? p.B + (int64_t)kbeg * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + kbeg);
-  const int arows = p.M - m0, brows = p.N - n0;
-  const int ones_col = (p.Nt > p.N && p.N >= n0 && p.N < n0 + BN) ? p.N - n0 : -1;
-  const int nsl = (kval + kDmaBK - 1) / kDmaBK;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform in the wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, lh = lane >> 5;
-
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int c = 0; c < TN; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
-  // Prologue: stages 0 .. S-2 in flight.  Stages past the end of K read
-  // zeros, which keeps the per-thread load count (and so the vmcnt
-  // arithmetic) the same for every slice.
+  // Work items: whole tiles b, b + G, ... below dp_tiles, then the block's
+  // stream-K range, tile by tile.  One store site keeps the epilogue's code
+  // (and registers) out of the pipelined loop.
+  const int S = s.sk_iters;
+  int it = S > 0 ? sk_start(b, S, G) : 0;
+  const int end = S > 0 ? sk_start(b + 1, S, G) : 0;
+  int t_next = b;
+  bool first_sk = true;
+  for (;;) {
+    int t, k0, k1, slot = -1;
+    if (t_next < s.dp_tiles) {
+      t = t_next;
+      k0 = 0;
+      k1 = s.ipt;
+      t_next += G;
+    } else if (it < end) {
+      const int tt = (int)((uint32_t)it / (uint32_t)s.ipt);
+      k0 = it - tt * s.ipt;
+      k1 = min(s.ipt, k0 + (end - it));
+      t = s.dp_tiles + tt;
+      it += k1 - k0;
+      slot = first_sk ? 2 * b : 2 * b + 1;
+      first_sk = false;
+    } else {
+      break;
+    }
+    const int tn_i = t / tiles_m, tm_i = t - tn_i * tiles_m;
+    const int m0 = tm_i * BM, n0 = tn_i * BN;
+    const int kbeg = k0 * kDmaBK;
+    const int kval = min(p.K, k1 * kDmaBK) - kbeg;
+    const int nsl = k1 - k0;
+    const int arows = p.M - m0, brows = p.N - n0;
+    const int ones_col = (p.Nt > p.N && p.N >= n0 && p.N < n0 + BN) ? p.N - n0 : -1;
+    const i32x4 ra = buffer_rsrc(AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
+    const i32x4 rb = buffer_rsrc(BT ? p.B + (int64_t)kbeg * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + kbeg);
+    const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
+
 #pragma unroll
-  for (int st = 0; st < kDmaStages - 1; ++st) {
-    SA::load(ra, As[st], p.lda, arows, st * kDmaBK, kval);
-    SB::load(rb, Bs[st], p.ldb, brows, st * kDmaBK, kval);
-  }
-  for (int i = 0; i < nsl; ++i) {
-    const int cur = i % kDmaStages;
-    wait_vmcnt<kLoads * (kDmaStages - 2)>();  // this thread's loads of slice i are in LDS
-    if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval, 0);
-    lds_barrier();  // everyone's loads of slice i landed; everyone finished slice i-1
-    const int nx = i + kDmaStages - 1;  // refill the buffer slice i-1 used
-    SA::load(ra, As[nx % kDmaStages], p.lda, arows, nx * kDmaBK, kval);
-    SB::load(rb, Bs[nx % kDmaStages], p.ldb, brows, nx * kDmaBK, kval);
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int g = 0; g < kDmaBK / 8; ++g) {
-      float4 av[TM], bv[TN];
+      for (int c = 0; c < TN; ++c)
 #pragma unroll
-      for (int a = 0; a < TM; ++a) av[a] = SA::operand(As[cur], wm * WM + a * 32 + li, g, lh);
+        for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+    __syncthreads();  // every wave is done with the ring from the previous item
+    // Prologue: slices 0 .. S-2 in flight.  Slices past the end of the item
+    // read zeros, which keeps the per-thread load count (and so the vmcnt
+    // arithmetic) the same for every slice.
 #pragma unroll
-      for (int c = 0; c < TN; ++c) bv[c] = SB::operand(Bs[cur], wn * WN + c * 32 + li, g, lh);
+    for (int st = 0; st < kDmaStages - 1; ++st) {
+      SA::load(ra, As[st], lda, arows, st * kDmaBK, kval);
+      SB::load(rb, Bs[st], ldb, brows, st * kDmaBK, kval);
+    }
+    for (int i = 0; i < nsl; ++i) {
+      const int cur = i % kDmaStages;
+      wait_vmcnt<kLoads * (kDmaStages - 2)>();  // this thread's loads of slice i are in LDS
+      if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval);
+      lds_barrier();  // everyone's loads of slice i landed; everyone finished slice i-1
+      const int nx = i + kDmaStages - 1;  // refill the buffer slice i-1 used
+      SA::load(ra, As[nx % kDmaStages], lda, arows, nx * kDmaBK, kval);
+      SB::load(rb, Bs[nx % kDmaStages], ldb, brows, nx * kDmaBK, kval);
+#pragma unroll
+      for (int g = 0; g < kDmaBK / 8; ++g) {
+        float4 av[TM], bv[TN];
+#pragma unroll
+        for (int a = 0; a < TM; ++a) av[a] = SA::operand(As[cur], wm * WM + a * 32 + li, g, lh);
+#pragma unroll
+        for (int c = 0; c < TN; ++c) bv[c] = SB::operand(Bs[cur], wn * WN + c * 32 + li, g, lh);
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int c = 0; c < TN; ++c) {
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].x, bv[c].x, acc[a][c], 0, 0, 0);
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].y, bv[c].y, acc[a][c], 0, 0, 0);
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].z, bv[c].z, acc[a][c], 0, 0, 0);
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].w, bv[c].w, acc[a][c], 0, 0, 0);
+          }
+      }
+    }
+    wait_vmcnt<0>();  // the trailing zero-fill loads land before the ring is reused
+
+    if (k0 == 0 && k1 == s.ipt) {
+      if (EM == EM_GENERIC) {
+        __syncthreads();  // the ring is free for the epilogue's LDS blocks
+        store_tile_generic<TM, TN>(acc, p, m0 + wm * WM, n0 + wn * WN, 0, li, lh, lds + wave * 1024);
+      } else {
+        store_wave<TM, TN, EM>(acc, p, m0 + wm * WM, n0 + wn * WN, li, lh);
+      }
+    } else {
+      float* dst = s.part + (int64_t)slot * (BM * BN);
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int c = 0; c < TN; ++c) {
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].x, bv[c].x, acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].y, bv[c].y, acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].z, bv[c].z, acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].w, bv[c].w, acc[a][c], 0, 0, 0);
-        }
+        for (int c = 0; c < TN; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(dst + slot_index<TM, TN>(wave, a, c, q, lane)) =
+                make_float4(acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]);
     }
   }
-  wait_vmcnt<0>();  // the trailing zero-fill loads must land before the workgroup ends
-  store_tile<TM, TN, FUSED>(acc, p, m0 + wm * WM, n0 + wn * WN, z, li, lh);
+}
+
+// Completes the stream-K tiles that were shared between blocks: block
+// (j, y) takes elements [1024 y, 1024 y + 1024) of stream-K tile j (one float4
+// per thread), adds the tile's slots in block (= k) order and stores through
+// finish(), which computes what the gemm_dma epilogue variants compute.
+constexpr int kFixChunk = 1024;
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int G) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  __shared__ int slots[1024];
+  const int j = blockIdx.x;
+  const int S = s.sk_iters;
+  const int x0 = j * s.ipt;
+  const int blo = sk_block_of(x0, S, G), bhi = sk_block_of(x0 + s.ipt - 1, S, G);
+  if (blo == bhi) return;  // inside one range: stored by gemm_dma
+  const int n = bhi - blo + 1;  // <= G <= 1024 (checked on the host)
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int bb = blo + i;
+    slots[i] = sk_start(bb, S, G) / s.ipt == j ? 2 * bb : 2 * bb + 1;
+  }
+  __syncthreads();
+  const int t = s.dp_tiles + j;
+  const int tiles_m = p.tiles / p.tiles_n;
+  const int tn_i = t / tiles_m, tm_i = t - tn_i * tiles_m;
+  const int m0 = tm_i * BM, n0 = tn_i * BN;
+  // Each thread adds one float4 (4 rows of one column) over the slots, with
+  // several slots' loads in flight.
+  const int idx = blockIdx.y * kFixChunk + 4 * threadIdx.x;
+  const float4* src = reinterpret_cast<const float4*>(s.part + idx);
+  constexpr int64_t kSlot4 = BM * BN / 4;
+  float4 v = src[(int64_t)slots[0] * kSlot4];
+  int i = 1;
+  for (; i + 4 <= n; i += 4) {
+    float4 u[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = src[(int64_t)slots[i + k] * kSlot4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v.x += u[k].x;
+      v.y += u[k].y;
+      v.z += u[k].z;
+      v.w += u[k].w;
+    }
+  }
+  for (; i < n; ++i) {
+    const float4 u = src[(int64_t)slots[i] * kSlot4];
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  // Inverse of slot_index: float4 (wave, a, c, q) of lane l holds rows
+  // 8q .. 8q+3 (plus 4 * lane half) of column l % 32 of block (a, c).
+  const int lane = (idx >> 2) & 63;
+  int rest = idx >> 8;
+  const int q = rest & 3;
+  rest >>= 2;
+  const int c = rest % TN;
+  rest /= TN;
+  const int a = rest % TM, wave = rest / TM;
+  const int row = m0 + (wave >> 1) * WM + a * 32 + 4 * (lane >> 5) + 8 * q;
+  const int col = n0 + (wave & 1) * WN + c * 32 + (lane & 31);
+  if (col < p.Nt && row < p.M) {
+    const float r4[4] = {v.x, v.y, v.z, v.w};
+    finish4(r4, row, min(4, p.M - row), col, p);
+  }
 }
 
 // Sum split-K partial tiles in slice order, then store: the ones column to
@@ -559,103 +882,274 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 struct Cfg {
   int bm, bn, bk;
 };
-// gemm_staged configurations: 0: 128x128x16  1: 256x128x16  2: 128x256x16
-// 3: 128x64x32  4: 64x128x32
-constexpr int kStagedConfigs = 5;
-const Cfg kCfg[kStagedConfigs] = {{128, 128, 16}, {256, 128, 16}, {128, 256, 16}, {128, 64, 32}, {64, 128, 32}};
-// gemm_dma configurations: 0: 128x128  1: 256x128  2: 128x64  3: 64x128
-constexpr int kDmaConfigs = 4;
-const Cfg kDma[kDmaConfigs] = {{128, 128, kDmaBK}, {256, 128, kDmaBK}, {128, 64, kDmaBK}, {64, 128, kDmaBK}};
+// gemm_staged configurations: 0: 128x128x16  1: 128x64x32  2: 64x128x32
+constexpr int kStagedConfigs = 3;
+const Cfg kCfg[kStagedConfigs] = {{128, 128, 16}, {128, 64, 32}, {64, 128, 32}};
+// gemm_dma configurations: 0: 128x128  1: 128x64  2: 64x128
+constexpr int kDmaConfigs = 3;
+const Cfg kDma[kDmaConfigs] = {{128, 128, kDmaBK}, {128, 64, kDmaBK}, {64, 128, kDmaBK}};
 
-const char* const kNames[kStagedConfigs][3] = {
-    {"gemm_staged_128x128_nt", "gemm_staged_128x128_tn", "gemm_staged_128x128_nn"},
-    {"gemm_staged_256x128_nt", "gemm_staged_256x128_tn", "gemm_staged_256x128_nn"},
-    {"gemm_staged_128x256_nt", "gemm_staged_128x256_tn", "gemm_staged_128x256_nn"},
-    {"gemm_staged_128x64_nt", "gemm_staged_128x64_tn", "gemm_staged_128x64_nn"},
-    {"gemm_staged_64x128_nt", "gemm_staged_64x128_tn", "gemm_staged_64x128_nn"},
+const char* const kNames[kStagedConfigs][4] = {
+    {"gemm_staged_128x128_nt", "gemm_staged_128x128_tn", "gemm_staged_128x128_nn", "gemm_staged_128x128_tt"},
+    {"gemm_staged_128x64_nt", "gemm_staged_128x64_tn", "gemm_staged_128x64_nn", "gemm_staged_128x64_tt"},
+    {"gemm_staged_64x128_nt", "gemm_staged_64x128_tn", "gemm_staged_64x128_nn", "gemm_staged_64x128_tt"},
 };
-const char* const kDmaNames[kDmaConfigs][3] = {
-    {"gemm_dma_128x128_nt", "gemm_dma_128x128_tn", "gemm_dma_128x128_nn"},
-    {"gemm_dma_256x128_nt", "gemm_dma_256x128_tn", "gemm_dma_256x128_nn"},
-    {"gemm_dma_128x64_nt", "gemm_dma_128x64_tn", "gemm_dma_128x64_nn"},
-    {"gemm_dma_64x128_nt", "gemm_dma_64x128_tn", "gemm_dma_64x128_nn"},
+const char* const kDmaNames[kDmaConfigs][4] = {
+    {"gemm_dma_128x128_nt", "gemm_dma_128x128_tn", "gemm_dma_128x128_nn", "gemm_dma_128x128_tt"},
+    {"gemm_dma_128x64_nt", "gemm_dma_128x64_tn", "gemm_dma_128x64_nn", "gemm_dma_128x64_tt"},
+    {"gemm_dma_64x128_nt", "gemm_dma_64x128_tn", "gemm_dma_64x128_nn", "gemm_dma_64x128_tt"},
 };
 
-template <int BM, int BN, int BK, bool AT, bool BT>
-void launch(const KArgs& a, int splits, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_staged<BM, BN, BK, AT, BT>), dim3(a.tiles * splits), dim3(kThreads), 0, s, a);
+typedef void (*StagedKernel)(KArgs);
+
+// gemm_staged instances for a configuration, operand form and epilogue
+// variant (the same variants as gemm_dma's; split partials use the generic
+// path).
+template <int BM, int BN, int BK>
+StagedKernel staged_fn_of(int form, int em) {
+  switch (form) {
+    case 0:
+      if (em == EM_BIAS) return gemm_staged<BM, BN, BK, false, false, EM_BIAS>;
+      if (em == EM_STORE) return gemm_staged<BM, BN, BK, false, false, EM_STORE>;
+      return gemm_staged<BM, BN, BK, false, false, EM_GENERIC>;
+    case 1:
+      if (em == EM_DW) return gemm_staged<BM, BN, BK, true, true, EM_DW>;
+      if (em == EM_UPDATE) return gemm_staged<BM, BN, BK, true, true, EM_UPDATE>;
+      if (em == EM_STORE) return gemm_staged<BM, BN, BK, true, true, EM_STORE>;
+      return gemm_staged<BM, BN, BK, true, true, EM_GENERIC>;
+    case 2:
+      if (em == EM_MASK) return gemm_staged<BM, BN, BK, false, true, EM_MASK>;
+      if (em == EM_STORE) return gemm_staged<BM, BN, BK, false, true, EM_STORE>;
+      return gemm_staged<BM, BN, BK, false, true, EM_GENERIC>;
+    default:
+      return gemm_staged<BM, BN, BK, true, false, EM_GENERIC>;
+  }
 }
-
-template <bool AT, bool BT>
-void launch_cfg(int cfg, const KArgs& a, int splits, hipStream_t s) {
+StagedKernel staged_fn(int cfg, int form, int em) {
   switch (cfg) {
-    case 0: launch<128, 128, 16, AT, BT>(a, splits, s); break;
-    case 1: launch<256, 128, 16, AT, BT>(a, splits, s); break;
-    case 2: launch<128, 256, 16, AT, BT>(a, splits, s); break;
-    case 3: launch<128, 64, 32, AT, BT>(a, splits, s); break;
-    default: launch<64, 128, 32, AT, BT>(a, splits, s); break;
+    case 0: return staged_fn_of<128, 128, 16>(form, em);
+    case 1: return staged_fn_of<128, 64, 32>(form, em);
+    default: return staged_fn_of<64, 128, 32>(form, em);
   }
 }
 
-template <int BM, int BN, bool AT, bool BT, bool FUSED = false>
-void launch_dma(const KArgs& a, int splits, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_dma<BM, BN, AT, BT, FUSED>), dim3(a.tiles * splits), dim3(kThreads), 0, s, a);
+typedef void (*DmaKernel)(KArgs, SkArgs);
+typedef void (*FixKernel)(KArgs, SkArgs, int);
+
+// gemm_dma / gemm_sk_fixup instances for a configuration, operand form
+// (0: A*B^T, 1: A^T*B, 2: A*B, 3: A^T*B^T) and epilogue variant; the
+// variants instantiated per form are the ones the step uses, anything else
+// runs the generic epilogue.
+struct DmaFns {
+  DmaKernel main;
+  FixKernel fix;
+  int bm, bn;
+};
+template <int BM, int BN, bool AT, bool BT, int EM>
+DmaFns dma_inst() {
+  return {gemm_dma<BM, BN, AT, BT, EM>, gemm_sk_fixup<BM, BN>, BM, BN};
+}
+template <int BM, int BN>
+DmaFns dma_fns_of(int form, int em) {
+  switch (form) {
+    case 0:
+      if (em == EM_BIAS) return dma_inst<BM, BN, false, false, EM_BIAS>();
+      if (em == EM_STORE) return dma_inst<BM, BN, false, false, EM_STORE>();
+      return dma_inst<BM, BN, false, false, EM_GENERIC>();
+    case 1:
+      if (em == EM_DW) return dma_inst<BM, BN, true, true, EM_DW>();
+      if (em == EM_UPDATE) return dma_inst<BM, BN, true, true, EM_UPDATE>();
+      if (em == EM_STORE) return dma_inst<BM, BN, true, true, EM_STORE>();
+      return dma_inst<BM, BN, true, true, EM_GENERIC>();
+    case 2:
+      if (em == EM_MASK) return dma_inst<BM, BN, false, true, EM_MASK>();
+      if (em == EM_STORE) return dma_inst<BM, BN, false, true, EM_STORE>();
+      return dma_inst<BM, BN, false, true, EM_GENERIC>();
+    default:
+      return dma_inst<BM, BN, true, false, EM_GENERIC>();
+  }
+}
+DmaFns dma_fns(int cfg, int form, int em) {
+  switch (cfg) {
+    case 0: return dma_fns_of<128, 128>(form, em);
+    case 1: return dma_fns_of<128, 64>(form, em);
+    default: return dma_fns_of<64, 128>(form, em);
+  }
 }
 
-template <bool AT, bool BT, bool FUSED = false>
-void launch_dma_cfg(int cfg, const KArgs& a, int splits, hipStream_t s) {
-  switch (cfg) {
-    case 0: launch_dma<128, 128, AT, BT, FUSED>(a, splits, s); break;
-    case 1: launch_dma<256, 128, AT, BT, FUSED>(a, splits, s); break;
-    case 2: launch_dma<128, 64, AT, BT, FUSED>(a, splits, s); break;
-    default: launch_dma<64, 128, AT, BT, FUSED>(a, splits, s); break;
+// The epilogue variant for a product (see EpiMode).  The specialised ones
+// address 128 rows of their output (and mask) from one buffer resource, so
+// those must span less than 1 GiB.
+int epi_mode(const GemmDesc& d, int form) {
+  const int64_t kMaxLd = (int64_t)1 << 21;
+  if (d.ldc >= kMaxLd || (d.epi == EPI_MASK && d.ldm >= kMaxLd)) return EM_GENERIC;
+  const bool extra = d.ones_out || d.perm_c > 0 || d.accum || d.urule >= 0;
+  if (form == 1) {
+    if (d.epi != EPI_STORE) return EM_GENERIC;
+    if (d.urule >= 0) return EM_UPDATE;
+    return extra ? EM_DW : EM_STORE;
   }
+  if (extra) return EM_GENERIC;
+  if (form == 0 && (d.epi == EPI_BIAS || d.epi == EPI_BIAS_RELU)) return EM_BIAS;
+  if (form == 2 && d.epi == EPI_MASK) return EM_MASK;
+  if (d.epi == EPI_STORE && form != 3) return EM_STORE;
+  return EM_GENERIC;
 }
 
 int64_t tiles_of(const Cfg& c, int M, int N) { return ceil_div(M, c.bm) * ceil_div(N, c.bn); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Compute units of the current device (cached per device; the MI355X's 256
+// without a device, when a workspace is planned on a host without a GPU) and
+// the gemm_dma blocks of a configuration that fit on one CU by their LDS ring
+// (160 KiB per CU).  The schedule depends on nothing else, so a product
+// rounds the same way whichever epilogue variant runs it.
+struct Machine {
+  int cus;
+  int occ;
+};
+Machine machine_for(int cfg) {
+  static std::mutex mu;
+  static std::map<int, int> cus_of;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  (void)hipGetLastError();
+  int cus = 256;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cus_of.find(dev);
+    if (it != cus_of.end()) {
+      cus = it->second;
+    } else {
+      int n = 0;
+      if (dev >= 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cus = n;
+      (void)hipGetLastError();
+      cus_of[dev] = cus;
+    }
+  }
+  const Cfg& c = kDma[cfg];
+  const int lds = kDmaStages * kDmaBK * 4 * (c.bm + c.bn);
+  return {cus, std::max(1, std::min(4, (160 * 1024) / lds))};
+}
+
+// Launch plan of one gemm_dma product: grid size, whole tiles first, then
+// the stream-K part.  Chosen by a cost model in units of one 16-deep k-slice
+// of one block at full occupancy:
+//  * a block with k of the `occ` resident blocks per CU runs a slice in
+//    k/occ of that time, scaled by the matrix-core efficiency measured at k
+//    resident blocks (0.72, 0.85, 0.88 for 1, 2, 3+);
+//  * each tile or stream-K segment costs a further kItemCost slices
+//    (prologue latency and epilogue stores);
+//  * the fixup pass moves the partial tiles through HBM at ~4 TB/s.
+// Candidates: one block per tile, and stream-K on grids of 1 .. occ blocks
+// per CU with the last one or two rounds of whole tiles given to stream-K.
+struct SkPlan {
+  int grid;
+  int dp;
+  int64_t sk_iters;
+};
+constexpr double kItemCost = 6.0;
+SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, int64_t cap_floats) {
+  static const double eff[5] = {0.0, 0.72, 0.85, 0.88, 0.88};
+  const int occ = std::max(1, std::min(m.occ, 4));
+  auto slice_time = [&](int64_t k) {
+    k = std::max<int64_t>(1, std::min<int64_t>(k, occ));
+    return (double)k / occ * eff[occ] / eff[k];
+  };
+  const int64_t G3 = (int64_t)m.cus * occ;
+  SkPlan best{(int)std::min<int64_t>(T, INT32_MAX), (int)std::min<int64_t>(T, INT32_MAX), 0};
+  const int64_t full = T / G3, rem = T % G3;
+  double best_cost = (double)full * (I + kItemCost) * slice_time(occ) +
+                     (rem ? (I + kItemCost) * slice_time(ceil_div(rem, m.cus)) : 0.0);
+  // Seconds per slice at full occupancy, for the fixup's memory time.
+  const double unit_s = 2.0 * tile_floats * kDmaBK * (double)G3 / (eff[occ] * 157.3e12);
+  for (int k = 1; k <= occ; ++k) {
+    const int64_t g = (int64_t)m.cus * k;
+    if (g > 1024 || 2 * g * tile_floats > cap_floats) continue;  // the fixup's slot list holds 1024
+    for (int64_t r = std::max<int64_t>(0, T / g - 1); r <= T / g; ++r) {
+      const int64_t dp = r * g;
+      if (dp >= T) continue;
+      const int64_t S = (T - dp) * I;
+      if (S < g || S * g >= ((int64_t)1 << 31)) continue;
+      const double per = (double)S / g;
+      const double segs = std::ceil(per / I) + 1.0;
+      const int64_t shared = std::min<int64_t>(T - dp, g);
+      const double fix = 4.0 * tile_floats * (double)(2 * shared + g) / 4e12 / unit_s + 1.0;
+      const double cost = ((double)r * (I + kItemCost) + per + segs * kItemCost) * slice_time(k) + fix;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = {(int)g, (int)dp, S};
+      }
+    }
+  }
+  return best;
+}
+
 // Tile choice for gemm_staged, from measurements on the step's shapes.
 int staged_cfg(int M, int Nt) {
-  if (Nt <= 64) return 3;
-  if (M <= 64) return 4;
-  if (tiles_of(kCfg[0], M, Nt) >= 4096 && M >= 1024 && Nt >= 1024) return M >= Nt ? 1 : 2;
+  if (Nt <= 64) return 1;
+  if (M <= 64) return 2;
   return 0;
 }
 
 // Tile choice for gemm_dma: 128x128 unless one side of the output is narrow.
 int dma_cfg(int M, int Nt) {
-  if (Nt <= 64) return 2;
-  if (M <= 64) return 3;
+  if (Nt <= 64) return 1;
+  if (M <= 64) return 2;
   return 0;
 }
 
 // gemm_dma preconditions: aligned operands and strides; K a multiple of 4 for
 // a K-contiguous operand, the row count a multiple of 4 for a row-contiguous
 // one (whole 16-byte quads are either in or out of range); the ones column at
-// a quad boundary; every in-block offset below 2^31 bytes.
-bool dma_ok(const GemmDesc& d, const Cfg& c, int kps) {
-  auto operand_ok = [&](const float* X, int64_t ld, bool t, int rows, int tile) {
+// a quad boundary.
+bool dma_ok(const GemmDesc& d) {
+  auto operand_ok = [&](const float* X, int64_t ld, bool t, int rows) {
     if (!aligned16(X) || ld % 4) return false;
-    if (t ? rows % 4 : d.K % 4) return false;
-    const int64_t span = t ? ((int64_t)(kps - 1) * ld + tile) * 4 : ((int64_t)(tile - 1) * ld + kps) * 4;
-    return span < (int64_t)kOffBad;
+    return t ? rows % 4 == 0 : d.K % 4 == 0;
   };
   if (d.ones_out && d.N % 4) return false;
-  return operand_ok(d.A, d.lda, d.a_t, d.M, c.bm) && operand_ok(d.B, d.ldb, d.b_t, d.N, c.bn);
+  return operand_ok(d.A, d.lda, d.a_t, d.M) && operand_ok(d.B, d.ldb, d.b_t, d.N);
 }
+
+// Every offset a work item of up to `slices` k-slices addresses from its
+// buffer resource is below 2^31 bytes.
+bool dma_span_ok(const GemmDesc& d, const Cfg& c, int64_t slices) {
+  auto span = [&](int64_t ld, bool t, int tile) {
+    const int64_t k = slices * kDmaBK;
+    return (t ? (k - 1) * ld + tile : (int64_t)(tile - 1) * ld + k) * 4;
+  };
+  return span(d.lda, d.a_t, c.bm) < (int64_t)kOffBad && span(d.ldb, d.b_t, c.bn) < (int64_t)kOffBad;
+}
+
+int form_of(bool a_t, bool b_t) { return (!a_t && !b_t) ? 0 : (a_t && b_t) ? 1 : (!a_t && b_t) ? 2 : 3; }
 
 }  // namespace
 
 int gemm_pick_splits(int M, int Nt, int K) {
-  const int64_t tiles = tiles_of(kDma[dma_cfg(M, Nt)], M, Nt);
+  const int64_t tiles = tiles_of(kCfg[staged_cfg(M, Nt)], M, Nt);
   int s = 1;
-  // Aim for >= 4 workgroups per CU while keeping each K slice >= 256 long
-  // and the partial tiles' extra traffic ((s + 1) * M * Nt floats written
-  // and read back) small next to the product: s <= K / 512.
+  // gemm_staged only (gemm_dma balances with stream-K): aim for >= 4
+  // workgroups per CU while keeping each K slice >= 256 long and the partial
+  // tiles' extra traffic ((s + 1) * M * Nt floats written and read back)
+  // small next to the product: s <= K / 512.
   while (tiles * s < 1024 && K / (2 * s) >= 256 && 2 * s <= K / 512 && s < 256) s *= 2;
+  // A product with few tiles is latency-bound: split while slices keep >= 64
+  // k-values and the partial tiles stay small (<= 64 MiB).
+  while (tiles * s < 256 && K / (2 * s) >= 64 && (int64_t)2 * s * M * Nt <= ((int64_t)1 << 24) && s < 256) s *= 2;
   return s;
+}
+
+int64_t gemm_scratch_floats(int M, int Nt, int K, bool a_t, bool b_t, bool fused, int splits) {
+  const int64_t staged = splits > 1 ? (int64_t)splits * M * Nt : 0;
+  (void)fused;
+  const int cfg = dma_cfg(M, Nt);
+  const Cfg& c = kDma[cfg];
+  const SkPlan p = sk_choose(tiles_of(c, M, Nt), ceil_div(K, kDmaBK), machine_for(cfg), (int64_t)c.bm * c.bn, INT64_MAX);
+  const int64_t sk = p.sk_iters > 0 ? 2 * (int64_t)p.grid * c.bm * c.bn : 0;
+  return std::max(staged, sk);
 }
 
 int gemm(const GemmDesc& d, hipStream_t s) {
@@ -689,10 +1183,14 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     set_error("gemm: an update rule can only replace a plain store");
     return SGD_EINVAL;
   }
+  if (d.accum && d.epi != EPI_STORE) {
+    set_error("gemm: accumulation is only defined for plain stores");
+    return SGD_EINVAL;
+  }
   a.a_vec = aligned16(d.A) && d.lda % 4 == 0;
   a.b_vec = aligned16(d.B) && d.ldb % 4 == 0;
-  const int splits = d.splits < 1 ? 1 : d.splits;
-  // d.cfg selects a gemm_dma configuration (0..3) or, as 4 + c, gemm_staged
+  const int form = form_of(d.a_t, d.b_t);
+  // d.cfg selects a gemm_dma configuration (0..2) or, as 3 + c, gemm_staged
   // configuration c; -1 picks from the shape, preferring gemm_dma.
   bool dma;
   int cfg;
@@ -704,48 +1202,105 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     cfg = d.cfg - kDmaConfigs;
   } else {
     cfg = dma_cfg(d.M, a.Nt);
-    dma = dma_ok(d, kDma[cfg], (int)round_up(ceil_div(d.K, splits), kDmaBK));
+    dma = dma_ok(d);
     if (!dma) cfg = staged_cfg(d.M, a.Nt);
   }
-  const Cfg& c = dma ? kDma[cfg] : kCfg[cfg];
-  a.k_per_split = (int)round_up(ceil_div(d.K, splits), c.bk);
-  if (dma && !dma_ok(d, c, a.k_per_split)) {
+  if (dma && !dma_ok(d)) {
     set_error("gemm: operands do not meet the direct-load preconditions");
     return SGD_EINVAL;
   }
+  const double flops = d.flops > 0 ? d.flops : 2.0 * d.M * d.N * (double)d.K;
+  const double bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * a.Nt);
+
+  // gemm_dma schedule.  The plan depends only on the shape and the machine
+  // (the instance without an update rule sets the occupancy), so a product
+  // rounds the same way with and without the fused update.
+  SkPlan plan{};
+  if (dma) {
+    const Cfg& c = kDma[cfg];
+    const int64_t T = tiles_of(c, d.M, a.Nt), ipt = ceil_div(d.K, kDmaBK), tile = (int64_t)c.bm * c.bn;
+    const int64_t cap = d.partial ? d.partial_floats : 0;
+    if (d.sk_grid > 1024) {
+      set_error("gemm: stream-K grid above 1024 blocks");
+      return SGD_EINVAL;
+    }
+    if (d.sk_grid > 0) {  // forced schedule
+      const int64_t dp = std::max<int64_t>(0, std::min<int64_t>(d.sk_dp, T));
+      plan = {d.sk_grid, (int)dp, (T - dp) * ipt};
+      if (plan.sk_iters > 0 && plan.sk_iters < plan.grid) {
+        set_error("gemm: stream-K part has fewer k-slices than blocks");
+        return SGD_EINVAL;
+      }
+    } else {
+      plan = sk_choose(T, ipt, machine_for(cfg), tile, cap);
+    }
+    if (plan.sk_iters > 0 && plan.sk_iters * plan.grid >= ((int64_t)1 << 31)) {
+      set_error("gemm: stream-K schedule too long for 32-bit range arithmetic");
+      return SGD_EINVAL;
+    }
+    if (plan.sk_iters > 0 && 2 * (int64_t)plan.grid * tile > cap) {
+      set_error("gemm: partial-tile buffer too small for the stream-K schedule");
+      return SGD_EINVAL;
+    }
+    const int64_t item = plan.dp > 0 ? ipt : std::min<int64_t>(ipt, ceil_div(plan.sk_iters, plan.grid));
+    if (!dma_span_ok(d, c, item)) {
+      if (d.cfg >= 0) {
+        set_error("gemm: a work item spans more than 2 GiB of an operand");
+        return SGD_EINVAL;
+      }
+      dma = false;
+      cfg = staged_cfg(d.M, a.Nt);
+    }
+  }
+  const Cfg& c = dma ? kDma[cfg] : kCfg[cfg];
   a.tiles_n = (int)ceil_div(a.Nt, c.bn);
   a.tiles = (int)(ceil_div(d.M, c.bm) * a.tiles_n);
-  const bool via_partial = splits > 1;
-  if (via_partial) {
-    a.C = d.partial;
-    a.ldc = a.Nt;
-    a.split = 1;
-  } else {
+
+  if (dma) {
     a.C = d.C;
     a.ldc = d.ldc;
     a.split = 0;
+    a.k_per_split = (int)round_up(d.K, kDmaBK);
+    const DmaFns f = dma_fns(cfg, form, epi_mode(d, form));
+    const int64_t T = a.tiles, ipt = ceil_div(d.K, kDmaBK), tile = (int64_t)c.bm * c.bn;
+    const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial};
+    prof_begin(kDmaNames[cfg][form], flops, bytes, s);
+    hipLaunchKernelGGL(f.main, dim3(plan.grid), dim3(kThreads), 0, s, a, sk);
+    prof_end(s);
+    if (int e = check_launch("gemm")) return e;
+    if (plan.sk_iters > 0) {
+      // Partial tiles written and read back by the fixup (for the profile).
+      int64_t shared = 0, slots = 0;
+      for (int64_t j = 0; j < T - plan.dp; ++j) {
+        const int blo = sk_block_of((int)(j * ipt), sk.sk_iters, plan.grid);
+        const int bhi = sk_block_of((int)(j * ipt + ipt - 1), sk.sk_iters, plan.grid);
+        if (blo != bhi) {
+          ++shared;
+          slots += bhi - blo + 1;
+        }
+      }
+      prof_begin("gemm_sk_fixup", (double)(slots - shared) * tile, 4.0 * (double)(slots + shared) * tile, s);
+      hipLaunchKernelGGL(f.fix, dim3((unsigned)(T - plan.dp), (unsigned)(tile / kFixChunk)), dim3(kThreads), 0, s, a, sk,
+                         plan.grid);
+      prof_end(s);
+      if (int e = check_launch("gemm_sk_fixup")) return e;
+    }
+    return 0;
   }
-  const int form = (!d.a_t && !d.b_t) ? 0 : (d.a_t && d.b_t) ? 1 : 2;
-  if (d.accum && d.epi != EPI_STORE) {
-    set_error("gemm: accumulation is only defined for plain stores");
+
+  const int splits = d.splits < 1 ? 1 : d.splits;
+  a.k_per_split = (int)round_up(ceil_div(d.K, splits), c.bk);
+  const bool via_partial = splits > 1;
+  if (via_partial && (!d.partial || (int64_t)splits * d.M * a.Nt > d.partial_floats)) {
+    set_error("gemm: partial buffer too small for the split count");
     return SGD_EINVAL;
   }
-  const double flops = d.flops > 0 ? d.flops : 2.0 * d.M * d.N * (double)d.K;
-  prof_begin(dma ? kDmaNames[cfg][form] : kNames[cfg][form], flops,
-             4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * a.Nt), s);
-  if (dma) {
-    if (!d.a_t && !d.b_t) launch_dma_cfg<false, false>(cfg, a, splits, s);
-    else if (d.a_t && d.b_t && d.urule >= 0 && !via_partial && d.perm_c == 0)
-      launch_dma_cfg<true, true, true>(cfg, a, splits, s);
-    else if (d.a_t && d.b_t) launch_dma_cfg<true, true>(cfg, a, splits, s);
-    else if (!d.a_t && d.b_t) launch_dma_cfg<false, true>(cfg, a, splits, s);
-    else launch_dma_cfg<true, false>(cfg, a, splits, s);
-  } else {
-    if (!d.a_t && !d.b_t) launch_cfg<false, false>(cfg, a, splits, s);
-    else if (d.a_t && d.b_t) launch_cfg<true, true>(cfg, a, splits, s);
-    else if (!d.a_t && d.b_t) launch_cfg<false, true>(cfg, a, splits, s);
-    else launch_cfg<true, false>(cfg, a, splits, s);
-  }
+  a.C = via_partial ? d.partial : d.C;
+  a.ldc = via_partial ? a.Nt : d.ldc;
+  a.split = via_partial ? 1 : 0;
+  prof_begin(kNames[cfg][form], flops, bytes, s);
+  hipLaunchKernelGGL(staged_fn(cfg, form, via_partial ? EM_GENERIC : epi_mode(d, form)), dim3(a.tiles * splits),
+                     dim3(kThreads), 0, s, a);
   prof_end(s);
   if (int e = check_launch("gemm")) return e;
   if (via_partial) {

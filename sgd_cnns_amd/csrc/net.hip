@@ -304,9 +304,11 @@ int plan(sgd_net* net) {
       s.split_fwd = gemm_pick_splits((int)P, s.Co, s.ldk);
       s.split_dw = gemm_pick_splits(s.Co, s.ldk + 1, (int)P);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)P, s.ldk, s.Co);
-      if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * P * s.Co);
-      if (s.split_dw > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * (s.ldk + 1));
-      if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * P * s.ldk);
+      partial = std::max(partial, gemm_scratch_floats((int)P, s.Co, s.ldk, false, false, false, s.split_fwd));
+      for (bool fused : {false, true})
+        partial = std::max(partial, gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw));
+      if (!s.first_weighted)
+        partial = std::max(partial, gemm_scratch_floats((int)P, s.ldk, s.Co, false, true, false, s.split_dx));
     } else if (s.kind == SGD_MAXPOOL) {
       const int lay = s.out_nchw ? SGD_LAYOUT_NCHW : SGD_LAYOUT_NHWC;
       if (s.out_nchw) {
@@ -324,9 +326,11 @@ int plan(sgd_net* net) {
       s.split_fwd = gemm_pick_splits((int)N, s.Co, s.Ci);
       s.split_dw = gemm_pick_splits(s.Co, s.Ci + 1, (int)N);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)N, s.Ci, s.Co);
-      if (s.split_fwd > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_fwd * N * s.Co);
-      if (s.split_dw > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dw * s.Co * (s.Ci + 1));
-      if (s.split_dx > 1) partial = std::max<int64_t>(partial, (int64_t)s.split_dx * N * s.Ci);
+      partial = std::max(partial, gemm_scratch_floats((int)N, s.Co, s.Ci, false, false, false, s.split_fwd));
+      for (bool fused : {false, true})
+        partial = std::max(partial, gemm_scratch_floats(s.Co, s.Ci + 1, (int)N, true, true, fused, s.split_dw));
+      if (!s.first_weighted)
+        partial = std::max(partial, gemm_scratch_floats((int)N, s.Ci, s.Co, false, true, false, s.split_dx));
     } else if (s.kind == SGD_SOFTMAX_CE) {
       // the logits' gradient lives in the last fc stage's dout
       net->row_loss = make_tensor(b, 4, SGD_LAYOUT_ROWS, N, 1, 1, 1);
@@ -394,6 +398,7 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
       g.bias = Wt + s.b_off;
       g.splits = s.split_fwd;
       g.partial = partial;
+      g.partial_floats = net->partial_floats;
       if ((e = gemm(g, st))) return e;
     } else if (s.kind == SGD_MAXPOOL) {
       if ((e = maxpool_fwd(xin, at<float>(ws, s.out), at<uint8_t>(ws, s.argmax), s.N, s.Ci, s.H, s.W, s.p,
@@ -414,6 +419,7 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
       g.bias = Wt + s.b_off;
       g.splits = s.split_fwd;
       g.partial = partial;
+      g.partial_floats = net->partial_floats;
       if ((e = gemm(g, st))) return e;
     } else if (s.kind == SGD_SOFTMAX_CE) {
       const float scale = net->reduction == SGD_REDUCE_SUM ? 1.f : 1.f / (float)s.N;
@@ -459,6 +465,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.ldm = s.Ci;
         d.splits = s.split_dx;
         d.partial = partial;
+        d.partial_floats = net->partial_floats;
         if ((e = gemm(d, st))) return e;
       }
       GemmDesc g{};  // dedw: dW[out][in] = dout^T * input; dedb via the ones column
@@ -476,6 +483,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
       g.partial = partial;
+      g.partial_floats = net->partial_floats;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
       set_update(g, rule, state, s);
@@ -506,6 +514,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
       g.partial = partial;
+      g.partial_floats = net->partial_floats;
       g.perm_c = s.c;
       g.perm_ci = s.Ci;
       g.perm_k = s.K;
@@ -529,6 +538,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.epi = EPI_STORE;
         d.splits = s.split_dx;
         d.partial = partial;
+        d.partial_floats = net->partial_floats;
         if ((e = gemm(d, st))) return e;
         const Stage& src = stages[s.input];
         const float* mask = (src.relu && src.kind != SGD_MAXPOOL) ? at<float>(ws, src.out) : nullptr;
