@@ -112,16 +112,27 @@ def gpu_step_bench(wl, steps, warmup):
               file=sys.stderr, flush=True)
 
     # per-kernel totals over the timed region
-    kern = {}
-    for (name, layer, phase, ms, flops, nbytes) in recs:
-        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
-        k["launches"] += 1
-        k["ms"] += ms
-        k["flops"] += flops
-        k["bytes"] += nbytes
+    kern = kernel_totals(recs)
+    # the same step with the dedw products on the caller's stream (no
+    # overlap): each kernel then has the GPU to itself, so its event time is
+    # its own duration
+    reps = max(3, min(steps, 10))
+    net.set_overlap(False)
+    step()
+    torch.cuda.synchronize()
+    i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    net.profile(True)
+    i0.record(stream)
+    for _ in range(reps):
+        step()
+    i1.record(stream)
+    torch.cuda.synchronize()
+    net.profile(False)
+    net.set_overlap(True)
+    kern_iso = kernel_totals(net.profile_read())
+    iso_ms = i0.elapsed_time(i1) / reps
     # the unfused pair for reference: gradient into the GradBuf, then the
     # standalone apply kernel (its bandwidth is the update kernel's figure)
-    reps = max(3, min(steps, 10))
     u0, u1, u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     upd_ms = 0.0
     torch.cuda.synchronize()
@@ -139,7 +150,33 @@ def gpu_step_bench(wl, steps, warmup):
                 loss_first=warm_losses[0] if warm_losses else None,
                 update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * upd_ms / reps,
                         "GB/s": upd_b / (upd_ms / reps / 1e3) / 1e9},
-                unfused_ms=unfused_ms)
+                unfused_ms=unfused_ms, kern_iso=kern_iso, iso_ms=iso_ms, iso_reps=reps)
+
+
+def kernel_totals(recs):
+    kern = {}
+    for (name, layer, phase, ms, flops, nbytes) in recs:
+        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        k["launches"] += 1
+        k["ms"] += ms
+        k["flops"] += flops
+        k["bytes"] += nbytes
+    return kern
+
+
+def kernel_table(kern, total_ms):
+    rows = []
+    for name, v in sorted(kern.items(), key=lambda kv: -kv[1]["ms"]):
+        e = {"kernel": name, "launches": v["launches"], "avg_us": 1e3 * v["ms"] / v["launches"],
+             "share_of_step": v["ms"] / total_ms}
+        if v["flops"] and name.startswith("gemm_"):
+            e["TFLOP/s"] = v["flops"] / (v["ms"] / 1e3) / 1e12
+            e["frac_fp32_peak"] = e["TFLOP/s"] / PEAK_FP32_TFLOPS
+        if v["bytes"]:
+            e["GB/s"] = v["bytes"] / (v["ms"] / 1e3) / 1e9
+            e["frac_hbm_peak"] = e["GB/s"] / PEAK_HBM_GBS
+        rows.append(e)
+    return rows
 
 
 def ps_apply_bench(steps=100, pool=16):
@@ -243,17 +280,8 @@ def main():
     g_flops = sum(v["flops"] for v in gemms.values())
     g_ms = sum(v["ms"] for v in gemms.values())
     upd = r["update"]
-    kernels = []
-    for name, v in sorted(kern.items(), key=lambda kv: -kv[1]["ms"]):
-        e = {"kernel": name, "launches": v["launches"], "avg_us": 1e3 * v["ms"] / v["launches"],
-             "share_of_step": v["ms"] / r["total_ms"]}
-        if v["flops"] and name.startswith("gemm_"):
-            e["TFLOP/s"] = v["flops"] / (v["ms"] / 1e3) / 1e12
-            e["frac_fp32_peak"] = e["TFLOP/s"] / PEAK_FP32_TFLOPS
-        if v["bytes"]:
-            e["GB/s"] = v["bytes"] / (v["ms"] / 1e3) / 1e9
-            e["frac_hbm_peak"] = e["GB/s"] / PEAK_HBM_GBS
-        kernels.append(e)
+    kernels = kernel_table(kern, r["total_ms"])
+    iso = r["kern_iso"].get(dom)
     out = {
         "metric": METRIC,
         "value": value,
@@ -273,7 +301,16 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
                      "traffic": measured_traffic(dom, wl.name),
                      "launches": d["launches"], "avg_launch_us": 1e3 * d["ms"] / d["launches"],
-                     "flops_per_launch": d["flops"] / d["launches"]},
+                     "flops_per_launch": d["flops"] / d["launches"],
+                     "note": "timed region: each layer's dedw product runs on a second stream, overlapping the next "
+                             "layer's dedx product, so avg_launch_us is the launch's duration while it shares the "
+                             "GPU; roofline_isolated is the same kernel with the overlap switched off"},
+        "roofline_isolated": None if iso is None else {
+            "kernel": dom, "achieved": iso["flops"] / (iso["ms"] / 1e3) / 1e12, "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s", "frac": iso["flops"] / (iso["ms"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
+            "launches": iso["launches"], "avg_launch_us": 1e3 * iso["ms"] / iso["launches"],
+            "ms_per_step_no_overlap": r["iso_ms"]},
+        "kernels_isolated": kernel_table(r["kern_iso"], r["iso_ms"] * r["iso_reps"])[:8],
         "gemm_mfma_util": {"achieved_TFLOP/s": g_flops / (g_ms / 1e3) / 1e12,
                            "frac_fp32_peak": g_flops / (g_ms / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
                            "share_of_step": g_ms / r["total_ms"]},

@@ -227,9 +227,21 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
                     const sgd_rule* rule, void* stream);
 
 /*
+ * Backward-pass concurrency.  With overlap on (the default) each layer's
+ * dedw product runs on a second stream the library owns, forked from the
+ * caller's stream once the product's inputs are final and joined back into
+ * it before the call's work ends, so a dedw product overlaps the next
+ * layer's dedx product (SPRINT section 3.3's products are independent once
+ * the layer's output gradient exists).  Results are bitwise identical with
+ * overlap off; the caller still sees one stream-ordered operation.  Errors:
+ * SGD_EINVAL (null net).
+ */
+int sgd_set_overlap(sgd_net* net, int enable);
+
+/*
  * Per-launch kernel timing, for measurement.  While enabled, every kernel
  * sgd_compute_gradient launches is bracketed by a HIP event pair on the
- * caller's stream, and its algorithmic work is recorded: flops of the
+ * stream it is launched on, and its algorithmic work is recorded: flops of the
  * arithmetic the method needs (2mnk for a product of the SPRINT section 3.3
  * table, with k the unpadded reduction length) and bytes it must move
  * through HBM (each operand read once, each result written once).

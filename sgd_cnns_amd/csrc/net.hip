@@ -62,6 +62,43 @@ struct Profiler {
 
 thread_local Profiler* g_prof = nullptr;
 
+// The stream the weight-gradient products run on, so each overlaps the next
+// layer's input-gradient product on the caller's stream (and fills the
+// partly occupied last round of each): created on first use per device,
+// default priority, with one fork event per weighted layer and a join event.
+struct SideStream {
+  int dev = -1;
+  hipStream_t s = nullptr;
+  std::vector<hipEvent_t> ev;
+  void release() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    if (s) (void)hipStreamDestroy(s);
+    s = nullptr;
+    dev = -1;
+  }
+  // Ready on the current device with n fork events plus the join event.
+  int ready(int n) {
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess) return SGD_EDEVICE;
+    if (s && d != dev) release();
+    if (!s) {
+      if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+        s = nullptr;
+        return SGD_EDEVICE;
+      }
+      dev = d;
+    }
+    while ((int)ev.size() < n + 1) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return SGD_EDEVICE;
+      ev.push_back(e);
+    }
+    return 0;
+  }
+  ~SideStream() { release(); }
+};
+
 void prof_set_layer(int layer, int phase) {
   if (g_prof) {
     g_prof->layer = layer;
@@ -123,8 +160,16 @@ struct sgd_net {
   std::vector<int64_t> w_offs, b_offs;
   int64_t ws_bytes = 0;
   sgd::Tensor row_loss;
+  // Partial-tile scratch of the GEMMs: one region for the products on the
+  // caller's stream, one for the weight-gradient products on the side
+  // stream (they run concurrently).
   int64_t partial_off = 0, partial_floats = 0;
+  int64_t partial_dw_off = 0, partial_dw_floats = 0;
+  // dCol of the conv dedx products (dedw reads Col concurrently).
+  int64_t dcol_off = 0;
   sgd::Profiler prof;
+  sgd::SideStream side;
+  bool overlap = true;  // dedw products on the side stream
 };
 
 namespace sgd {
@@ -292,7 +337,7 @@ int plan(sgd_net* net) {
 
   // Workspace layout and product split factors.
   Bump b;
-  int64_t partial = 0;
+  int64_t partial = 0, partial_dw = 0, dcol = 0;
   for (Stage& s : st) {
     const int64_t N = s.N;
     if (s.kind == SGD_CONV) {
@@ -306,9 +351,11 @@ int plan(sgd_net* net) {
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)P, s.ldk, s.Co);
       partial = std::max(partial, gemm_scratch_floats((int)P, s.Co, s.ldk, false, false, false, s.split_fwd));
       for (bool fused : {false, true})
-        partial = std::max(partial, gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw));
-      if (!s.first_weighted)
+        partial_dw = std::max(partial_dw, gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw));
+      if (!s.first_weighted) {
         partial = std::max(partial, gemm_scratch_floats((int)P, s.ldk, s.Co, false, true, false, s.split_dx));
+        dcol = std::max(dcol, P * s.ldk);
+      }
     } else if (s.kind == SGD_MAXPOOL) {
       const int lay = s.out_nchw ? SGD_LAYOUT_NCHW : SGD_LAYOUT_NHWC;
       if (s.out_nchw) {
@@ -328,7 +375,7 @@ int plan(sgd_net* net) {
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)N, s.Ci, s.Co);
       partial = std::max(partial, gemm_scratch_floats((int)N, s.Co, s.Ci, false, false, false, s.split_fwd));
       for (bool fused : {false, true})
-        partial = std::max(partial, gemm_scratch_floats(s.Co, s.Ci + 1, (int)N, true, true, fused, s.split_dw));
+        partial_dw = std::max(partial_dw, gemm_scratch_floats(s.Co, s.Ci + 1, (int)N, true, true, fused, s.split_dw));
       if (!s.first_weighted)
         partial = std::max(partial, gemm_scratch_floats((int)N, s.Ci, s.Co, false, true, false, s.split_dx));
     } else if (s.kind == SGD_SOFTMAX_CE) {
@@ -340,6 +387,9 @@ int plan(sgd_net* net) {
   }
   net->partial_floats = partial;
   net->partial_off = b.take(4 * std::max<int64_t>(partial, 1));
+  net->partial_dw_floats = partial_dw;
+  net->partial_dw_off = b.take(4 * std::max<int64_t>(partial_dw, 1));
+  net->dcol_off = b.take(4 * std::max<int64_t>(dcol, 1));
   net->ws_bytes = b.top;
   for (const Stage& s : st)
     if (s.kind == SGD_CONV || s.kind == SGD_FC) {
@@ -434,15 +484,38 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
 // them (the GradBuf update of SPRINT Algorithm 1 for a non-empty buffer).
 // rule (fused training step): `grad` is the weight vector itself and each
 // layer's update is applied as soon as its gradient is final; an fc layer's
-// dedx product, which reads that layer's weights, runs before its dedw.
+// dedx product, which reads that layer's weights, runs before its dedw (a
+// conv layer's dedx reads the repacked copy W').
+//
+// Every dedw product runs on the side stream, forked from the caller's
+// stream once its inputs (the layer's output gradient, and the input
+// activation or Col from the forward pass) are final and, for an fc layer,
+// after the dedx product that reads W.  Nothing on the caller's stream
+// writes what a dedw product reads or reads what it writes, and the caller's
+// stream joins the side stream at the end, so the step stays one stream-
+// ordered operation for the caller.
 int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, bool accum, const sgd_rule* rule,
                  float* state, void* ws, hipStream_t st) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
+  float* partial_dw = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_dw_off);
+  float* dcol = reinterpret_cast<float*>(static_cast<char*>(ws) + net->dcol_off);
   auto& stages = net->stages;
-  for (int si = (int)stages.size() - 1; si >= 0; --si) {
+  int weighted = 0;
+  for (const Stage& s : stages) weighted += (s.kind == SGD_FC || s.kind == SGD_CONV);
+  if (net->overlap && net->side.ready(weighted)) return fail(SGD_EDEVICE, "backward: could not create the side stream");
+  const hipStream_t side = net->overlap ? net->side.s : st;
+  int fork_i = 0;
+  auto fork = [&]() -> int {
+    if (!net->overlap) return 0;
+    hipEvent_t ev = net->side.ev[fork_i++];
+    if (hipEventRecord(ev, st) != hipSuccess || hipStreamWaitEvent(side, ev, 0) != hipSuccess)
+      return fail(SGD_EDEVICE, "backward: fork to the side stream failed");
+    return 0;
+  };
+  int e = 0;
+  for (int si = (int)stages.size() - 1; si >= 0 && !e; --si) {
     Stage& s = stages[si];
     const float* xin = input_of(net, s, ws, X);
-    int e = 0;
     prof_set_layer(s.spec, 1);
     if (s.kind == SGD_FC) {
       const float* dout = at<float>(ws, s.dout);
@@ -466,7 +539,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.splits = s.split_dx;
         d.partial = partial;
         d.partial_floats = net->partial_floats;
-        if ((e = gemm(d, st))) return e;
+        if ((e = gemm(d, st))) continue;
       }
       GemmDesc g{};  // dedw: dW[out][in] = dout^T * input; dedb via the ones column
       g.A = dout;
@@ -482,18 +555,18 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.K = s.N;
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
-      g.partial = partial;
-      g.partial_floats = net->partial_floats;
+      g.partial = partial_dw;
+      g.partial_floats = net->partial_dw_floats;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
       set_update(g, rule, state, s);
-      if ((e = gemm(g, st))) return e;
+      if ((e = fork()) || (e = gemm(g, side))) continue;
     } else if (s.kind == SGD_MAXPOOL) {
       const Stage& src = stages[s.input];
       const float* pooled = src.relu ? at<float>(ws, s.out) : nullptr;
       if ((e = maxpool_bwd(at<float>(ws, s.dout), at<uint8_t>(ws, s.argmax), pooled, at<float>(ws, src.dout), s.N,
                            s.Ci, s.H, s.W, s.p, s.out_nchw, st)))
-        return e;
+        continue;
     } else if (s.kind == SGD_CONV) {
       const float* dout = at<float>(ws, s.dout);
       float* col = at<float>(ws, s.col);
@@ -513,23 +586,23 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.flops = 2.0 * s.Co * (double)s.K * (double)P;
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
-      g.partial = partial;
-      g.partial_floats = net->partial_floats;
+      g.partial = partial_dw;
+      g.partial_floats = net->partial_dw_floats;
       g.perm_c = s.c;
       g.perm_ci = s.Ci;
       g.perm_k = s.K;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
       set_update(g, rule, state, s);
-      if ((e = gemm(g, st))) return e;
+      if ((e = fork()) || (e = gemm(g, side))) continue;
       if (!s.first_weighted) {
-        GemmDesc d{};  // dedx_conv: dcol[P][kk] = dout * W' (written over the im2col matrix)
+        GemmDesc d{};  // dedx_conv: dcol[P][kk] = dout * W' (its own buffer: dedw reads Col meanwhile)
         d.A = dout;
         d.lda = s.Co;
         d.B = at<float>(ws, s.wrep);
         d.ldb = s.ldk;
         d.b_t = true;
-        d.C = col;
+        d.C = dcol;
         d.ldc = s.ldk;
         d.M = (int)P;
         d.N = s.ldk;
@@ -539,15 +612,21 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.splits = s.split_dx;
         d.partial = partial;
         d.partial_floats = net->partial_floats;
-        if ((e = gemm(d, st))) return e;
+        if ((e = gemm(d, st))) continue;
         const Stage& src = stages[s.input];
         const float* mask = (src.relu && src.kind != SGD_MAXPOOL) ? at<float>(ws, src.out) : nullptr;
-        if ((e = col2im(col, mask, at<float>(ws, src.dout), s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st)))
-          return e;
+        if ((e = col2im(dcol, mask, at<float>(ws, src.dout), s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st)))
+          continue;
       }
     }
   }
-  return 0;
+  // Join even after an error, so nothing enqueued on the side stream is left
+  // unordered with the caller's stream.
+  if (!net->overlap) return e;
+  hipEvent_t join = net->side.ev[weighted];
+  if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess)
+    return e ? e : fail(SGD_EDEVICE, "backward: join of the side stream failed");
+  return e;
 }
 
 }  // namespace
@@ -648,6 +727,12 @@ int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, cons
                      "sgd_compute_gradient_into");
   if (!e) gb->empty = 0;
   return e;
+}
+
+int sgd_set_overlap(sgd_net* net, int enable) {
+  if (!net) return fail(SGD_EINVAL, "sgd_set_overlap: null net");
+  net->overlap = enable != 0;
+  return SGD_OK;
 }
 
 int sgd_profile(sgd_net* net, int enable) {

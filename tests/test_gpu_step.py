@@ -214,3 +214,41 @@ def test_train_step_equals_gradient_then_apply(rule, case):
     if rule != "plain":
         assert torch.equal(sa, sb)
     assert not torch.equal(Wb, torch.from_numpy(W).to(dev))
+
+
+@pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged"])
+def test_overlap_on_and_off_bitwise_equal(case):
+    # the dedw products run on a second stream by default; with overlap off
+    # they run in order on the caller's stream: every output must be bitwise
+    # the same (gradient, loss, and a fused momentum step's W and V)
+    if case == "lenet5":
+        wl = workloads.WORKLOADS["lenet5"]
+    elif case == "vgg_cifar_b2":
+        wl = workloads.WORKLOADS["vgg_cifar"].with_batch(2)
+    else:
+        wl = workloads.Workload("mlp_ragged", 31, 70, (3072, 1, 1),
+                                [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)])
+    print(f"[overlap] {case}", flush=True)
+    X, y, W = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    n = net.param_count()
+    dev = torch.device("cuda")
+    Xd, yd, Wd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev), torch.from_numpy(W).to(dev)
+    ws = net.workspace()
+    R = S.Rule("momentum", 0.01, 0.9, 1e-8)
+    out = {}
+    for ov in (True, False):
+        net.set_overlap(ov)
+        g = torch.empty(n, device=dev)
+        loss = torch.empty(1, device=dev)
+        net.compute_gradient(Wd, Xd, yd, g, loss, ws)
+        Wt = Wd.clone()
+        V = torch.zeros(n, device=dev)
+        loss2 = torch.empty(1, device=dev)
+        net.train_step(Wt, Xd, yd, V, R, loss2, ws)
+        net.train_step(Wt, Xd, yd, V, R, loss2, ws)
+        torch.cuda.synchronize()
+        out[ov] = (g.cpu(), loss.item(), Wt.cpu(), V.cpu(), loss2.item())
+    a, b = out[True], out[False]
+    assert torch.equal(a[0], b[0]) and a[1] == b[1]
+    assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3]) and a[4] == b[4]
