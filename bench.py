@@ -179,6 +179,34 @@ def kernel_table(kern, total_ms):
     return rows
 
 
+def variant_apply_bench(n, reps=20):
+    """Standalone update kernels for the rule variants (weight decay, Nesterov) on n parameters."""
+    import torch
+
+    import sgd_cnns_amd as S
+
+    dev = torch.device("cuda")
+    W = torch.randn(n, device=dev)
+    V = torch.zeros(n, device=dev)
+    G = torch.randn(n, device=dev) * 1e-3
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, rule, nbytes in (("apply_nesterov_decay", S.Rule("nesterov", 0.01, 0.9, 0.0, 5e-4), 20.0),
+                               ("apply_plain_decay", S.Rule("plain", 0.01, 0.0, 0.0, 5e-4), 12.0)):
+        st = V if name.startswith("apply_nesterov") else None
+        S.apply_fused(W, st, [G], rule, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            S.apply_fused(W, st, [G], rule, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"params": n, "bytes_per_param": nbytes, "avg_us": 1e3 * ms,
+                     "GB/s": nbytes * n / ms / 1e6, "frac_hbm_peak": nbytes * n / ms / 1e6 / PEAK_HBM_GBS}
+    return out
+
+
 def ps_apply_bench(steps=100, pool=16):
     """Parameter-server apply: 138,357,544 params, K = 8 buffers left-folded + Adagrad, fresh buffers per step."""
     import torch
@@ -323,6 +351,7 @@ def main():
         "loss_first_step": r["loss_first"],
         "loss_last_step": r["loss"] if np.isfinite(r["loss"]) else str(r["loss"]),
     }
+    out["update_variants"] = variant_apply_bench(r["n_params"])
     if not args.no_ps_apply:
         print("[bench] parameter-server apply", file=sys.stderr, flush=True)
         out["ps_apply"] = ps_apply_bench()

@@ -58,6 +58,7 @@ extern "C" {
 #define SGD_PLAIN 0    /* W = W - eta*G                          (SPRINT eq. (1))           */
 #define SGD_MOMENTUM 1 /* V = mu*V - eta*G; W = W + V            (SPRINT Algorithm 2, nu=mu) */
 #define SGD_ADAGRAD 2  /* A = A + G*G; W = W - (eta/(sqrt(A)+eps))*G  (DistBelief review)   */
+#define SGD_NESTEROV 3 /* V = mu*V - eta*G; W = W + mu*V - eta*G  (PIPE report, appendix A) */
 
 /* ---- tensor-info selectors (sgd_tensor_info) ---- */
 #define SGD_T_OUT 0    /* forward output of the layer                                  */
@@ -178,6 +179,20 @@ int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, cons
                               float* loss, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sgd_compute_gradient_into with the worker-side scaling of SPRINT Algorithm
+ * 1 (its line 10, Grad <- -eta * grad): every gradient value is multiplied
+ * by `scale` (one rounding) before it is stored in or added to the buffer.
+ * scale = -eta makes the buffer hold the step itself; applying it with
+ * sgd_apply_update and eta = -1 then gives bitwise the unscaled path's
+ * result (the products -1 * (-eta*g) and eta*g round identically).  scale = 1
+ * is sgd_compute_gradient_into.  Errors as sgd_compute_gradient_into, and
+ * SGD_EINVAL for a non-finite scale.
+ */
+int sgd_compute_gradient_into_scaled(sgd_net* net, const float* W, const float* X, const int32_t* y,
+                                     sgd_gradbuf* gb, float scale, float* loss, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/*
  * GradBuf <- grad if the buffer is empty, else GradBuf + grad (SPRINT
  * Algorithm 1, the GradBuf update).  Clears `empty`.  grad has gb->n floats.
  * Errors: SGD_EINVAL, SGD_EDEVICE.
@@ -194,24 +209,29 @@ int sgd_accumulate_grad(sgd_gradbuf* gb, const float* grad, void* stream);
 int sgd_accumulate_grads(sgd_gradbuf* gb, const float* const* grads, int k, void* stream);
 
 typedef struct sgd_rule {
-  int rule;  /* SGD_PLAIN, SGD_MOMENTUM or SGD_ADAGRAD */
-  float eta; /* learning rate                          */
-  float mu;  /* momentum coefficient (SGD_MOMENTUM)    */
-  float eps; /* Adagrad denominator offset             */
+  int rule;    /* SGD_PLAIN, SGD_MOMENTUM, SGD_ADAGRAD or SGD_NESTEROV  */
+  float eta;   /* learning rate                                         */
+  float mu;    /* momentum coefficient (SGD_MOMENTUM, SGD_NESTEROV)     */
+  float eps;   /* Adagrad denominator offset                            */
+  float decay; /* weight decay (0: none); the PIPE report's appendix A
+                  trains with 5e-4                                      */
 } sgd_rule;
 
 /*
  * Apply the buffered gradient G to W in place, elementwise, one rounding per
  * statement in this order (no fused multiply-add; correctly rounded sqrt and
  * division):
+ *   decay != 0 first: wd = decay*W; G = G + wd      (weight decay, any rule)
  *   plain:    t = eta*G;  W = W - t
  *   momentum: t1 = mu*V; t2 = eta*G; V = t1 - t2; W = W + V
  *   adagrad:  A = A + G*G; d = sqrt(A) + eps; r = eta/d; t = r*G; W = W - t
- * `state` is V (momentum) or A (Adagrad), n = gb->n floats; NULL for plain.
- * An empty GradBuf is a zero gradient (SPRINT Algorithm 2 sends 0 when the
- * first buffer is empty): plain and Adagrad then leave W unchanged, momentum
- * still decays V.  Marks the buffer empty afterwards.  Errors: SGD_EINVAL,
- * SGD_EDEVICE.
+ *   nesterov: t1 = mu*V; t2 = eta*G; V = t1 - t2; t3 = mu*V; u = t3 - t2;
+ *             W = W + u
+ * `state` is V (momentum, Nesterov) or A (Adagrad), n = gb->n floats; NULL
+ * for plain.  An empty GradBuf is a zero gradient (SPRINT Algorithm 2 sends
+ * 0 when the first buffer is empty): without decay, plain and Adagrad then
+ * leave W unchanged and momentum still decays V; weight decay still applies.
+ * Marks the buffer empty afterwards.  Errors: SGD_EINVAL, SGD_EDEVICE.
  */
 int sgd_apply_update(float* W, sgd_gradbuf* gb, float* state, const sgd_rule* rule, void* stream);
 

@@ -51,9 +51,10 @@ def lib(dtype=np.float32):
             "or_fc_bwd": (None, [i, i, i, P, P, P, P, P, P]),
             "or_softmax_ce": (d, [i, i, P, P, i, P]),
             "or_accumulate": (None, [P, P, P, i64]),
-            "or_apply_plain": (None, [P, P, i64, rt]),
-            "or_apply_momentum": (None, [P, P, P, i64, rt, rt]),
-            "or_apply_adagrad": (None, [P, P, P, i64, rt, rt]),
+            "or_apply_plain": (None, [P, P, i64, rt, rt]),
+            "or_apply_momentum": (None, [P, P, P, i64, rt, rt, rt]),
+            "or_apply_nesterov": (None, [P, P, P, i64, rt, rt, rt]),
+            "or_apply_adagrad": (None, [P, P, P, i64, rt, rt, rt]),
         }
         for fn, (res, args) in sig.items():
             f = getattr(L, fn)
@@ -201,26 +202,32 @@ class GradBuf:
         self.empty = bool(e.value)
 
 
-def apply_plain(W, g, eta):
-    lib(W.dtype).or_apply_plain(_p(W), _p(g), W.size, eta)
+def apply_plain(W, g, eta, decay=0.0):
+    lib(W.dtype).or_apply_plain(_p(W), _p(g), W.size, eta, decay)
 
 
-def apply_momentum(W, V, g, mu, eta):
-    lib(W.dtype).or_apply_momentum(_p(W), _p(V), _p(g), W.size, mu, eta)
+def apply_momentum(W, V, g, mu, eta, decay=0.0):
+    lib(W.dtype).or_apply_momentum(_p(W), _p(V), _p(g), W.size, mu, eta, decay)
 
 
-def apply_adagrad(W, A, g, eta, eps):
-    lib(W.dtype).or_apply_adagrad(_p(W), _p(A), _p(g), W.size, eta, eps)
+def apply_nesterov(W, V, g, mu, eta, decay=0.0):
+    lib(W.dtype).or_apply_nesterov(_p(W), _p(V), _p(g), W.size, mu, eta, decay)
 
 
-def apply_rule(rule, W, state, g, eta, mu=0.0, eps=0.0):
+def apply_adagrad(W, A, g, eta, eps, decay=0.0):
+    lib(W.dtype).or_apply_adagrad(_p(W), _p(A), _p(g), W.size, eta, eps, decay)
+
+
+def apply_rule(rule, W, state, g, eta, mu=0.0, eps=0.0, decay=0.0):
     """Apply one update in place; g None means an empty GradBuf (zero gradient)."""
     if rule == "plain":
-        apply_plain(W, g, eta)
+        apply_plain(W, g, eta, decay)
     elif rule == "momentum":
-        apply_momentum(W, state, g, mu, eta)
+        apply_momentum(W, state, g, mu, eta, decay)
+    elif rule == "nesterov":
+        apply_nesterov(W, state, g, mu, eta, decay)
     elif rule == "adagrad":
-        apply_adagrad(W, state, g, eta, eps)
+        apply_adagrad(W, state, g, eta, eps, decay)
     else:
         raise ValueError(rule)
 

@@ -350,11 +350,22 @@ void or_accumulate(real* buf, int* empty, const real* g, int64_t n) {
 /* Algorithm 2: with no gradient in the first buffer the send buffer is 0). */
 /* ------------------------------------------------------------------------ */
 
+/* Weight decay ([PIPE] appendix A trains with weight decay; the pages give
+ * no formula).  Read as the gradient of (decay/2)*|W|^2 added to the data
+ * gradient before any rule, for every parameter:  wd = decay*W;  g = g + wd.
+ * With decay == 0 the gradient is used as it is. */
+static real decayed(real g, real w, real decay) {
+  if (decay == (real)0) return g;
+  const real wd = decay * w;
+  return g + wd;
+}
+
 /* Plain SGD, [SPRINT] eq. (1): W(t+1) = W(t) - eta * sum of gradients. */
-void or_apply_plain(real* W, const real* g, int64_t n, real eta) {
-  if (!g) return;
+void or_apply_plain(real* W, const real* g, int64_t n, real eta, real decay) {
+  if (!g && decay == (real)0) return;
   for (int64_t i = 0; i < n; ++i) {
-    const real t = eta * g[i];
+    const real gi = decayed(g ? g[i] : (real)0, W[i], decay);
+    const real t = eta * gi;
     W[i] = W[i] - t;
   }
 }
@@ -362,9 +373,9 @@ void or_apply_plain(real* W, const real* g, int64_t n, real eta) {
 /* Momentum ([SPRINT] sec. 2 design point (b) and Algorithm 2, where the
  * new weights add nu times the previous weight change).  With the change
  * kept in V:  V = mu*V - eta*g;  W = W + V. */
-void or_apply_momentum(real* W, real* V, const real* g, int64_t n, real mu, real eta) {
+void or_apply_momentum(real* W, real* V, const real* g, int64_t n, real mu, real eta, real decay) {
   for (int64_t i = 0; i < n; ++i) {
-    const real gi = g ? g[i] : (real)0;
+    const real gi = decayed(g ? g[i] : (real)0, W[i], decay);
     const real t1 = mu * V[i];
     const real t2 = eta * gi;
     V[i] = t1 - t2;
@@ -372,14 +383,32 @@ void or_apply_momentum(real* W, real* V, const real* g, int64_t n, real mu, real
   }
 }
 
+/* Nesterov momentum ([PIPE] appendix A trains AlexNet and VGG-16 with it;
+ * the pages give no formula).  Read as the look-ahead form of the momentum
+ * above: the change V is updated as for momentum, and the weights move by
+ * mu times the new change plus the gradient step:
+ *   V = mu*V - eta*g;  W = W + (mu*V - eta*g). */
+void or_apply_nesterov(real* W, real* V, const real* g, int64_t n, real mu, real eta, real decay) {
+  for (int64_t i = 0; i < n; ++i) {
+    const real gi = decayed(g ? g[i] : (real)0, W[i], decay);
+    const real t1 = mu * V[i];
+    const real t2 = eta * gi;
+    V[i] = t1 - t2;
+    const real t3 = mu * V[i];
+    const real u = t3 - t2;
+    W[i] = W[i] + u;
+  }
+}
+
 /* Adagrad, a separate adaptive rate per parameter on the parameter server
  * ([DISTBELIEF]: the server applies w' = w - eta_i * dw with Adagrad's rate).
  * The accumulator includes the current gradient before it is used:
  *   A = A + g*g;  r = eta / (sqrt(A) + eps);  W = W - r*g. */
-void or_apply_adagrad(real* W, real* A, const real* g, int64_t n, real eta, real eps) {
-  if (!g) return;
+void or_apply_adagrad(real* W, real* A, const real* g, int64_t n, real eta, real eps, real decay) {
+  if (!g && decay == (real)0) return;
   for (int64_t i = 0; i < n; ++i) {
-    const real gg = g[i] * g[i];
+    const real gi = decayed(g ? g[i] : (real)0, W[i], decay);
+    const real gg = gi * gi;
     A[i] = A[i] + gg;
 #if defined(OR_REAL_IS_DOUBLE)
     const real d = sqrt(A[i]) + eps;
@@ -387,7 +416,7 @@ void or_apply_adagrad(real* W, real* A, const real* g, int64_t n, real eta, real
     const real d = sqrtf(A[i]) + eps;
 #endif
     const real r = eta / d;
-    const real t = r * g[i];
+    const real t = r * gi;
     W[i] = W[i] - t;
   }
 }

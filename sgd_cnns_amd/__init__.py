@@ -26,12 +26,12 @@ LIB_PATH = os.path.join(_HERE, "libsgdstep.so")
 OK, EINVAL, ESHAPE, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 CONV, RELU, MAXPOOL, FC, SOFTMAX_CE = 1, 2, 3, 4, 5
 REDUCE_MEAN, REDUCE_SUM = 0, 1
-PLAIN, MOMENTUM, ADAGRAD = 0, 1, 2
+PLAIN, MOMENTUM, ADAGRAD, NESTEROV = 0, 1, 2, 3
 T_OUT, T_DOUT, T_COL, T_WREP, T_ARGMAX = 0, 1, 2, 3, 4
 LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
-           "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_accumulate_grad",
+           "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
            "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_profile", "sgd_profile_read",
            "sgd_last_error"]
@@ -50,7 +50,7 @@ class SgdGradBuf(C.Structure):
 
 
 class SgdRule(C.Structure):
-    _fields_ = [("rule", C.c_int), ("eta", C.c_float), ("mu", C.c_float), ("eps", C.c_float)]
+    _fields_ = [("rule", C.c_int), ("eta", C.c_float), ("mu", C.c_float), ("eps", C.c_float), ("decay", C.c_float)]
 
 
 class SgdKernelTime(C.Structure):
@@ -84,6 +84,7 @@ def lib():
             "sgd_tensor_info": (i, [P, i, i, C.POINTER(i64), C.POINTER(i64), C.POINTER(i)]),
             "sgd_compute_gradient": (i, [P, P, P, P, P, P, P, sz, P]),
             "sgd_compute_gradient_into": (i, [P, P, P, P, C.POINTER(SgdGradBuf), P, P, sz, P]),
+            "sgd_compute_gradient_into_scaled": (i, [P, P, P, P, C.POINTER(SgdGradBuf), C.c_float, P, P, sz, P]),
             "sgd_accumulate_grad": (i, [C.POINTER(SgdGradBuf), P, P]),
             "sgd_accumulate_grads": (i, [C.POINTER(SgdGradBuf), C.POINTER(P), i, P]),
             "sgd_apply_update": (i, [P, C.POINTER(SgdGradBuf), P, C.POINTER(SgdRule), P]),
@@ -239,6 +240,13 @@ class Net:
                                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+    def compute_gradient_into_scaled(self, W, X, y, gb, scale, loss, ws, stream=None):
+        """As compute_gradient_into with every gradient value multiplied by `scale` first."""
+        _require_cuda(W, X, y, gb.data, loss, ws)
+        _check(lib().sgd_compute_gradient_into_scaled(self._h, _ptr(W), _ptr(X), _ptr(y), C.byref(gb._c),
+                                                      C.c_float(scale), _ptr(loss), _ptr(ws),
+                                                      ws.numel() * ws.element_size(), _stream(stream)))
+
     def train_step(self, W, X, y, state, rule, loss, ws, stream=None):
         """Gradient + update in one pass: W (and state) updated in place."""
         _require_cuda(W, X, y, state, loss, ws)
@@ -274,11 +282,11 @@ def accumulate_grads(gb, grads, stream=None):
     _check(lib().sgd_accumulate_grads(C.byref(gb._c), arr, len(grads), _stream(stream)))
 
 
-_RULES = {"plain": PLAIN, "momentum": MOMENTUM, "adagrad": ADAGRAD}
+_RULES = {"plain": PLAIN, "momentum": MOMENTUM, "adagrad": ADAGRAD, "nesterov": NESTEROV}
 
 
-def Rule(rule, eta, mu=0.0, eps=0.0):
-    return SgdRule(_RULES[rule] if isinstance(rule, str) else rule, eta, mu, eps)
+def Rule(rule, eta, mu=0.0, eps=0.0, decay=0.0):
+    return SgdRule(_RULES[rule] if isinstance(rule, str) else rule, eta, mu, eps, decay)
 
 
 def apply_update(W, gb, state, rule, stream=None):

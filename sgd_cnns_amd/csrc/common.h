@@ -84,7 +84,11 @@ struct GemmDesc {
   int urule = -1;
   float* ustate = nullptr;
   float* ustate_b = nullptr;
-  float eta = 0.f, mu = 0.f, eps = 0.f;
+  float eta = 0.f, mu = 0.f, eps = 0.f, decay = 0.f;
+  // Every final value is multiplied by gscale (one rounding) before it is
+  // stored or accumulated: the worker-side gradient scaling of SPRINT
+  // Algorithm 1.  Must be 1 with an update rule.
+  float gscale = 1.f;
   // Kernel/tile override (-1: chosen from the shape and the operands).
   int cfg = -1;
   // gemm_dma schedule override: sk_grid > 0 forces that many blocks with

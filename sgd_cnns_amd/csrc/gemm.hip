@@ -82,7 +82,8 @@ struct KArgs {
   int urule;         // >= 0: apply this update rule instead of storing the gradient
   float* ustate;     // rule state at the same offsets as C
   float* ustate_b;   // rule state of the ones column (bias)
-  float eta, mu, eps;
+  float eta, mu, eps, decay;
+  float gscale;      // every final gradient value is multiplied by this (1: none)
   int a_vec, b_vec;  // float4 global loads allowed (aligned base, ld % 4 == 0)
   int tiles_n;       // tiles along Nt
   int tiles;         // tiles per split
@@ -199,19 +200,20 @@ __device__ __forceinline__ float epilogue(float v, int epi, int row, int col, co
 // final gradient and the update rule is applied to the parameter (and its
 // state) in place of storing it.
 __device__ __forceinline__ void finish(float v, int row, int col, const KArgs& p) {
+  v = v * p.gscale;
   if (col == p.N) {
-    if (p.urule >= 0) apply_one(p.urule, p.ones_out + row, p.ustate_b + row, v, p.eta, p.mu, p.eps);
+    if (p.urule >= 0) apply_one(p.urule, p.ones_out + row, p.ustate_b + row, v, p.eta, p.mu, p.eps, p.decay);
     else p.ones_out[row] = p.accum ? p.ones_out[row] + v : v;
   } else if (p.perm_c > 0) {
     if (col < p.perm_k) {
       const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
       const int64_t off = (int64_t)row * p.ldc + (int64_t)ci * p.perm_c * p.perm_c + tap;
-      if (p.urule >= 0) apply_one(p.urule, p.C + off, p.ustate + off, v, p.eta, p.mu, p.eps);
+      if (p.urule >= 0) apply_one(p.urule, p.C + off, p.ustate + off, v, p.eta, p.mu, p.eps, p.decay);
       else p.C[off] = p.accum ? p.C[off] + v : v;
     }
   } else if (p.urule >= 0) {
     const int64_t off = (int64_t)row * p.ldc + col;
-    apply_one(p.urule, p.C + off, p.ustate + off, v, p.eta, p.mu, p.eps);
+    apply_one(p.urule, p.C + off, p.ustate + off, v, p.eta, p.mu, p.eps, p.decay);
   } else {
     float* dst = p.C + (int64_t)row * p.ldc + col;
     *dst = epilogue(v, p.epi, row, col, p, p.epi == EPI_ACCUM ? *dst : 0.f);
@@ -248,16 +250,17 @@ __device__ __forceinline__ void finish4(const float (&v)[4], int row, int nrow, 
     if (e >= nrow) break;
     if (old_c) aux[e] = dst[base + e * ld];
     else if (plain && p.epi == EPI_MASK) aux[e] = p.mask[(int64_t)(row + e) * p.ldm + col];
-    if (p.urule == SGD_MOMENTUM || p.urule == SGD_ADAGRAD) sv[e] = stt[base + e * ld];
+    if (p.urule == SGD_MOMENTUM || p.urule == SGD_ADAGRAD || p.urule == SGD_NESTEROV) sv[e] = stt[base + e * ld];
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (e >= nrow) break;
-    float x = v[e];
+    float x = v[e] * p.gscale;
     if (p.urule >= 0) {
-      if (p.urule == SGD_PLAIN) rule1<SGD_PLAIN>(aux[e], sv[e], x, p.eta, p.mu, p.eps);
-      else if (p.urule == SGD_MOMENTUM) rule1<SGD_MOMENTUM>(aux[e], sv[e], x, p.eta, p.mu, p.eps);
-      else rule1<SGD_ADAGRAD>(aux[e], sv[e], x, p.eta, p.mu, p.eps);
+      if (p.urule == SGD_PLAIN) rule1<SGD_PLAIN>(aux[e], sv[e], x, p.eta, p.mu, p.eps, p.decay);
+      else if (p.urule == SGD_MOMENTUM) rule1<SGD_MOMENTUM>(aux[e], sv[e], x, p.eta, p.mu, p.eps, p.decay);
+      else if (p.urule == SGD_NESTEROV) rule1<SGD_NESTEROV>(aux[e], sv[e], x, p.eta, p.mu, p.eps, p.decay);
+      else rule1<SGD_ADAGRAD>(aux[e], sv[e], x, p.eta, p.mu, p.eps, p.decay);
       dst[base + e * ld] = aux[e];
       if (p.urule != SGD_PLAIN) stt[base + e * ld] = sv[e];
       continue;
@@ -363,18 +366,22 @@ __device__ __forceinline__ void store_wave(const f32x16 (&acc)[TM][TN], const KA
       for (int e = 0; e < 8; ++e) {
         const uint32_t o = vo + (a * 32 + blk_row(8 * h + e)) * ld * 4u;
         w[e] = (RULE >= 0 || p.accum) ? bload(d, o) : 0.f;
-        st[e] = (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD) ? bload(st_r, o) : 0.f;
+        st[e] = (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD || RULE == SGD_NESTEROV) ? bload(st_r, o) : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (RULE >= 0) rule1<(RULE >= 0 ? RULE : 0)>(w[e], st[e], v[8 * h + e], p.eta, p.mu, p.eps);
-        else w[e] = p.accum ? w[e] + v[8 * h + e] : v[8 * h + e];
+        if (RULE >= 0) {
+          rule1<(RULE >= 0 ? RULE : 0)>(w[e], st[e], v[8 * h + e], p.eta, p.mu, p.eps, p.decay);
+        } else {
+          const float x = v[8 * h + e] * p.gscale;
+          w[e] = p.accum ? w[e] + x : x;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t o = vo + (a * 32 + blk_row(8 * h + e)) * ld * 4u;
         bstore(w[e], d, o);
-        if (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD) bstore(st[e], st_r, o);
+        if (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD || RULE == SGD_NESTEROV) bstore(st[e], st_r, o);
       }
       sched_fence();
     };
@@ -384,6 +391,7 @@ __device__ __forceinline__ void store_wave(const f32x16 (&acc)[TM][TN], const KA
         if (EM == EM_DW) rows8(std::integral_constant<int, -1>{}, v, h, a, d, st_r, vo, ld);
         else if (p.urule == SGD_PLAIN) rows8(std::integral_constant<int, SGD_PLAIN>{}, v, h, a, d, st_r, vo, ld);
         else if (p.urule == SGD_MOMENTUM) rows8(std::integral_constant<int, SGD_MOMENTUM>{}, v, h, a, d, st_r, vo, ld);
+        else if (p.urule == SGD_NESTEROV) rows8(std::integral_constant<int, SGD_NESTEROV>{}, v, h, a, d, st_r, vo, ld);
         else rows8(std::integral_constant<int, SGD_ADAGRAD>{}, v, h, a, d, st_r, vo, ld);
       }
     };
@@ -1179,7 +1187,9 @@ int gemm(const GemmDesc& d, hipStream_t s) {
   a.eta = d.eta;
   a.mu = d.mu;
   a.eps = d.eps;
-  if (d.urule >= 0 && (d.epi != EPI_STORE || d.accum)) {
+  a.decay = d.decay;
+  a.gscale = d.gscale;
+  if (d.urule >= 0 && (d.epi != EPI_STORE || d.accum || d.gscale != 1.f)) {
     set_error("gemm: an update rule can only replace a plain store");
     return SGD_EINVAL;
   }

@@ -15,6 +15,8 @@
 #include <string>
 #include <vector>
 
+#include <cmath>
+
 #include "common.h"
 #include "layers.h"
 
@@ -407,6 +409,7 @@ void set_update(GemmDesc& g, const sgd_rule* rule, float* state, const Stage& s)
   g.eta = rule->eta;
   g.mu = rule->mu;
   g.eps = rule->eps;
+  g.decay = rule->decay;
   g.ustate = state ? state + s.w_off : nullptr;
   g.ustate_b = state ? state + s.b_off : nullptr;
 }
@@ -495,7 +498,7 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
 // stream joins the side stream at the end, so the step stays one stream-
 // ordered operation for the caller.
 int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, bool accum, const sgd_rule* rule,
-                 float* state, void* ws, hipStream_t st) {
+                 float* state, float gscale, void* ws, hipStream_t st) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
   float* partial_dw = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_dw_off);
   float* dcol = reinterpret_cast<float*>(static_cast<char*>(ws) + net->dcol_off);
@@ -559,6 +562,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.partial_floats = net->partial_dw_floats;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
+      g.gscale = gscale;
       set_update(g, rule, state, s);
       if ((e = fork()) || (e = gemm(g, side))) continue;
     } else if (s.kind == SGD_MAXPOOL) {
@@ -593,6 +597,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.perm_k = s.K;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
+      g.gscale = gscale;
       set_update(g, rule, state, s);
       if ((e = fork()) || (e = gemm(g, side))) continue;
       if (!s.first_weighted) {
@@ -697,7 +702,7 @@ int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offs
 
 static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, bool accum,
                 const sgd_rule* rule, float* state, float* loss, void* ws, size_t ws_bytes, void* stream,
-                const char* who) {
+                const char* who, float gscale = 1.f) {
   if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, std::string(who) + ": null pointer");
   if ((int64_t)ws_bytes < net->ws_bytes)
     return fail(SGD_EWORKSPACE, std::string(who) + ": workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
@@ -707,7 +712,7 @@ static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, 
   (void)hipGetLastError();  // clear a stale error from an unrelated earlier call
   sgd::g_prof = &net->prof;
   int e = sgd::run_forward(net, W, X, y, loss, ws, st);
-  if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, ws, st);
+  if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, gscale, ws, st);
   sgd::g_prof = nullptr;
   return e;
 }
@@ -715,6 +720,20 @@ static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, 
 int sgd_compute_gradient(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, float* loss,
                          void* ws, size_t ws_bytes, void* stream) {
   return step(net, W, X, y, grad, false, nullptr, nullptr, loss, ws, ws_bytes, stream, "sgd_compute_gradient");
+}
+
+int sgd_compute_gradient_into_scaled(sgd_net* net, const float* W, const float* X, const int32_t* y,
+                                     sgd_gradbuf* gb, float scale, float* loss, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!std::isfinite(scale)) return fail(SGD_EINVAL, "sgd_compute_gradient_into_scaled: non-finite scale");
+  if (!gb || !gb->data) return fail(SGD_EINVAL, "sgd_compute_gradient_into_scaled: null gradient buffer");
+  if (net && gb->n != net->n_params)
+    return fail(SGD_EINVAL, "sgd_compute_gradient_into_scaled: buffer length " + std::to_string(gb->n) +
+                                " != parameter count " + std::to_string(net->n_params));
+  const int e = step(net, W, X, y, gb->data, gb->empty == 0, nullptr, nullptr, loss, ws, ws_bytes, stream,
+                     "sgd_compute_gradient_into_scaled", scale);
+  if (!e) gb->empty = 0;
+  return e;
 }
 
 int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, const int32_t* y, sgd_gradbuf* gb,
@@ -793,7 +812,8 @@ int sgd_accumulate_grads(sgd_gradbuf* gb, const float* const* grads, int k, void
 
 static int check_rule(const sgd_rule* rule, const float* state, const char* who) {
   if (!rule) return fail(SGD_EINVAL, std::string(who) + ": null rule");
-  if (rule->rule != SGD_PLAIN && rule->rule != SGD_MOMENTUM && rule->rule != SGD_ADAGRAD)
+  if (rule->rule != SGD_PLAIN && rule->rule != SGD_MOMENTUM && rule->rule != SGD_ADAGRAD &&
+      rule->rule != SGD_NESTEROV)
     return fail(SGD_EINVAL, std::string(who) + ": unknown rule");
   if (rule->rule != SGD_PLAIN && !state) return fail(SGD_EINVAL, std::string(who) + ": rule needs a state buffer");
   return SGD_OK;
@@ -806,12 +826,13 @@ int sgd_apply_update(float* W, sgd_gradbuf* gb, float* state, const sgd_rule* ru
   int e = SGD_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (gb->empty) {
-    // zero gradient: plain and Adagrad leave W (and A) unchanged; momentum decays V
-    if (rule->rule == SGD_MOMENTUM)
-      e = sgd::apply_rule(W, state, nullptr, 0, gb->n, rule->rule, rule->eta, rule->mu, rule->eps, st);
+    // zero gradient: without weight decay plain and Adagrad leave W (and A)
+    // unchanged; the momentum rules still decay V (and move W)
+    if (rule->rule == SGD_MOMENTUM || rule->rule == SGD_NESTEROV || rule->decay != 0.f)
+      e = sgd::apply_rule(W, state, nullptr, 0, gb->n, rule->rule, rule->eta, rule->mu, rule->eps, rule->decay, st);
   } else {
     const float* g[1] = {gb->data};
-    e = sgd::apply_rule(W, state, g, 1, gb->n, rule->rule, rule->eta, rule->mu, rule->eps, st);
+    e = sgd::apply_rule(W, state, g, 1, gb->n, rule->rule, rule->eta, rule->mu, rule->eps, rule->decay, st);
   }
   if (!e) gb->empty = 1;
   return e;
@@ -825,7 +846,7 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
   for (int j = 0; j < k; ++j)
     if (!grads[j]) return fail(SGD_EINVAL, "sgd_apply_fused: null gradient pointer");
   if (int e = check_rule(rule, state, "sgd_apply_fused")) return e;
-  return sgd::apply_rule(W, state, grads, k, n, rule->rule, rule->eta, rule->mu, rule->eps,
+  return sgd::apply_rule(W, state, grads, k, n, rule->rule, rule->eta, rule->mu, rule->eps, rule->decay,
                          static_cast<hipStream_t>(stream));
 }
 

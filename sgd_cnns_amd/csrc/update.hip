@@ -81,7 +81,7 @@ __global__ void accumulate_kernel(float* __restrict__ buf, Ptrs P, int k, int fi
 
 template <int RULE>
 __global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, Ptrs P, int k, int64_t n, float eta,
-                             float mu, float eps, int vec) {
+                             float mu, float eps, float decay, int vec) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   constexpr bool kState = RULE != SGD_PLAIN;
@@ -97,7 +97,7 @@ __global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, P
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        rule1<RULE>(w[u], st[u], g[u], eta, mu, eps);
+        rule1<RULE>(w[u], st[u], g[u], eta, mu, eps, decay);
         st4(W, i + u * stride, w[u]);
         if (kState) st4(state, i + u * stride, st[u]);
       }
@@ -106,7 +106,7 @@ __global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, P
       v4f g = k > 0 ? fold4(P, k, i) : v4f{0.f, 0.f, 0.f, 0.f};
       v4f w = ld4(W, i);
       v4f st = kState ? ld4(state, i) : v4f{0.f, 0.f, 0.f, 0.f};
-      rule1<RULE>(w, st, g, eta, mu, eps);
+      rule1<RULE>(w, st, g, eta, mu, eps, decay);
       st4(W, i, w);
       if (kState) st4(state, i, st);
     }
@@ -116,7 +116,7 @@ __global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, P
     const float g = k > 0 ? fold1(P, k, i) : 0.f;
     float w = W[i];
     float st = kState ? state[i] : 0.f;
-    rule1<RULE>(w, st, g, eta, mu, eps);
+    rule1<RULE>(w, st, g, eta, mu, eps, decay);
     W[i] = w;
     if (kState) state[i] = st;
   }
@@ -150,7 +150,7 @@ int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy,
 }
 
 int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t n, int rule, float eta, float mu,
-               float eps, hipStream_t s) {
+               float eps, float decay, hipStream_t s) {
   Ptrs P{};
   bool vec = a16(W) && (rule == SGD_PLAIN || a16(state));
   for (int j = 0; j < k; ++j) {
@@ -158,18 +158,21 @@ int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t
     vec = vec && a16(grads[j]);
   }
   const dim3 g(grid_for(n)), b(kBlock);
-  static const char* const names[3] = {"apply_plain", "apply_momentum", "apply_adagrad"};
+  static const char* const names[4] = {"apply_plain", "apply_momentum", "apply_adagrad", "apply_nesterov"};
   const double streams = k + (rule == SGD_PLAIN ? 2 : 4);
   prof_begin(names[rule], (double)n * (k + 4), 4.0 * streams * n, s);
   switch (rule) {
     case SGD_PLAIN:
-      hipLaunchKernelGGL(apply_kernel<SGD_PLAIN>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, (int)vec);
+      hipLaunchKernelGGL(apply_kernel<SGD_PLAIN>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
       break;
     case SGD_MOMENTUM:
-      hipLaunchKernelGGL(apply_kernel<SGD_MOMENTUM>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, (int)vec);
+      hipLaunchKernelGGL(apply_kernel<SGD_MOMENTUM>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
+      break;
+    case SGD_NESTEROV:
+      hipLaunchKernelGGL(apply_kernel<SGD_NESTEROV>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
       break;
     default:
-      hipLaunchKernelGGL(apply_kernel<SGD_ADAGRAD>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, (int)vec);
+      hipLaunchKernelGGL(apply_kernel<SGD_ADAGRAD>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
       break;
   }
   prof_end(s);

@@ -170,7 +170,7 @@ def test_compute_gradient_into_vgg_split_k_paths():
     np.testing.assert_array_equal(gb.data.cpu().numpy(), (g0 + grad.cpu().numpy()).astype(np.float32))
 
 
-@pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad"])
+@pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad", "nesterov_wd"])
 @pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged", "mlp5000"])
 def test_train_step_equals_gradient_then_apply(rule, case):
     # the fused step (update applied in the dedw epilogues / split-K reduction)
@@ -194,7 +194,8 @@ def test_train_step_equals_gradient_then_apply(rule, case):
     st0 = workloads.normal(9, 3, n, 1e-3)
     if rule == "adagrad":
         st0 = np.abs(st0) + np.float32(0.1)
-    R = S.Rule(rule, 0.01, 0.9, 1e-8)
+    # nesterov_wd: Nesterov momentum with weight decay 5e-4 (PIPE appendix A)
+    R = S.Rule("nesterov", 0.01, 0.9, 0.0, 5e-4) if rule == "nesterov_wd" else S.Rule(rule, 0.01, 0.9, 1e-8)
     ws = net.workspace()
     loss_a = torch.empty(1, device=dev)
     loss_b = torch.empty(1, device=dev)
@@ -252,3 +253,57 @@ def test_overlap_on_and_off_bitwise_equal(case):
     a, b = out[True], out[False]
     assert torch.equal(a[0], b[0]) and a[1] == b[1]
     assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3]) and a[4] == b[4]
+
+
+@pytest.mark.parametrize("case", ["mlp_ragged", "vgg_cifar_b2"])
+def test_prescaled_gradient(case):
+    # SPRINT Algorithm 1 line 10: the worker stores Grad = -eta * grad.  The
+    # scaled product rounds fl(scale * g) of the very g the unscaled path
+    # stores, added into a non-empty buffer the same way; applied with
+    # eta = -1 it gives the unscaled step's W and V bitwise; against the
+    # oracle's gradient it is within the gradient tolerance.
+    if case == "vgg_cifar_b2":
+        wl = workloads.WORKLOADS["vgg_cifar"].with_batch(2)
+    else:
+        wl = workloads.Workload("mlp_ragged", 31, 70, (3072, 1, 1),
+                                [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)])
+    print(f"[prescaled] {case}", flush=True)
+    X, y, W = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    n = net.param_count()
+    dev = torch.device("cuda")
+    Xd, yd, Wd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev), torch.from_numpy(W).to(dev)
+    ws = net.workspace()
+    loss = torch.empty(1, device=dev)
+    eta = np.float32(0.01)
+    g = torch.empty(n, device=dev)
+    net.compute_gradient(Wd, Xd, yd, g, loss, ws)
+    gs = S.GradBuf(n)
+    net.compute_gradient_into_scaled(Wd, Xd, yd, gs, float(-eta), loss, ws)
+    torch.cuda.synchronize()
+    g_np = g.cpu().numpy()
+    np.testing.assert_array_equal(gs.data.cpu().numpy(), (np.float32(-eta) * g_np).astype(np.float32))
+    # into a non-empty buffer: GradBuf + fl(scale * g)
+    base = workloads.normal(14, 1, n, 1e-3)
+    gb2 = S.GradBuf(n, data=torch.from_numpy(base).to(dev))
+    gb2.empty = False
+    net.compute_gradient_into_scaled(Wd, Xd, yd, gb2, float(-eta), loss, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gb2.data.cpu().numpy(), base + (np.float32(-eta) * g_np).astype(np.float32))
+    # apply with eta = -1 == the unscaled step
+    V0 = workloads.normal(14, 2, n, 1e-3)
+    Wa, Va = Wd.clone(), torch.from_numpy(V0).to(dev)
+    gu = S.GradBuf(n)
+    net.compute_gradient_into(Wd, Xd, yd, gu, loss, ws)
+    S.apply_update(Wa, gu, Va, S.Rule("momentum", float(eta), 0.9))
+    Wb, Vb = Wd.clone(), torch.from_numpy(V0).to(dev)
+    S.apply_update(Wb, gs, Vb, S.Rule("momentum", -1.0, 0.9))
+    torch.cuda.synchronize()
+    assert torch.equal(Wa, Wb) and torch.equal(Va, Vb)
+    # against the oracle
+    onet = O.OracleNet(wl.chw, wl.layers)
+    _, g_ref = onet.gradient(W, X, y)
+    wo = [onet.params[i][0] for i in sorted(onet.params)]
+    bo = [onet.params[i][2] for i in sorted(onet.params)]
+    per_tensor_grad_check((np.float32(-eta) * g_np).astype(np.float32), (np.float32(-eta) * g_ref).astype(np.float32),
+                          wo, bo, n)

@@ -156,3 +156,46 @@ def test_parameter_server_workload_full_size():
             torch.cuda.synchronize()
             assert np.array_equal(Wd.cpu().numpy()[sub], Wr)
             assert np.array_equal(Ad.cpu().numpy()[sub], Ar)
+
+
+# ----------------------------------------- rule variants: decay, Nesterov ----
+
+@pytest.mark.parametrize("n,offset", [(1000003, 0), (4099, 1)])
+@pytest.mark.parametrize("rule,decay", [("nesterov", 0.0), ("nesterov", 5e-4), ("plain", 5e-4), ("momentum", 5e-4),
+                                        ("adagrad", 5e-4)])
+def test_rule_variants_match_oracle(n, offset, rule, decay):
+    print(f"[update-variant] rule={rule} decay={decay} n={n} offset={offset}", flush=True)
+    W0 = workloads.normal(12, 2, n)
+    st0 = np.abs(workloads.normal(12, 3, n)) + np.float32(0.1) if rule == "adagrad" else \
+        workloads.normal(12, 3, n, 1e-3)
+    gs = [workloads.normal(12, 100 + j, n, 1e-3) for j in range(2)]
+    eta, mu, eps = 0.01, 0.9, 1e-8
+    gb = O.GradBuf(n)
+    for g in gs:
+        gb.accumulate(g)
+    Wr, sr = W0.copy(), st0.copy()
+    O.apply_rule(rule, Wr, sr, gb.data, eta, mu, eps, decay)
+    Wd, sd = dev(W0, offset), dev(st0, offset)
+    S.apply_fused(Wd, sd if rule != "plain" else None, [dev(g, offset) for g in gs], S.Rule(rule, eta, mu, eps, decay))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wd.cpu().numpy(), Wr)
+    if rule != "plain":
+        np.testing.assert_array_equal(sd.cpu().numpy(), sr)
+
+
+@pytest.mark.parametrize("rule", ["plain", "nesterov"])
+def test_empty_gradbuf_with_decay_matches_oracle(rule):
+    n = 5003
+    W0 = workloads.normal(13, 2, n)
+    V0 = workloads.normal(13, 3, n, 1e-3)
+    Wr, Vr = W0.copy(), V0.copy()
+    O.apply_rule(rule, Wr, Vr, None, 0.01, 0.9, 0.0, 5e-4)
+    Wd, Vd = dev(W0), dev(V0)
+    gb = S.GradBuf(n)
+    assert gb.empty
+    S.apply_update(Wd, gb, Vd if rule != "plain" else None, S.Rule(rule, 0.01, 0.9, 0.0, 5e-4))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wd.cpu().numpy(), Wr)
+    assert not np.array_equal(Wr, W0)
+    if rule != "plain":
+        np.testing.assert_array_equal(Vd.cpu().numpy(), Vr)

@@ -203,3 +203,110 @@ def test_adagrad_eps_is_outside_the_root():
 def test_relu_of_negative_zero_is_positive_zero():
     a = O.relu_fwd(np.array([-0.0, -1e-30], np.float32))
     assert not np.signbit(a).any()
+
+
+# ------------------------------------------------ rule variants (NEXT f4) ----
+# The PIPE report's appendix A trains with weight decay (5e-4) and Nesterov
+# momentum and SPRINT Algorithm 1 (line 10) scales the worker's gradient by
+# -eta; the pages give no formulas, so these pin the readings the oracle
+# implements: decay adds decay*W to the gradient before any rule, Nesterov
+# moves W by mu times the new change plus the gradient step.
+
+def test_nesterov_two_steps_closed_form():
+    W = np.array([1.0], np.float32)
+    V = np.array([0.0], np.float32)
+    g = np.array([1.0], np.float32)
+    O.apply_nesterov(W, V, g, 0.9, 0.01)
+    # V = -0.01, W = 1 + (0.9 * -0.01 - 0.01) = 0.981
+    assert V[0] == np.float32(-0.01)
+    assert abs(float(W[0]) - 0.981) <= float(np.spacing(np.float32(0.981)))
+    O.apply_nesterov(W, V, g, 0.9, 0.01)
+    # V = 0.9 * -0.01 - 0.01 = -0.019, W = 0.981 + (0.9 * -0.019 - 0.01) = 0.9539
+    assert V[0] == np.float32(-0.019)
+    assert abs(float(W[0]) - 0.9539) <= 2 * float(np.spacing(np.float32(0.9539)))
+
+
+def test_nesterov_with_zero_momentum_is_plain_sgd_bitwise():
+    W0, g, V0 = _rand(400, 11), _rand(400, 12, 1e-2), _rand(400, 13, 1e-3)
+    Wn, Vn = W0.copy(), V0.copy()
+    O.apply_nesterov(Wn, Vn, g, 0.0, 0.01)
+    Wp = W0.copy()
+    O.apply_plain(Wp, g, 0.01)
+    np.testing.assert_array_equal(Wn, Wp)
+
+
+def test_nesterov_matches_the_two_history_form_in_double():
+    # the same step written as W -= (1 + mu) H_new - mu H_old with the
+    # history H = mu H + eta g (H = -V): equal in exact arithmetic
+    n = 500
+    W0 = _rand(n, 14).astype(np.float64)
+    g = _rand(n, 15, 1e-2).astype(np.float64)
+    V0 = _rand(n, 16, 1e-3).astype(np.float64)
+    mu, eta = 0.9, 0.01
+    W, V = W0.copy(), V0.copy()
+    O.apply_nesterov(W, V, g, mu, eta)
+    h_old = -V0
+    h_new = mu * h_old + eta * g
+    ref = W0 - ((1 + mu) * h_new - mu * h_old)
+    np.testing.assert_allclose(V, -h_new, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(W, ref, rtol=0, atol=1e-14)
+
+
+def test_weight_decay_closed_form():
+    W = np.array([0.5], np.float32)
+    O.apply_plain(W, np.array([0.25], np.float32), 0.01, 5e-4)
+    # g' = 0.25 + 5e-4 * 0.5 = 0.25025;  W = 0.5 - 0.01 * 0.25025 = 0.4974975
+    lam, E = f32(5e-4), f32(0.01)
+    gp = rne32(Fr(1, 4) + rne32(lam * Fr(1, 2)))
+    assert Fr(float(W[0])) == rne32(Fr(1, 2) - rne32(E * gp))
+    assert abs(float(W[0]) - 0.4974975) <= float(np.spacing(np.float32(0.4974975)))
+
+
+def test_decayed_rules_match_exact_rounding_model():
+    n = 300
+    W0, g, V0 = _rand(n, 17), _rand(n, 18, 1e-2), _rand(n, 19, 1e-3)
+    A0 = np.abs(_rand(n, 20)) + np.float32(0.1)
+    eta, mu, eps, lam = np.float32(0.01), np.float32(0.9), np.float32(1e-8), np.float32(5e-4)
+    Wp = W0.copy(); O.apply_plain(Wp, g, eta, lam)
+    Wm, Vm = W0.copy(), V0.copy(); O.apply_momentum(Wm, Vm, g, mu, eta, lam)
+    Wn, Vn = W0.copy(), V0.copy(); O.apply_nesterov(Wn, Vn, g, mu, eta, lam)
+    Wa, Aa = W0.copy(), A0.copy(); O.apply_adagrad(Wa, Aa, g, eta, eps, lam)
+    E, M, P, L = Fr(float(eta)), Fr(float(mu)), Fr(float(eps)), Fr(float(lam))
+    for i in range(n):
+        w, v, a = Fr(float(W0[i])), Fr(float(V0[i])), Fr(float(A0[i]))
+        gi = rne32(Fr(float(g[i])) + rne32(L * w))          # wd = decay*W; g = g + wd
+        assert Fr(float(Wp[i])) == rne32(w - rne32(E * gi))
+        t2 = rne32(E * gi)
+        vn = rne32(rne32(M * v) - t2)
+        assert Fr(float(Vm[i])) == vn and Fr(float(Wm[i])) == rne32(w + vn)
+        assert Fr(float(Vn[i])) == vn
+        assert Fr(float(Wn[i])) == rne32(w + rne32(rne32(M * vn) - t2))
+        an = rne32(a + rne32(gi * gi))
+        r = rne32(E / rne32(sqrt32(an) + P))
+        assert Fr(float(Aa[i])) == an and Fr(float(Wa[i])) == rne32(w - rne32(r * gi))
+
+
+def test_empty_gradbuf_with_decay_still_decays():
+    W0 = _rand(64, 21)
+    W = W0.copy()
+    O.apply_rule("plain", W, None, None, 0.01, decay=5e-4)
+    E, L = Fr(float(np.float32(0.01))), Fr(float(np.float32(5e-4)))
+    for i in range(64):
+        w = Fr(float(W0[i]))
+        assert Fr(float(W[i])) == rne32(w - rne32(E * rne32(L * w)))
+
+
+def test_prescaled_gradient_applied_with_minus_one_is_bitwise_the_unscaled_step():
+    # SPRINT Algorithm 1 line 10 stores Grad = -eta * grad; applying that
+    # buffer with eta = -1 rounds exactly like applying grad with eta
+    # (-1 * fl(-eta g) = fl(eta g), negation is exact)
+    W0, g, V0 = _rand(300, 22), _rand(300, 23, 1e-2), _rand(300, 24, 1e-3)
+    eta = np.float32(0.01)
+    G = (np.float32(-eta) * g).astype(np.float32)
+    for rule in ("plain", "momentum", "nesterov"):
+        Wa, Va = W0.copy(), V0.copy()
+        O.apply_rule(rule, Wa, Va, g, eta, mu=0.9)
+        Wb, Vb = W0.copy(), V0.copy()
+        O.apply_rule(rule, Wb, Vb, G, -1.0, mu=0.9)
+        np.testing.assert_array_equal(Wa, Wb)
+        np.testing.assert_array_equal(Va, Vb)
