@@ -247,6 +247,20 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
                     const sgd_rule* rule, void* stream);
 
 /*
+ * Implicit-GEMM convolution (on by default).  A conv layer whose input is
+ * an activation of this network with Ci % 16 == 0 gathers the im2col
+ * operand of its forward and dedw products straight from that activation
+ * (SPRINT section 3.3's im2col matrix is never written), and a conv layer
+ * with Co % 16 == 0 (not the first) computes dedx as one gather-form product
+ * over its output gradient with the ReLU mask in the epilogue, in place of
+ * the dCol product and col2im.  Other layers use the explicit im2col path.
+ * Changing the setting re-plans the workspace: query sgd_workspace_bytes
+ * again.  The forward and dedw results are bitwise the same either way; dedx
+ * sums its terms in another order.  Errors: SGD_EINVAL (null net).
+ */
+int sgd_set_implicit_conv(sgd_net* net, int enable);
+
+/*
  * Backward-pass concurrency.  With overlap on (the default) each layer's
  * dedw product runs on a second stream the library owns, forked from the
  * caller's stream once the product's inputs are final and joined back into

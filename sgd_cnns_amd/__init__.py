@@ -33,7 +33,7 @@ LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
-           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_profile", "sgd_profile_read",
+           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_profile", "sgd_profile_read",
            "sgd_last_error"]
 
 
@@ -92,6 +92,7 @@ def lib():
             "sgd_train_step": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P, sz, P]),
             "sgd_profile": (i, [P, i]),
             "sgd_set_overlap": (i, [P, i]),
+            "sgd_set_implicit_conv": (i, [P, i]),
             "sgd_profile_read": (i, [P, C.POINTER(SgdKernelTime), i]),
             "sgd_last_error": (C.c_char_p, []),
         }
@@ -207,6 +208,10 @@ class Net:
         if which == T_ARGMAX:
             return ws[off:off + n].view(shape)
         return ws[off:off + 4 * n].view(torch.float32).view(shape)
+
+    def set_implicit_conv(self, enable):
+        """Implicit-GEMM convolutions where the shapes allow (default on); re-plans the workspace."""
+        _check(lib().sgd_set_implicit_conv(self._h, 1 if enable else 0))
 
     def set_overlap(self, enable):
         """Run the dedw products on a second stream, overlapping the next layer (default on)."""

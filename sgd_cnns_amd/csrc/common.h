@@ -41,6 +41,20 @@ enum Epilogue : int {
   EPI_ACCUM = 4,      // C = C + v
 };
 
+// An implicit-GEMM operand: the rows (A) or k-rows (B) of the product run
+// over a pixel grid RH x RW per image, and the index (ky*c + kx)*SC + ch over
+// the c x c taps and SC channels of the NHWC source `src` (SH x SW pixels
+// per image): channel ch of source pixel (y + dy, x + dx) with dy = ky - P,
+// or dy = P - ky when `flip` (the dedx gather over the output gradient);
+// zero outside the source.  inv_* are 1.0f/RW and 1.0f/RH.
+struct ConvGather {
+  const float* src;
+  int RH, RW;
+  int SH, SW, SC;
+  int c, P, flip;
+  float inv_RW, inv_RH;
+};
+
 struct GemmDesc {
   const float* A;
   const float* B;
@@ -94,6 +108,11 @@ struct GemmDesc {
   // gemm_dma schedule override: sk_grid > 0 forces that many blocks with
   // the first sk_dp tiles done whole and the rest by stream-K.
   int sk_grid = -1, sk_dp = 0;
+  // Implicit GEMM: 1 = A (K-contiguous, not transposed) is gathered by cv
+  // (A and lda are ignored); 2 = B (row-contiguous, transposed) is (B and
+  // ldb are ignored).  Needs cv.SC % 16 == 0 for A, % 4 == 0 for B.
+  int gather = 0;
+  ConvGather cv{};
 };
 
 int gemm(const GemmDesc& d, hipStream_t s);

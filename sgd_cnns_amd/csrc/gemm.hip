@@ -87,6 +87,7 @@ struct KArgs {
   int a_vec, b_vec;  // float4 global loads allowed (aligned base, ld % 4 == 0)
   int tiles_n;       // tiles along Nt
   int tiles;         // tiles per split
+  ConvGather cv;     // implicit-GEMM operand (see GemmDesc::gather)
 };
 
 // One operand slice: R rows (of the output) x BK values of k.
@@ -644,6 +645,119 @@ struct DmaT {
   }
 };
 
+// ---- implicit-GEMM operands: convolution windows gathered straight from an
+// NHWC activation tensor (no im2col matrix in HBM).
+//
+// Row index q of the product runs over a pixel grid RH x RW (per image);
+// column/k index (ky*c + kx)*SC + ch selects channel ch of source pixel
+// (y + dy, x + dx) of the SH x SW x SC source, dy = ky - P (dy = P - ky when
+// `flip`, the dedx gather), zero outside the source.
+
+// q / d for 0 <= q < 2^22 from a float reciprocal, corrected to exact.
+__device__ __forceinline__ int fdiv(int q, int d, float inv) {
+  int r = (int)((float)q * inv);
+  const int rem = q - r * d;
+  r += (rem >= d) - (rem < 0);
+  return r;
+}
+
+// K-contiguous gather (the A operand of conv forward and of dedx): LDS
+// layout and operand reads as DmaK.  A 16-deep k-slice lies inside one tap
+// (SC % 16 == 0), so each row's slice is 64 contiguous bytes of one source
+// pixel.
+template <int R>
+struct DmaKg : DmaK<R> {
+  using Base = DmaK<R>;
+  static constexpr int NI = Base::NI;
+  struct Item {
+    i32x4 rs;
+    int base[NI];  // first channel of the row's image in the source (floats)
+    int y[NI], x[NI];
+    int kbeg;
+  };
+  __device__ static __forceinline__ Item prep(const ConvGather& g, int m0, int rvalid, int kbeg) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    Item it;
+    it.rs = buffer_rsrc(g.src);
+    it.kbeg = kbeg;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = ((wave * NI + j) * 64 + lane) >> 2;
+      const int q = m0 + r;
+      const int t = fdiv(q, g.RW, g.inv_RW);
+      const int n = fdiv(t, g.RH, g.inv_RH);
+      it.x[j] = q - t * g.RW;
+      it.y[j] = r < rvalid ? t - n * g.RH : -(1 << 20);  // rows past M read zeros
+      it.base[j] = n * g.SH * g.SW * g.SC;
+    }
+    return it;
+  }
+  __device__ static __forceinline__ void load(const Item& it, const ConvGather& g, float* S, int kk, int kvalid) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ka = it.kbeg + kk;
+    const int tap = ka / g.SC, ch0 = ka - tap * g.SC;
+    const int ky = tap / g.c, kx = tap - ky * g.c;
+    const int dy = g.flip ? g.P - ky : ky - g.P;
+    const int dx = g.flip ? g.P - kx : kx - g.P;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int qi = (wave * NI + j) * 64 + lane;
+      const int r = qi >> 2, q4 = (qi & 3) ^ Base::swz(r);
+      const int sy = it.y[j] + dy, sx = it.x[j] + dx;
+      const bool ok = kk + 4 * q4 < kvalid && (unsigned)sy < (unsigned)g.SH && (unsigned)sx < (unsigned)g.SW;
+      const uint32_t off = (uint32_t)(it.base[j] + (sy * g.SW + sx) * g.SC + ch0 + 4 * q4) * 4u;
+      dma16(it.rs, S + (wave * NI + j) * 256, ok ? off : kOffBad);
+    }
+  }
+};
+
+// Row-contiguous gather (the B operand of conv dedw, Col viewed as [pixel]
+// [(ky,kx,ch)]): LDS layout, operand reads and the ones-column fix-up as
+// DmaT.  A 4-column quad lies inside one tap (SC % 4 == 0).
+template <int R>
+struct DmaTg : DmaT<R> {
+  using Base = DmaT<R>;
+  static constexpr int NI = Base::NI;
+  struct Item {
+    i32x4 rs;
+    int ch[NI], dy[NI], dx[NI];  // the quad's channel and tap offset; dy < -2^19: column past N
+    int kbeg;
+  };
+  __device__ static __forceinline__ Item prep(const ConvGather& g, int n0, int rvalid, int kbeg) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    Item it;
+    it.rs = buffer_rsrc(g.src);
+    it.kbeg = kbeg;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int qi = (wave * NI + j) * 64 + lane;
+      const int k = qi / Base::Q, c4 = (qi % Base::Q) ^ Base::swzT(k);
+      const int col = n0 + 4 * c4;
+      const int tap = col / g.SC;
+      const int ky = tap / g.c, kx = tap - ky * g.c;
+      it.ch[j] = col - tap * g.SC;
+      it.dy[j] = 4 * c4 < rvalid ? ky - g.P : -(1 << 20);
+      it.dx[j] = kx - g.P;
+    }
+    return it;
+  }
+  __device__ static __forceinline__ void load(const Item& it, const ConvGather& g, float* S, int kk, int kvalid) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int qi = (wave * NI + j) * 64 + lane;
+      const int k = qi / Base::Q;
+      const int q = it.kbeg + kk + k;  // pixel of this k-row
+      const int t = fdiv(q, g.RW, g.inv_RW);
+      const int n = fdiv(t, g.RH, g.inv_RH);
+      const int sy = t - n * g.RH + it.dy[j], sx = q - t * g.RW + it.dx[j];
+      const bool ok = kk + k < kvalid && (unsigned)sy < (unsigned)g.SH && (unsigned)sx < (unsigned)g.SW;
+      const uint32_t off = (uint32_t)(((n * g.SH + sy) * g.SW + sx) * g.SC + it.ch[j]) * 4u;
+      dma16(it.rs, S + (wave * NI + j) * 256, ok ? off : kOffBad);
+    }
+  }
+};
+
 // Stream-K schedule of one gemm_dma launch.  Blocks first take whole tiles
 // round-robin (tiles [0, dp_tiles)); the k-slices of the remaining tiles,
 // flattened tile by tile, are then cut into gridDim.x equal contiguous
@@ -679,12 +793,15 @@ __device__ __forceinline__ int64_t slot_index(int wave, int a, int c, int q, int
   return ((((int64_t)(wave * TM + a) * TN + c) * 4 + q) * 64 + lane) * 4;
 }
 
-template <int BM, int BN, bool AT, bool BT, int EM>
+// GA: the A operand is a K-contiguous convolution gather (DmaKg); GB: the B
+// operand is a row-contiguous one (DmaTg).
+template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
 __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  using SA = typename std::conditional<AT, DmaT<BM>, DmaK<BM>>::type;
-  using SB = typename std::conditional<BT, DmaT<BN>, DmaK<BN>>::type;
+  static_assert(!(GA && AT) && !(GB && !BT), "gathers: K-contiguous A, row-contiguous B");
+  using SA = typename std::conditional<GA, DmaKg<BM>, typename std::conditional<AT, DmaT<BM>, DmaK<BM>>::type>::type;
+  using SB = typename std::conditional<GB, DmaTg<BN>, typename std::conditional<BT, DmaT<BN>, DmaK<BN>>::type>::type;
   constexpr int kLoads = SA::NI + SB::NI;
   __shared__ __align__(16) float lds[kDmaStages * (SA::SIZE + SB::SIZE)];
   static_assert(kDmaStages * (SA::SIZE + SB::SIZE) >= 4 * 1024, "LDS too small for the generic epilogue");
@@ -737,9 +854,21 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     const int nsl = k1 - k0;
     const int arows = p.M - m0, brows = p.N - n0;
     const int ones_col = (p.Nt > p.N && p.N >= n0 && p.N < n0 + BN) ? p.N - n0 : -1;
-    const i32x4 ra = buffer_rsrc(AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
-    const i32x4 rb = buffer_rsrc(BT ? p.B + (int64_t)kbeg * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + kbeg);
+    const i32x4 ra = buffer_rsrc(GA ? p.A : AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
+    const i32x4 rb = buffer_rsrc(GB ? p.B : BT ? p.B + (int64_t)kbeg * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + kbeg);
     const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
+    typename DmaKg<BM>::Item ga{};
+    typename DmaTg<BN>::Item gb{};
+    if constexpr (GA) ga = DmaKg<BM>::prep(p.cv, m0, arows, kbeg);
+    if constexpr (GB) gb = DmaTg<BN>::prep(p.cv, n0, brows, kbeg);
+    auto load_a = [&](float* S, int kk) {
+      if constexpr (GA) DmaKg<BM>::load(ga, p.cv, S, kk, kval);
+      else SA::load(ra, S, lda, arows, kk, kval);
+    };
+    auto load_b = [&](float* S, int kk) {
+      if constexpr (GB) DmaTg<BN>::load(gb, p.cv, S, kk, kval);
+      else SB::load(rb, S, ldb, brows, kk, kval);
+    };
 
 #pragma unroll
     for (int a = 0; a < TM; ++a)
@@ -753,8 +882,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     // arithmetic) the same for every slice.
 #pragma unroll
     for (int st = 0; st < kDmaStages - 1; ++st) {
-      SA::load(ra, As[st], lda, arows, st * kDmaBK, kval);
-      SB::load(rb, Bs[st], ldb, brows, st * kDmaBK, kval);
+      load_a(As[st], st * kDmaBK);
+      load_b(Bs[st], st * kDmaBK);
     }
     for (int i = 0; i < nsl; ++i) {
       const int cur = i % kDmaStages;
@@ -762,8 +891,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
       if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval);
       lds_barrier();  // everyone's loads of slice i landed; everyone finished slice i-1
       const int nx = i + kDmaStages - 1;  // refill the buffer slice i-1 used
-      SA::load(ra, As[nx % kDmaStages], lda, arows, nx * kDmaBK, kval);
-      SB::load(rb, Bs[nx % kDmaStages], ldb, brows, nx * kDmaBK, kval);
+      load_a(As[nx % kDmaStages], nx * kDmaBK);
+      load_b(Bs[nx % kDmaStages], nx * kDmaBK);
 #pragma unroll
       for (int g = 0; g < kDmaBK / 8; ++g) {
         float4 av[TM], bv[TN];
@@ -902,6 +1031,12 @@ const char* const kNames[kStagedConfigs][4] = {
     {"gemm_staged_128x64_nt", "gemm_staged_128x64_tn", "gemm_staged_128x64_nn", "gemm_staged_128x64_tt"},
     {"gemm_staged_64x128_nt", "gemm_staged_64x128_tn", "gemm_staged_64x128_nn", "gemm_staged_64x128_tt"},
 };
+// Convolution gathers: forward, dedx (the flipped gather), dedw.
+const char* const kConvNames[kDmaConfigs][3] = {
+    {"gemm_conv_fwd_128x128", "gemm_conv_dx_128x128", "gemm_conv_dw_128x128"},
+    {"gemm_conv_fwd_128x64", "gemm_conv_dx_128x64", "gemm_conv_dw_128x64"},
+    {"gemm_conv_fwd_64x128", "gemm_conv_dx_64x128", "gemm_conv_dw_64x128"},
+};
 const char* const kDmaNames[kDmaConfigs][4] = {
     {"gemm_dma_128x128_nt", "gemm_dma_128x128_tn", "gemm_dma_128x128_nn", "gemm_dma_128x128_tt"},
     {"gemm_dma_128x64_nt", "gemm_dma_128x64_tn", "gemm_dma_128x64_nn", "gemm_dma_128x64_tt"},
@@ -953,12 +1088,23 @@ struct DmaFns {
   FixKernel fix;
   int bm, bn;
 };
-template <int BM, int BN, bool AT, bool BT, int EM>
+template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
 DmaFns dma_inst() {
-  return {gemm_dma<BM, BN, AT, BT, EM>, gemm_sk_fixup<BM, BN>, BM, BN};
+  return {gemm_dma<BM, BN, AT, BT, EM, GA, GB>, gemm_sk_fixup<BM, BN>, BM, BN};
 }
 template <int BM, int BN>
-DmaFns dma_fns_of(int form, int em) {
+DmaFns dma_fns_of(int form, int em, int gather) {
+  if (gather == 1) {  // conv forward (bias) and dedx (mask or plain store)
+    if (em == EM_BIAS) return dma_inst<BM, BN, false, false, EM_BIAS, true>();
+    if (em == EM_MASK) return dma_inst<BM, BN, false, false, EM_MASK, true>();
+    if (em == EM_STORE) return dma_inst<BM, BN, false, false, EM_STORE, true>();
+    return dma_inst<BM, BN, false, false, EM_GENERIC, true>();
+  }
+  if (gather == 2) {  // conv dedw
+    if (em == EM_DW) return dma_inst<BM, BN, true, true, EM_DW, false, true>();
+    if (em == EM_UPDATE) return dma_inst<BM, BN, true, true, EM_UPDATE, false, true>();
+    return dma_inst<BM, BN, true, true, EM_GENERIC, false, true>();
+  }
   switch (form) {
     case 0:
       if (em == EM_BIAS) return dma_inst<BM, BN, false, false, EM_BIAS>();
@@ -977,11 +1123,11 @@ DmaFns dma_fns_of(int form, int em) {
       return dma_inst<BM, BN, true, false, EM_GENERIC>();
   }
 }
-DmaFns dma_fns(int cfg, int form, int em) {
+DmaFns dma_fns(int cfg, int form, int em, int gather) {
   switch (cfg) {
-    case 0: return dma_fns_of<128, 128>(form, em);
-    case 1: return dma_fns_of<128, 64>(form, em);
-    default: return dma_fns_of<64, 128>(form, em);
+    case 0: return dma_fns_of<128, 128>(form, em, gather);
+    case 1: return dma_fns_of<128, 64>(form, em, gather);
+    default: return dma_fns_of<64, 128>(form, em, gather);
   }
 }
 
@@ -1119,7 +1265,23 @@ bool dma_ok(const GemmDesc& d) {
     return t ? rows % 4 == 0 : d.K % 4 == 0;
   };
   if (d.ones_out && d.N % 4) return false;
-  return operand_ok(d.A, d.lda, d.a_t, d.M) && operand_ok(d.B, d.ldb, d.b_t, d.N);
+  return (d.gather == 1 || operand_ok(d.A, d.lda, d.a_t, d.M)) && (d.gather == 2 || operand_ok(d.B, d.ldb, d.b_t, d.N));
+}
+
+// Preconditions of a convolution gather: the form it is built for, channel
+// counts that keep a slice (A) or a quad (B) inside one tap, an aligned
+// source, 32-bit offsets into it and pixel indices below 2^22 (the float
+// reciprocal division is exact there).
+bool gather_ok(const GemmDesc& d) {
+  const ConvGather& g = d.cv;
+  if (d.gather == 0) return true;
+  if (!g.src || !aligned16(g.src) || g.c < 1 || g.P < 0 || g.RH < 1 || g.RW < 1 || g.SH < 1 || g.SW < 1) return false;
+  const int64_t pix = d.gather == 1 ? d.M : d.K;  // the gathered pixel index
+  if (pix % ((int64_t)g.RH * g.RW) || pix + 256 >= ((int64_t)1 << 22)) return false;
+  const int64_t imgs = pix / ((int64_t)g.RH * g.RW);
+  if (imgs * g.SH * g.SW * g.SC * 4 + 64 >= (int64_t)kOffBad) return false;
+  if (d.gather == 1) return !d.a_t && !d.b_t && g.SC % 16 == 0 && d.K == g.c * g.c * g.SC;
+  return d.a_t && d.b_t && g.SC % 4 == 0 && d.N == g.c * g.c * g.SC;
 }
 
 // Every offset a work item of up to `slices` k-slices addresses from its
@@ -1129,7 +1291,8 @@ bool dma_span_ok(const GemmDesc& d, const Cfg& c, int64_t slices) {
     const int64_t k = slices * kDmaBK;
     return (t ? (k - 1) * ld + tile : (int64_t)(tile - 1) * ld + k) * 4;
   };
-  return span(d.lda, d.a_t, c.bm) < (int64_t)kOffBad && span(d.ldb, d.b_t, c.bn) < (int64_t)kOffBad;
+  return (d.gather == 1 || span(d.lda, d.a_t, c.bm) < (int64_t)kOffBad) &&
+         (d.gather == 2 || span(d.ldb, d.b_t, c.bn) < (int64_t)kOffBad);
 }
 
 int form_of(bool a_t, bool b_t) { return (!a_t && !b_t) ? 0 : (a_t && b_t) ? 1 : (!a_t && b_t) ? 2 : 3; }
@@ -1215,10 +1378,15 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     dma = dma_ok(d);
     if (!dma) cfg = staged_cfg(d.M, a.Nt);
   }
+  if (d.gather && (!dma || !gather_ok(d))) {
+    set_error("gemm: the convolution gather's preconditions do not hold");
+    return SGD_EINVAL;
+  }
   if (dma && !dma_ok(d)) {
     set_error("gemm: operands do not meet the direct-load preconditions");
     return SGD_EINVAL;
   }
+  a.cv = d.cv;
   const double flops = d.flops > 0 ? d.flops : 2.0 * d.M * d.N * (double)d.K;
   const double bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * a.Nt);
 
@@ -1254,7 +1422,7 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     }
     const int64_t item = plan.dp > 0 ? ipt : std::min<int64_t>(ipt, ceil_div(plan.sk_iters, plan.grid));
     if (!dma_span_ok(d, c, item)) {
-      if (d.cfg >= 0) {
+      if (d.cfg >= 0 || d.gather) {
         set_error("gemm: a work item spans more than 2 GiB of an operand");
         return SGD_EINVAL;
       }
@@ -1271,10 +1439,10 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     a.ldc = d.ldc;
     a.split = 0;
     a.k_per_split = (int)round_up(d.K, kDmaBK);
-    const DmaFns f = dma_fns(cfg, form, epi_mode(d, form));
+    const DmaFns f = dma_fns(cfg, form, epi_mode(d, form), d.gather);
     const int64_t T = a.tiles, ipt = ceil_div(d.K, kDmaBK), tile = (int64_t)c.bm * c.bn;
     const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial};
-    prof_begin(kDmaNames[cfg][form], flops, bytes, s);
+    prof_begin(d.gather ? kConvNames[cfg][d.gather == 2 ? 2 : (d.cv.flip ? 1 : 0)] : kDmaNames[cfg][form], flops, bytes, s);
     hipLaunchKernelGGL(f.main, dim3(plan.grid), dim3(kThreads), 0, s, a, sk);
     prof_end(s);
     if (int e = check_launch("gemm")) return e;

@@ -160,6 +160,19 @@ __global__ void repack_conv_weight(const float* __restrict__ w, float* __restric
   }
 }
 
+// W''[ci][(ky*c + kx)*Co + co] = W[co][ci][ky][kx]: the B operand of the
+// gather-form dedx product (each input pixel gathers its c*c taps of the
+// output gradient, Co channels each, against these rows).
+__global__ void repack_conv_weight_dx(const float* __restrict__ w, float* __restrict__ wdx, int Co, int Ci, int c) {
+  const int64_t ldk = (int64_t)c * c * Co;
+  const int64_t total = (int64_t)Ci * ldk;
+  GRID_STRIDE(i, total) {
+    const int ci = (int)(i / ldk), kk = (int)(i - (int64_t)ci * ldk);
+    const int tap = kk / Co, co = kk - tap * Co;
+    wdx[i] = w[((int64_t)co * Ci + ci) * c * c + tap];
+  }
+}
+
 // --------------------------------------------------------------- max pool ----
 // p x p windows, stride p, over NHWC input.  The window is scanned row-major
 // and a strict '>' keeps the first maximum; a NaN in the window makes the
@@ -322,6 +335,14 @@ int repack_weight(const float* w, float* wrep, int Co, int Ci, int c, int ldk, h
                      ldk);
   prof_end(s);
   return check_launch("repack_weight");
+}
+
+int repack_weight_dx(const float* w, float* wdx, int Co, int Ci, int c, hipStream_t s) {
+  const int64_t total = (int64_t)Ci * c * c * Co;
+  prof_begin("repack_weight_dx", 0, 8.0 * (double)total, s);
+  hipLaunchKernelGGL(repack_conv_weight_dx, dim3(grid_for(total)), dim3(kBlock), 0, s, w, wdx, Co, Ci, c);
+  prof_end(s);
+  return check_launch("repack_weight_dx");
 }
 
 int maxpool_fwd(const float* x, float* y, uint8_t* argmax, int N, int C, int H, int W, int p, bool out_nchw,

@@ -145,7 +145,13 @@ struct Stage {
   bool out_nchw = false;             // pool: output written NCHW (feeds an fc)
   int64_t w_off = -1, b_off = -1;    // parameter offsets (elements)
   int split_fwd = 1, split_dw = 1, split_dx = 1;
-  Tensor out, dout, col, wrep, argmax;
+  // conv: implicit GEMM.  `implicit`: the forward and dedw products gather
+  // their im2col operand straight from the NHWC input (no Col in HBM; needs
+  // Ci % 16 == 0 and an NHWC input).  `implicit_dx`: dedx is one gather-form
+  // product over the output gradient (needs Co % 16 == 0), replacing the dCol
+  // product and col2im.
+  bool implicit = false, implicit_dx = false;
+  Tensor out, dout, col, wrep, wdx, argmax;
 };
 
 }  // namespace
@@ -171,7 +177,8 @@ struct sgd_net {
   int64_t dcol_off = 0;
   sgd::Profiler prof;
   sgd::SideStream side;
-  bool overlap = true;  // dedw products on the side stream
+  bool overlap = true;   // dedw products on the side stream
+  bool implicit = true;  // implicit-GEMM convolutions where the shapes allow
 };
 
 namespace sgd {
@@ -210,6 +217,9 @@ int plan(sgd_net* net) {
   if (in.batch <= 0 || in.channels <= 0 || in.height <= 0 || in.width <= 0)
     return fail(SGD_ESHAPE, "input sizes must be positive");
   auto& st = net->stages;
+  st.clear();
+  net->w_offs.clear();
+  net->b_offs.clear();
   const int n_layers = (int)net->spec.size();
   net->spec_to_stage.assign(n_layers, -1);
   // current activation: producing stage (-1 = images), shape, whether flat
@@ -344,8 +354,13 @@ int plan(sgd_net* net) {
     const int64_t N = s.N;
     if (s.kind == SGD_CONV) {
       const int64_t P = N * s.Ho * s.Wo;
+      const int64_t Pin = N * s.H * s.W;
+      // pixel indices of the gathers stay below 2^22 (their float division)
+      s.implicit = net->implicit && s.input >= 0 && s.Ci % 16 == 0 && P + 256 < (1 << 22);
+      s.implicit_dx = net->implicit && !s.first_weighted && s.Co % 16 == 0 && Pin + 256 < (1 << 22);
       s.wrep = make_tensor(b, 4, SGD_LAYOUT_ROWS, s.Co, s.K, s.ldk, 1);
-      s.col = make_tensor(b, 4, SGD_LAYOUT_ROWS, P, s.K, s.ldk, 1);
+      if (!s.implicit) s.col = make_tensor(b, 4, SGD_LAYOUT_ROWS, P, s.K, s.ldk, 1);
+      if (s.implicit_dx) s.wdx = make_tensor(b, 4, SGD_LAYOUT_ROWS, s.Ci, s.c * s.c * s.Co, s.c * s.c * s.Co, 1);
       s.out = make_tensor(b, 4, SGD_LAYOUT_NHWC, N, s.Ho, s.Wo, s.Co);
       s.dout = make_tensor(b, 4, SGD_LAYOUT_NHWC, N, s.Ho, s.Wo, s.Co);
       s.split_fwd = gemm_pick_splits((int)P, s.Co, s.ldk);
@@ -354,7 +369,9 @@ int plan(sgd_net* net) {
       partial = std::max(partial, gemm_scratch_floats((int)P, s.Co, s.ldk, false, false, false, s.split_fwd));
       for (bool fused : {false, true})
         partial_dw = std::max(partial_dw, gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw));
-      if (!s.first_weighted) {
+      if (s.implicit_dx) {
+        partial = std::max(partial, gemm_scratch_floats((int)Pin, s.Ci, s.c * s.c * s.Co, false, false, false, 1));
+      } else if (!s.first_weighted) {
         partial = std::max(partial, gemm_scratch_floats((int)P, s.ldk, s.Co, false, true, false, s.split_dx));
         dcol = std::max(dcol, P * s.ldk);
       }
@@ -424,6 +441,24 @@ const float* input_of(const sgd_net* net, const Stage& s, void* ws, const float*
   return s.input < 0 ? X : at<float>(ws, net->stages[s.input].out);
 }
 
+// Gather over a source tensor (NHWC, sh x sw x sc per image) for a product
+// whose gathered index runs over an rh x rw pixel grid.
+ConvGather conv_gather(const float* src, int rh, int rw, int sh, int sw, int sc, int c, int P, bool flip) {
+  ConvGather g{};
+  g.src = src;
+  g.RH = rh;
+  g.RW = rw;
+  g.SH = sh;
+  g.SW = sw;
+  g.SC = sc;
+  g.c = c;
+  g.P = P;
+  g.flip = flip ? 1 : 0;
+  g.inv_RW = 1.f / (float)rw;
+  g.inv_RH = 1.f / (float)rh;
+  return g;
+}
+
 int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y, float* loss, void* ws,
                 hipStream_t st) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
@@ -433,12 +468,20 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
     prof_set_layer(s.spec, 0);
     if (s.kind == SGD_CONV) {
       float* wrep = at<float>(ws, s.wrep);
-      float* col = at<float>(ws, s.col);
       if ((e = repack_weight(Wt + s.w_off, wrep, s.Co, s.Ci, s.c, s.ldk, st))) return e;
-      if ((e = im2col(xin, s.input < 0, col, s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st))) return e;
+      // the dedx operand is repacked from the weights the forward pass uses
+      // (the fused training step updates W during the backward pass)
+      if (s.implicit_dx && (e = repack_weight_dx(Wt + s.w_off, at<float>(ws, s.wdx), s.Co, s.Ci, s.c, st))) return e;
       GemmDesc g{};
-      g.A = col;
-      g.lda = s.ldk;
+      if (s.implicit) {
+        g.gather = 1;
+        g.cv = conv_gather(xin, s.Ho, s.Wo, s.H, s.W, s.Ci, s.c, s.P, false);
+      } else {
+        float* col = at<float>(ws, s.col);
+        if ((e = im2col(xin, s.input < 0, col, s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st))) return e;
+        g.A = col;
+        g.lda = s.ldk;
+      }
       g.B = wrep;
       g.ldb = s.ldk;
       g.C = at<float>(ws, s.out);
@@ -573,14 +616,18 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         continue;
     } else if (s.kind == SGD_CONV) {
       const float* dout = at<float>(ws, s.dout);
-      float* col = at<float>(ws, s.col);
       const int64_t P = (int64_t)s.N * s.Ho * s.Wo;
       GemmDesc g{};  // dedw: dW'[co][kk] = dout^T * col, stored permuted to [co][ci][ky][kx]; dedb via ones
       g.A = dout;
       g.lda = s.Co;
       g.a_t = true;
-      g.B = col;
-      g.ldb = s.ldk;
+      if (s.implicit) {  // Col's rows gathered from the input activation
+        g.gather = 2;
+        g.cv = conv_gather(xin, s.Ho, s.Wo, s.H, s.W, s.Ci, s.c, s.P, false);
+      } else {
+        g.B = at<float>(ws, s.col);
+        g.ldb = s.ldk;
+      }
       g.b_t = true;
       g.C = grad + s.w_off;
       g.ldc = s.K;
@@ -600,7 +647,30 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.gscale = gscale;
       set_update(g, rule, state, s);
       if ((e = fork()) || (e = gemm(g, side))) continue;
-      if (!s.first_weighted) {
+      if (s.implicit_dx) {
+        // dedx_conv as one gather-form product: each input pixel gathers its
+        // c*c taps of dout (flipped offsets) against W''; the ReLU mask of
+        // the conv below is the epilogue
+        const Stage& src = stages[s.input];
+        const bool mask = src.relu && src.kind != SGD_MAXPOOL;
+        GemmDesc d{};
+        d.gather = 1;
+        d.cv = conv_gather(dout, s.H, s.W, s.Ho, s.Wo, s.Co, s.c, s.P, true);
+        d.B = at<float>(ws, s.wdx);
+        d.ldb = (int64_t)s.c * s.c * s.Co;
+        d.C = at<float>(ws, src.dout);
+        d.ldc = s.Ci;
+        d.M = s.N * s.H * s.W;
+        d.N = s.Ci;
+        d.K = s.c * s.c * s.Co;
+        d.epi = mask ? EPI_MASK : EPI_STORE;
+        d.mask = mask ? at<float>(ws, src.out) : nullptr;
+        d.ldm = s.Ci;
+        d.splits = 1;
+        d.partial = partial;
+        d.partial_floats = net->partial_floats;
+        if ((e = gemm(d, st))) continue;
+      } else if (!s.first_weighted) {
         GemmDesc d{};  // dedx_conv: dcol[P][kk] = dout * W' (its own buffer: dedw reads Col meanwhile)
         d.A = dout;
         d.lda = s.Co;
@@ -746,6 +816,12 @@ int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, cons
                      "sgd_compute_gradient_into");
   if (!e) gb->empty = 0;
   return e;
+}
+
+int sgd_set_implicit_conv(sgd_net* net, int enable) {
+  if (!net) return fail(SGD_EINVAL, "sgd_set_implicit_conv: null net");
+  net->implicit = enable != 0;
+  return sgd::plan(net);
 }
 
 int sgd_set_overlap(sgd_net* net, int enable) {

@@ -307,3 +307,58 @@ def test_prescaled_gradient(case):
     bo = [onet.params[i][2] for i in sorted(onet.params)]
     per_tensor_grad_check((np.float32(-eta) * g_np).astype(np.float32), (np.float32(-eta) * g_ref).astype(np.float32),
                           wo, bo, n)
+
+
+# ------------------------------------------------ implicit-GEMM convolution ----
+# Conv layers after the first with Ci % 16 == 0 gather their im2col operand
+# from the activation; those with Co % 16 == 0 compute dedx as one gathered
+# product.  These nets cover odd map sizes (ragged tiles), 3x3 / 5x5 / 1x1
+# filters, pad 0 / 1 / 2, a pool feeding the gathered dedx (no mask) and a
+# ReLU'd conv feeding it (mask in the epilogue).
+IMPLICIT_NET = [("conv", 16, 3, 1), ("relu",), ("conv", 32, 3, 1), ("relu",), ("pool", 2),
+                ("conv", 16, 5, 2), ("relu",), ("conv", 48, 1, 0), ("relu",), ("conv", 32, 3, 0), ("relu",),
+                ("fc", 10), ("softmax_ce",)]
+
+
+def test_implicit_conv_net_matches_oracle():
+    check((3, 10, 10), IMPLICIT_NET, 3, 41, 10)
+
+
+def test_implicit_conv_net_odd_maps():
+    check((3, 9, 7), [("conv", 16, 3, 1), ("relu",), ("conv", 16, 3, 1), ("relu",), ("conv", 32, 3, 0), ("relu",),
+                      ("fc", 7), ("softmax_ce",)], 5, 42, 7, x_dist="normal")
+
+
+def test_implicit_and_explicit_conv_agree():
+    # forward and dedw take the same k order either way (bitwise); dedx is
+    # summed in another order (gradient tolerance)
+    chw, N = (3, 10, 10), 3
+    X = workloads.normal(43, 0, (N,) + chw)
+    y = workloads.labels(43, 1, N, 10)
+    W = workloads.he_normal_params(43, chw, IMPLICIT_NET)
+    dev = torch.device("cuda")
+    out = {}
+    for imp in (True, False):
+        net = S.Net((N,) + chw, IMPLICIT_NET)
+        net.set_implicit_conv(imp)
+        ws = net.workspace()
+        g = torch.empty(W.size, device=dev)
+        loss = torch.empty(1, device=dev)
+        net.compute_gradient(torch.from_numpy(W).to(dev), torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev),
+                             g, loss, ws)
+        torch.cuda.synchronize()
+        outs = [net.view(ws, i, S.T_OUT).cpu().numpy() for i in (0, 2, 5, 7, 9)]
+        out[imp] = (g.cpu().numpy(), loss.item(), outs, net)
+    (ga, la, oa, neta), (gb, lb, ob, netb) = out[True], out[False]
+    assert la == lb
+    for a, b in zip(oa, ob):
+        np.testing.assert_array_equal(a, b)
+    onet = O.OracleNet(chw, IMPLICIT_NET)
+    wo = [onet.params[i][0] for i in sorted(onet.params)]
+    bo = [onet.params[i][2] for i in sorted(onet.params)]
+    # the last conv's dedw reads only forward data: bitwise
+    last = max(i for i, L in enumerate(IMPLICIT_NET) if L[0] == "conv")
+    w0, _, b0, nb = onet.params[last]
+    np.testing.assert_array_equal(ga[w0:b0 + nb], gb[w0:b0 + nb])
+    per_tensor_grad_check(ga, gb.astype(np.float32), wo, bo, W.size)
+    assert neta.workspace_bytes() < netb.workspace_bytes()
