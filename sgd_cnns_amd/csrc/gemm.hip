@@ -934,16 +934,20 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
   }
 }
 
-// Completes the stream-K tiles that were shared between blocks: block
-// (j, y) takes elements [1024 y, 1024 y + 1024) of stream-K tile j (one float4
-// per thread), adds the tile's slots in block (= k) order and stores through
-// finish(), which computes what the gemm_dma epilogue variants compute.
-constexpr int kFixChunk = 1024;
+// Completes the stream-K tiles that were shared between blocks.  Block
+// (j, y) takes 256 / TS float4s of stream-K tile j; the tile's slots (one per
+// block whose range touched the tile, in block = k order) are split into TS
+// contiguous groups, thread group g sums its group in order, and the TS
+// group sums are added in group order -- a fixed two-level order, so the
+// result depends only on the schedule.  Then finish4(), which computes what
+// the gemm_dma epilogue variants compute.
+constexpr int kFixChunk = 1024;  // elements a fixup block covers with one thread per float4
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int G) {
+__global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int G, int TS) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   __shared__ int slots[1024];
+  __shared__ float4 part_sum[kThreads];
   const int j = blockIdx.x;
   const int S = s.sk_iters;
   const int x0 = j * s.ipt;
@@ -959,14 +963,15 @@ __global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int
   const int tiles_m = p.tiles / p.tiles_n;
   const int tn_i = t / tiles_m, tm_i = t - tn_i * tiles_m;
   const int m0 = tm_i * BM, n0 = tn_i * BN;
-  // Each thread adds one float4 (4 rows of one column) over the slots, with
-  // several slots' loads in flight.
-  const int idx = blockIdx.y * kFixChunk + 4 * threadIdx.x;
+  const int grp = threadIdx.x % TS, v4 = threadIdx.x / TS;
+  const int idx = (blockIdx.y * (kThreads / TS) + v4) * 4;  // the float4's first element in the slot
   const float4* src = reinterpret_cast<const float4*>(s.part + idx);
   constexpr int64_t kSlot4 = BM * BN / 4;
-  float4 v = src[(int64_t)slots[0] * kSlot4];
-  int i = 1;
-  for (; i + 4 <= n; i += 4) {
+  const int i0 = grp * n / TS, i1 = (grp + 1) * n / TS;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  int i = i0;
+  if (i < i1) v = src[(int64_t)slots[i++] * kSlot4];
+  for (; i + 4 <= i1; i += 4) {
     float4 u[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) u[k] = src[(int64_t)slots[i + k] * kSlot4];
@@ -978,12 +983,24 @@ __global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int
       v.w += u[k].w;
     }
   }
-  for (; i < n; ++i) {
+  for (; i < i1; ++i) {
     const float4 u = src[(int64_t)slots[i] * kSlot4];
     v.x += u.x;
     v.y += u.y;
     v.z += u.z;
     v.w += u.w;
+  }
+  if (TS > 1) {
+    part_sum[threadIdx.x] = v;
+    __syncthreads();
+    if (grp != 0) return;
+    for (int g = 1; g < TS; ++g) {
+      const float4 u = part_sum[threadIdx.x + g];
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
   }
   // Inverse of slot_index: float4 (wave, a, c, q) of lane l holds rows
   // 8q .. 8q+3 (plus 4 * lane half) of column l % 32 of block (a, c).
@@ -1077,7 +1094,7 @@ StagedKernel staged_fn(int cfg, int form, int em) {
 }
 
 typedef void (*DmaKernel)(KArgs, SkArgs);
-typedef void (*FixKernel)(KArgs, SkArgs, int);
+typedef void (*FixKernel)(KArgs, SkArgs, int, int);
 
 // gemm_dma / gemm_sk_fixup instances for a configuration, operand form
 // (0: A*B^T, 1: A^T*B, 2: A*B, 3: A^T*B^T) and epilogue variant; the
@@ -1145,7 +1162,7 @@ int epi_mode(const GemmDesc& d, int form) {
   }
   if (extra) return EM_GENERIC;
   if (form == 0 && (d.epi == EPI_BIAS || d.epi == EPI_BIAS_RELU)) return EM_BIAS;
-  if (form == 2 && d.epi == EPI_MASK) return EM_MASK;
+  if ((form == 2 || (form == 0 && d.gather == 1)) && d.epi == EPI_MASK) return EM_MASK;
   if (d.epi == EPI_STORE && form != 3) return EM_STORE;
   return EM_GENERIC;
 }
@@ -1447,19 +1464,24 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     prof_end(s);
     if (int e = check_launch("gemm")) return e;
     if (plan.sk_iters > 0) {
-      // Partial tiles written and read back by the fixup (for the profile).
-      int64_t shared = 0, slots = 0;
+      // Partial tiles written and read back by the fixup (for the profile),
+      // and the most slots a tile has.
+      int64_t shared = 0, slots = 0, most = 1;
       for (int64_t j = 0; j < T - plan.dp; ++j) {
         const int blo = sk_block_of((int)(j * ipt), sk.sk_iters, plan.grid);
         const int bhi = sk_block_of((int)(j * ipt + ipt - 1), sk.sk_iters, plan.grid);
         if (blo != bhi) {
           ++shared;
           slots += bhi - blo + 1;
+          most = std::max<int64_t>(most, bhi - blo + 1);
         }
       }
+      // Threads per float4: about 8 slots each, a power of two up to 16.
+      int ts = 1;
+      while (ts < 16 && most > 8 * ts) ts *= 2;
       prof_begin("gemm_sk_fixup", (double)(slots - shared) * tile, 4.0 * (double)(slots + shared) * tile, s);
-      hipLaunchKernelGGL(f.fix, dim3((unsigned)(T - plan.dp), (unsigned)(tile / kFixChunk)), dim3(kThreads), 0, s, a, sk,
-                         plan.grid);
+      hipLaunchKernelGGL(f.fix, dim3((unsigned)(T - plan.dp), (unsigned)(tile * ts / kFixChunk)), dim3(kThreads), 0,
+                         s, a, sk, plan.grid, ts);
       prof_end(s);
       if (int e = check_launch("gemm_sk_fixup")) return e;
     }
