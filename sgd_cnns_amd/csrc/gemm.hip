@@ -1022,14 +1022,32 @@ __global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int
 // Sum split-K partial tiles in slice order, then store: the ones column to
 // ones_out, the conv weight gradient permuted, anything else through the
 // epilogue.
-__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, KArgs p) {
+// With TS > 1, TS threads share an element: each sums a contiguous group of
+// slices and the group sums are added in group order (a fixed two-level
+// order for products split many ways).
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, KArgs p, int TS) {
+  __shared__ float gsum[256];
   const int64_t MN = (int64_t)p.M * p.Nt;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < MN;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    float v = part[idx];
-    for (int s = 1; s < splits; ++s) v += part[(int64_t)s * MN + idx];
-    const int row = (int)(idx / p.Nt), col = (int)(idx - (int64_t)row * p.Nt);
-    finish(v, row, col, p);
+  const int grp = threadIdx.x % TS, per_block = blockDim.x / TS;
+  const int s0 = grp * splits / TS, s1 = (grp + 1) * splits / TS;
+  for (int64_t base = (int64_t)blockIdx.x * per_block; base < MN; base += (int64_t)gridDim.x * per_block) {
+    const int64_t idx = base + threadIdx.x / TS;
+    float v = 0.f;
+    if (idx < MN) {
+      v = part[(int64_t)s0 * MN + idx];
+      for (int s = s0 + 1; s < s1; ++s) v += part[(int64_t)s * MN + idx];
+    }
+    if (TS > 1) {
+      __syncthreads();  // the previous round's group sums were read
+      gsum[threadIdx.x] = v;
+      __syncthreads();
+      if (grp == 0)
+        for (int g = 1; g < TS; ++g) v += gsum[threadIdx.x + g];
+    }
+    if (grp == 0 && idx < MN) {
+      const int row = (int)(idx / p.Nt), col = (int)(idx - (int64_t)row * p.Nt);
+      finish(v, row, col, p);
+    }
   }
 }
 
@@ -1253,6 +1271,19 @@ SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, in
         best_cost = cost;
         best = {(int)g, (int)dp, S};
       }
+    }
+  }
+  // Products with fewer k-slices than CUs: a few slices per block, one block
+  // per CU.
+  const int64_t S = T * I;
+  for (int64_t per = 2; per <= 16; per *= 2) {
+    const int64_t g = S / per;
+    if (g < 2 || g >= m.cus || 2 * g * tile_floats > cap_floats) continue;
+    const double fix = 4.0 * tile_floats * (double)(2 * T + g) / 4e12 / unit_s + 1.0;
+    const double cost = ((double)S / g + (std::ceil((double)S / g / I) + 1.0) * kItemCost) * slice_time(1) + fix;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = {(int)g, 0, S};
     }
   }
   return best;
@@ -1508,9 +1539,11 @@ int gemm(const GemmDesc& d, hipStream_t s) {
     r.C = d.C;
     r.ldc = d.ldc;
     const int64_t mn = (int64_t)d.M * a.Nt;
-    const int blocks = (int)std::min<int64_t>(ceil_div(mn, 256), 8192);
+    int ts = 1;  // threads per element: about 8 slices each, a power of two up to 16
+    while (ts < 16 && splits > 8 * ts) ts *= 2;
+    const int blocks = (int)std::min<int64_t>(ceil_div(mn * ts, 256), 8192);
     prof_begin("splitk_reduce", (double)(splits - 1) * mn, 4.0 * (double)(splits + 1) * mn, s);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, d.partial, splits, r);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, d.partial, splits, r, ts);
     prof_end(s);
     if (int e = check_launch("splitk_reduce")) return e;
   }
