@@ -155,7 +155,7 @@ def gpu_step_bench(wl, steps, warmup):
 
 def kernel_totals(recs):
     kern = {}
-    for (name, layer, phase, ms, flops, nbytes) in recs:
+    for (name, layer, phase, ms, flops, nbytes, _shape) in recs:
         k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
         k["launches"] += 1
         k["ms"] += ms
@@ -266,6 +266,200 @@ def cpu_baseline(wl, sample):
                        f"full batch, plus one accumulate+apply over all {W.size} parameters ({t_upd:.2f} s)")}
 
 
+def timing_model_report(out_path, raw_prefix=None, reps=3):
+    """Refit the SPRINT report's timing model (section 3.3, eqs. 4-6) to these kernels and check its
+    step predictions: eq. 6 on a power-of-two grid of sgd_gemm launches for each kernel family and
+    form, validated off the grid (section 4.1, Fig. 6); the CUDA kernels' linear models (eq. 5,
+    Fig. 5) from each workload's explicit-im2col gradient step at a quarter and a half of its batch;
+    eq. 4 at the full batch."""
+    import numpy as np
+    import torch
+
+    import sgd_cnns_amd as S
+    import workloads
+    from sgd_cnns_amd import timing_model as TM
+
+    def say(msg):
+        print(f"[timing-model] {msg}", file=sys.stderr, flush=True)
+
+    t_start = time.perf_counter()
+    forms = ("nt", "tn", "nn")
+    grid = TM.grid_points()
+    say(f"grid: {len(grid)} shapes x {len(forms)} forms x 2 kernel families")
+    g = {"dma": TM.gemm_grid({f: grid for f in forms}, progress=say),
+         "staged": TM.gemm_grid({f: [TM.staged_shape(f, *p) for p in grid] for f in forms}, progress=say)}
+    alphas = {fam: {} for fam in g}
+    fit_err = {fam: {} for fam in g}
+    for fam in g:
+        for f in forms:
+            m, n, k, t = g[fam][f].T
+            alphas[fam][f] = TM.fit_eq6(m, n, k, t)
+            fit_err[fam][f] = TM.rel_errors(TM.eq6(alphas[fam][f], m, n, k), t)
+    off = TM.offgrid_points(400, seed=6)
+    say(f"off-grid validation: {len(off)} shapes")
+    go = TM.gemm_grid({f: off for f in forms}, progress=say)
+    off_err, off_err_big, off_fam = {}, {}, {}
+    for f in forms:
+        m, n, k, t = go[f].T
+        fams = [TM.family_for(f, int(a), int(b), int(c)) for a, b, c in zip(m, n, k)]
+        pred = np.array([float(TM.eq6(alphas[fam][f], a, b, c)) for fam, a, b, c in zip(fams, m, n, k)])
+        e = TM.rel_errors(pred, t)
+        off_err[f] = e
+        off_err_big[f] = e[m * n * k >= 2.0 ** 27]
+        off_fam[f] = sum(1 for x in fams if x == "dma")
+
+    def step_records(wl, batch):
+        w = wl.with_batch(batch)
+        X, y, W = workloads.make_inputs(w)
+        net = S.Net((batch,) + tuple(w.chw), w.layers)
+        net.set_implicit_conv(False)
+        net.set_overlap(False)
+        dev = torch.device("cuda")
+        Wd, Xd, yd = (torch.from_numpy(a).to(dev) for a in (W, X, y))
+        grad = torch.empty(net.param_count(), device=dev)
+        loss = torch.empty(1, device=dev)
+        ws = net.workspace(dev)
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # as the step runs normally: launched back to back, host launch gaps included
+        e0.record(stream)
+        for _ in range(reps):
+            net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = e0.elapsed_time(e1) / reps
+        # profiled, each step queued behind a 2 ms device sleep so the GPU runs it without waiting
+        # for the host: the kernels' event times are their device times, as on the grid
+        steps, dev_ms = [], 0.0
+        for _ in range(reps):
+            net.profile(True)
+            torch.cuda._sleep(5_000_000)
+            e0.record(stream)
+            net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            net.profile(False)
+            steps.append(net.profile_read())
+            dev_ms += e0.elapsed_time(e1)
+        del ws
+        torch.cuda.empty_cache()
+        return steps, wall, dev_ms / reps
+
+    names = ["lenet5", "mlp5000", "vgg_cifar", "vgg16"]
+    fit_recs = []
+    raw_steps = {}
+    for name in names:
+        wl = workloads.WORKLOADS[name]
+        for b in (max(1, wl.batch // 4), max(1, wl.batch // 2)):
+            say(f"{name} batch {b} (CUDA-kernel fit)")
+            steps, _, _ = step_records(wl, b)
+            raw_steps[f"{name}_{b}"] = steps
+            for rec in steps:
+                fit_recs.extend(rec)
+    kmodels = TM.fit_kernel_models(fit_recs)
+    preds = {}
+    for name in names:
+        wl = workloads.WORKLOADS[name]
+        say(f"{name} batch {wl.batch} (eq. 4 prediction)")
+        steps, wall, dev_ms = step_records(wl, wl.batch)
+        raw_steps[f"{name}_{wl.batch}"] = steps
+        per = [TM.predict_step(rec, alphas, kmodels) for rec in steps]
+        avg = {key: float(np.mean([p[key] for p in per])) for key in
+               ("sgemm_pred", "sgemm_meas", "cuda_pred", "cuda_meas", "pred", "meas")}
+        avg["wall"], avg["device"] = wall, dev_ms
+        avg["products"] = per[0]["products"]
+        preds[name] = avg
+    if raw_prefix:
+        np.savez(raw_prefix + "_grid.npz", **{f"{fam}_{f}": g[fam][f] for fam in g for f in forms},
+                 **{f"off_{f}": go[f] for f in forms})
+        with open(raw_prefix + "_steps.json", "w") as fh:
+            json.dump(raw_steps, fh)
+
+    L = []
+    L.append("# SPRINT timing model (eqs. 4-6) refitted on MI355X")
+    L.append("")
+    L.append("Command (from the repository root): `python bench.py --timing-model profiles/timing_model_fit.md`")
+    L.append("")
+    L.append(f"Run time {time.perf_counter() - t_start:.0f} s.  Times are event-bracketed launches, fp32: the "
+             "median of 5 per grid shape, queued ahead of the GPU; steps averaged over "
+             f"{reps} profiled gradient steps (sgd_compute_gradient with im2col explicit, the page's method, "
+             "and the dedw products on the caller's stream), each queued ahead the same way.")
+    L.append("")
+    L.append(f"## Eq. 6 fit: {len(grid)} shapes (m, n, k) = (2^x, 2^y, 2^z), 3 <= x, y, z <= 22, "
+             "x+y+z <= 38, every operand <= 2^29 elements; least squares on relative error")
+    L.append("")
+    L.append("The staged family is timed on the same grid with k + 2 (nt, nn) or m + 2 (tn), which the "
+             "direct-load kernels cannot take.")
+    L.append("")
+    L.append("| family | form | " + " | ".join(f"alpha_{t}" if t != "1" else "beta (ms)" for t in TM.EQ6_TERMS)
+             + " | asymptotic TFLOP/s | on-grid median abs. rel. error | p90 |")
+    L.append("|---|---|" + "---|" * (len(TM.EQ6_TERMS) + 3))
+    for fam in g:
+        for f in forms:
+            a = alphas[fam][f]
+            e = TM.summarize_errors(fit_err[fam][f])
+            L.append(f"| {fam} | {f} | " + " | ".join(f"{v:.4g}" for v in a) +
+                     f" | {2 / a[0] / 1e9:.1f} | {e['median']:.1%} | {e['p90']:.1%} |")
+    L.append("")
+    L.append("alpha_mnk is ms per multiply-add, so 2 / alpha_mnk / 1e9 is the fitted asymptotic TFLOP/s.")
+    L.append("")
+    L.append(f"## Off-grid check (Fig. 6's method): {len(off)} seeded grid shapes moved to 2^(x + 1/4), "
+             "each predicted with the family the library picks for it")
+    L.append("")
+    L.append("| form | direct-load / staged | median abs. rel. error | p90 | max | mnk >= 2^27: median | p90 | n |")
+    L.append("|---|---|---|---|---|---|---|---|")
+    for f in forms:
+        b, c = TM.summarize_errors(off_err[f]), TM.summarize_errors(off_err_big[f])
+        L.append(f"| {f} | {off_fam[f]} / {len(off) - off_fam[f]} | {b['median']:.1%} | {b['p90']:.1%} | "
+                 f"{b['max']:.1%} | {c['median']:.1%} | {c['p90']:.1%} | {c['n']} |")
+    L.append("")
+    L.append("## CUDA-kernel models: time = alpha * algorithmic bytes + beta (eq. 5's form; im2col's bytes are "
+             "its column matrix plus its input)")
+    L.append("")
+    L.append("Fitted on the explicit-im2col gradient steps of all four workloads at a quarter and a half of "
+             "their batch.")
+    L.append("")
+    L.append("| kernel | 1/alpha (GB/s) | beta (us) |")
+    L.append("|---|---|---|")
+    for kname in sorted(kmodels):
+        a, b = kmodels[kname]
+        L.append(f"| {kname} | {'-' if a <= 0 else f'{1e-6 / a:.0f}'} | {1e3 * b:.2f} |")
+    L.append("")
+    L.append("## Eq. 4: predicted vs measured gradient step at the full batch (ms per step)")
+    L.append("")
+    L.append("'device' is the profiled step queued ahead of the GPU; 'wall' the same step launched back to back "
+             "as in training, host launch gaps included.")
+    L.append("")
+    L.append("| workload | batch | SGEMM pred | SGEMM meas | CUDA pred | CUDA meas | eq. 4 pred | sum of kernels "
+             "| error | device | error | wall | error |")
+    L.append("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for name in names:
+        p = preds[name]
+        L.append(f"| {name} | {workloads.WORKLOADS[name].batch} | {p['sgemm_pred']:.3f} | {p['sgemm_meas']:.3f} | "
+                 f"{p['cuda_pred']:.3f} | {p['cuda_meas']:.3f} | {p['pred']:.3f} | {p['meas']:.3f} | "
+                 f"{(p['pred'] - p['meas']) / p['meas']:+.1%} | {p['device']:.3f} | "
+                 f"{(p['pred'] - p['device']) / p['device']:+.1%} | {p['wall']:.3f} | "
+                 f"{(p['pred'] - p['wall']) / p['wall']:+.1%} |")
+    L.append("")
+    L.append("## Largest products of each step: eq. 6 vs measured (ms)")
+    for name in names:
+        rows = sorted(preds[name]["products"], key=lambda r: -r[6])[:6]
+        L.append("")
+        L.append(f"{name}:")
+        L.append("")
+        L.append("| family | form | m | n | k | eq. 6 | measured | error |")
+        L.append("|---|---|---|---|---|---|---|---|")
+        for (fam, f, m, n, k, pr, me) in rows:
+            L.append(f"| {fam} | {f} | {m} | {n} | {k} | {pr:.4f} | {me:.4f} | {(pr - me) / me:+.1%} |")
+    text = "\n".join(L) + "\n"
+    with open(out_path, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
 def main():
     import numpy as np
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -278,6 +472,10 @@ def main():
     ap.add_argument("--no-ps-apply", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter scaling)")
+    ap.add_argument("--timing-model", metavar="OUT_MD", default=None,
+                    help="refit the SPRINT timing model (eqs. 4-6) and write its report instead of the step bench")
+    ap.add_argument("--timing-model-raw", metavar="PREFIX", default=None,
+                    help="also save the timing model's raw grid times and step records under this prefix")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -285,6 +483,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.timing_model:
+        timing_model_report(args.timing_model, args.timing_model_raw)
+        return
     import workloads
     wl = workloads.WORKLOADS[args.workload]
     if args.copy_calibration_mib:

@@ -247,6 +247,36 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
                     const sgd_rule* rule, void* stream);
 
 /*
+ * One fp32 matrix product on the library's matrix-core kernels, the SGEMM of
+ * the SPRINT report's section 3.3 table: C[m][n] = op(A) * op(B), row-major
+ * C with row stride ldc.
+ *   a_t == 0: A stored [m][k] (row stride lda); a_t == 1: A stored [k][m].
+ *   b_t == 0: B stored [n][k] (row stride ldb), i.e. C = A * B^T (the
+ *             forward form of conv and fc); b_t == 1: B stored [k][n].
+ * Results are deterministic (fixed summation order for a given shape and
+ * GPU).  `ws` is device scratch of sgd_gemm_workspace_bytes() bytes (may be
+ * NULL when that is 0), 256-byte aligned.  All pointers are device memory
+ * owned by the caller; the call is asynchronous on `stream`.  It serves the
+ * timing model of the SPRINT report's section 3.3 (eq. 6 is fitted over such
+ * calls) and any caller that wants one product.  Errors: SGD_EINVAL (null
+ * pointer, sizes < 1, strides shorter than a row, 2^22 or more 64 x 64
+ * output tiles), SGD_EWORKSPACE, SGD_EDEVICE.  sgd_gemm_workspace_bytes
+ * returns 0 for invalid arguments.
+ */
+typedef struct sgd_gemm_args {
+  int m, n, k;
+  int a_t, b_t;
+  const float* A;
+  int64_t lda;
+  const float* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+} sgd_gemm_args;
+size_t sgd_gemm_workspace_bytes(const sgd_gemm_args* g);
+int sgd_gemm(const sgd_gemm_args* g, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Implicit-GEMM convolution (on by default).  A conv layer whose input is
  * an activation of this network with Ci % 16 == 0 gathers the im2col
  * operand of its forward and dedw products straight from that activation
@@ -293,6 +323,10 @@ typedef struct sgd_kernel_time {
   double ms;          /* event-measured duration of the launch              */
   double flops;       /* algorithmic floating-point operations              */
   double bytes;       /* algorithmic HBM bytes                              */
+  int m, n, k;        /* the product's shape for GEMM launches (and their
+                         fixup / split-reduce passes), else 0               */
+  int product;        /* index of that product within the recording (all of
+                         its launches share it), -1 for other kernels      */
 } sgd_kernel_time;
 
 int sgd_profile(sgd_net* net, int enable);

@@ -33,7 +33,7 @@ LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
-           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_profile", "sgd_profile_read",
+           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
            "sgd_last_error"]
 
 
@@ -49,13 +49,20 @@ class SgdGradBuf(C.Structure):
     _fields_ = [("data", C.c_void_p), ("n", C.c_int64), ("empty", C.c_int)]
 
 
+class SgdGemmArgs(C.Structure):
+    _fields_ = [("m", C.c_int), ("n", C.c_int), ("k", C.c_int), ("a_t", C.c_int), ("b_t", C.c_int),
+                ("A", C.c_void_p), ("lda", C.c_int64), ("B", C.c_void_p), ("ldb", C.c_int64),
+                ("C", C.c_void_p), ("ldc", C.c_int64)]
+
+
 class SgdRule(C.Structure):
     _fields_ = [("rule", C.c_int), ("eta", C.c_float), ("mu", C.c_float), ("eps", C.c_float), ("decay", C.c_float)]
 
 
 class SgdKernelTime(C.Structure):
     _fields_ = [("kernel", C.c_char_p), ("layer", C.c_int), ("phase", C.c_int), ("ms", C.c_double),
-                ("flops", C.c_double), ("bytes", C.c_double)]
+                ("flops", C.c_double), ("bytes", C.c_double), ("m", C.c_int), ("n", C.c_int), ("k", C.c_int),
+                ("product", C.c_int)]
 
 
 class SgdError(RuntimeError):
@@ -93,6 +100,8 @@ def lib():
             "sgd_profile": (i, [P, i]),
             "sgd_set_overlap": (i, [P, i]),
             "sgd_set_implicit_conv": (i, [P, i]),
+            "sgd_gemm_workspace_bytes": (sz, [C.POINTER(SgdGemmArgs)]),
+            "sgd_gemm": (i, [C.POINTER(SgdGemmArgs), P, sz, P]),
             "sgd_profile_read": (i, [P, C.POINTER(SgdKernelTime), i]),
             "sgd_last_error": (C.c_char_p, []),
         }
@@ -110,13 +119,19 @@ def _check(rc):
     return rc
 
 
-def _require_cuda(*tensors):
+def _require_cuda(*tensors, rows=False):
+    """Device tensors, contiguous (rows=True: 2-D with unit column stride, any row stride)."""
     import torch
     if not torch.cuda.is_available():
         raise RuntimeError("sgd_cnns_amd compute calls need a ROCm GPU (no CPU fallback)")
     for t in tensors:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("tensors must be contiguous device tensors")
+        if t is None:
+            continue
+        if rows and t.dim() == 2 and t.is_cuda and t.stride(1) == 1:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors" + (" (matrices: unit column stride)"
+                                                                            if rows else ""))
 
 
 def _stream(stream):
@@ -222,7 +237,9 @@ class Net:
         _check(lib().sgd_profile(self._h, 1 if enable else 0))
 
     def profile_read(self):
-        """[(kernel, layer, phase, ms, flops, bytes)] for every recorded launch."""
+        """[(kernel, layer, phase, ms, flops, bytes, (m, n, k, product))] for every recorded launch.
+
+        The last field is (0, 0, 0, -1) for launches outside a matrix product."""
         n = lib().sgd_profile_read(self._h, None, 0)
         if n < 0:
             _check(n)
@@ -230,7 +247,7 @@ class Net:
         m = lib().sgd_profile_read(self._h, arr, n)
         if m < 0:
             _check(m)
-        return [(r.kernel.decode(), r.layer, r.phase, r.ms, r.flops, r.bytes) for r in arr[:n]]
+        return [(r.kernel.decode(), r.layer, r.phase, r.ms, r.flops, r.bytes, (r.m, r.n, r.k, r.product)) for r in arr[:n]]
 
     def compute_gradient(self, W, X, y, grad, loss, ws, stream=None):
         _require_cuda(W, X, y, grad, loss, ws)
@@ -274,6 +291,32 @@ class GradBuf:
     @empty.setter
     def empty(self, v):
         self._c.empty = 1 if v else 0
+
+
+def _gemm_args(A, B, C_, a_t, b_t):
+    m, n = C_.shape
+    k = A.shape[0] if a_t else A.shape[1]
+    if (A.shape[1] if a_t else A.shape[0]) != m or (B.shape[1] if b_t else B.shape[0]) != n or \
+            (B.shape[0] if b_t else B.shape[1]) != k:
+        raise ValueError(f"gemm: op(A) {tuple(A.shape)} (a_t={a_t}), op(B) {tuple(B.shape)} (b_t={b_t}) "
+                         f"and C {tuple(C_.shape)} do not form a product")
+    return SgdGemmArgs(m, n, k, int(a_t), int(b_t), A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0),
+                       C_.data_ptr(), C_.stride(0))
+
+
+def gemm_workspace_bytes(m, n, k, a_t=False, b_t=False):
+    """Scratch bytes sgd_gemm needs for an m x n x k product."""
+    g = SgdGemmArgs(m, n, k, int(a_t), int(b_t), None, k if not a_t else m, None, k if not b_t else n, None, n)
+    return lib().sgd_gemm_workspace_bytes(C.byref(g))
+
+
+def gemm(A, B, C_, a_t=False, b_t=False, ws=None, stream=None):
+    """C = op(A) op(B) on the GPU: A is [m][k] (a_t: [k][m]); B is [n][k] (b_t: [k][n])."""
+    _require_cuda(A, B, C_, rows=True)
+    _require_cuda(ws)
+    g = _gemm_args(A, B, C_, a_t, b_t)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().sgd_gemm(C.byref(g), _ptr(ws), nbytes, _stream(stream)))
 
 
 def accumulate_grad(gb, grad, stream=None):

@@ -24,6 +24,8 @@ int check_launch(const char* what);
 void prof_begin(const char* kernel, double flops, double bytes, hipStream_t s);
 void prof_end(hipStream_t s);
 void prof_set_layer(int layer, int phase);
+// The m x n x k of the product whose kernels are launched next (0 after it).
+void prof_set_shape(int m, int n, int k);
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

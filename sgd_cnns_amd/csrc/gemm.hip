@@ -1371,8 +1371,17 @@ int64_t gemm_scratch_floats(int M, int Nt, int K, bool a_t, bool b_t, bool fused
   return std::max(staged, sk);
 }
 
+int gemm_launch(const GemmDesc& d, hipStream_t s);
+
 int gemm(const GemmDesc& d, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return 0;
+  prof_set_shape(d.M, d.N + (d.ones_out ? 1 : 0), d.K);  // the ones column is computed too
+  const int e = gemm_launch(d, s);
+  prof_set_shape(0, 0, 0);
+  return e;
+}
+
+int gemm_launch(const GemmDesc& d, hipStream_t s) {
   const bool ones = d.ones_out != nullptr;
   KArgs a{};
   a.A = d.A;

@@ -41,6 +41,7 @@ struct ProfRec {
   int layer, phase;
   double flops, bytes;
   hipEvent_t beg, end;
+  int m, n, k, product;
 };
 
 struct Profiler {
@@ -49,6 +50,9 @@ struct Profiler {
   std::vector<hipEvent_t> pool;  // events reused across recordings
   size_t used = 0;
   int layer = -1, phase = 0;
+  int m = 0, n = 0, k = 0;  // shape of the product being launched (0: none)
+  int product = -1;         // its index among this recording's products
+  int products = 0;
   hipEvent_t get() {
     if (used == pool.size()) {
       hipEvent_t e = nullptr;
@@ -108,9 +112,19 @@ void prof_set_layer(int layer, int phase) {
   }
 }
 
+void prof_set_shape(int m, int n, int k) {
+  if (g_prof) {
+    g_prof->m = m;
+    g_prof->n = n;
+    g_prof->k = k;
+    g_prof->product = m > 0 ? g_prof->products++ : -1;
+  }
+}
+
 void prof_begin(const char* kernel, double flops, double bytes, hipStream_t s) {
   if (!g_prof || !g_prof->on) return;
-  ProfRec r{kernel, g_prof->layer, g_prof->phase, flops, bytes, g_prof->get(), g_prof->get()};
+  ProfRec r{kernel, g_prof->layer, g_prof->phase, flops, bytes, g_prof->get(), g_prof->get(),
+            g_prof->m, g_prof->n, g_prof->k, g_prof->product};
   if (!r.beg || !r.end) return;
   (void)hipEventRecord(r.beg, s);
   g_prof->recs.push_back(r);
@@ -818,6 +832,49 @@ int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, cons
   return e;
 }
 
+static int gemm_args_ok(const sgd_gemm_args* g) {
+  if (!g) return fail(SGD_EINVAL, "sgd_gemm: null arguments");
+  if (g->m < 1 || g->n < 1 || g->k < 1) return fail(SGD_EINVAL, "sgd_gemm: sizes must be positive");
+  // Launch grids count output tiles (64 x 64 and larger) in 32-bit fields.
+  if (((int64_t)g->m + 63) / 64 * (((int64_t)g->n + 63) / 64) >= ((int64_t)1 << 22))
+    return fail(SGD_EINVAL, "sgd_gemm: more than 2^22 output tiles");
+  const int64_t a_row = g->a_t ? g->m : g->k, b_row = g->b_t ? g->n : g->k;
+  if (g->lda < a_row || g->ldb < b_row || g->ldc < g->n) return fail(SGD_EINVAL, "sgd_gemm: stride shorter than a row");
+  return SGD_OK;
+}
+
+size_t sgd_gemm_workspace_bytes(const sgd_gemm_args* g) {
+  if (gemm_args_ok(g)) return 0;
+  const int splits = sgd::gemm_pick_splits(g->m, g->n, g->k);
+  return (size_t)(4 * sgd::gemm_scratch_floats(g->m, g->n, g->k, g->a_t != 0, g->b_t != 0, false, splits));
+}
+
+int sgd_gemm(const sgd_gemm_args* g, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = gemm_args_ok(g)) return e;
+  if (!g->A || !g->B || !g->C) return fail(SGD_EINVAL, "sgd_gemm: null matrix");
+  const size_t need = sgd_gemm_workspace_bytes(g);
+  if (ws_bytes < need || (need && !ws)) return fail(SGD_EWORKSPACE, "sgd_gemm: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SGD_EINVAL, "sgd_gemm: workspace not 256-byte aligned");
+  sgd::GemmDesc d{};
+  d.A = g->A;
+  d.lda = g->lda;
+  d.a_t = g->a_t != 0;
+  d.B = g->B;
+  d.ldb = g->ldb;
+  d.b_t = g->b_t != 0;
+  d.C = g->C;
+  d.ldc = g->ldc;
+  d.M = g->m;
+  d.N = g->n;
+  d.K = g->k;
+  d.epi = sgd::EPI_STORE;
+  d.splits = sgd::gemm_pick_splits(g->m, g->n, g->k);
+  d.partial = static_cast<float*>(ws);
+  d.partial_floats = (int64_t)(ws_bytes / 4);
+  (void)hipGetLastError();
+  return sgd::gemm(d, static_cast<hipStream_t>(stream));
+}
+
 int sgd_set_implicit_conv(sgd_net* net, int enable) {
   if (!net) return fail(SGD_EINVAL, "sgd_set_implicit_conv: null net");
   net->implicit = enable != 0;
@@ -835,6 +892,7 @@ int sgd_profile(sgd_net* net, int enable) {
   if (enable) {
     net->prof.recs.clear();
     net->prof.used = 0;
+    net->prof.products = 0;
   }
   net->prof.on = enable != 0;
   return SGD_OK;
@@ -854,6 +912,10 @@ int sgd_profile_read(sgd_net* net, sgd_kernel_time* out, int max_records) {
     out[i].ms = ms;
     out[i].flops = r.flops;
     out[i].bytes = r.bytes;
+    out[i].m = r.m;
+    out[i].n = r.n;
+    out[i].k = r.k;
+    out[i].product = r.product;
   }
   return n;
 }

@@ -1,0 +1,125 @@
+"""GPU parity of the standalone product sgd_gemm, and of the product shapes the step profiler records.
+
+sgd_gemm is the SGEMM of the SPRINT report's section 3.3 table (C = op(A)
+op(B)); the timing model of that section (eq. 6) is fitted over its
+launches.  The reference is the oracle's fc product in fp64 (z = a w^T, the
+definition written as loops), with op(A) and op(B) transposed on the host.
+The bound is the classical one for a dot product of k terms rounded in
+fp32 in any order: |C - ref| <= gamma_k (|op(A)| |op(B)|), gamma_k =
+k u / (1 - k u), u = 2^-24.  Shapes cover the direct-load kernels (aligned
+rows), the staged kernels (ragged rows), stream-K schedules with many
+k-slices, padded strides and tiny products; the padding columns of C must
+be left untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sgd_cnns_amd as S  # noqa: E402
+from sgd_cnns_amd import timing_model as TM  # noqa: E402
+
+U = 2.0 ** -24
+# (m, n, k, row padding of the stored operands in floats)
+SHAPES = [(77, 130, 1000, 0), (256, 192, 4096, 0), (128, 128, 30000, 0), (1000, 36, 4, 0), (5, 3, 7, 0),
+          (300, 516, 260, 12), (513, 257, 1031, 3), (4096, 64, 576, 0)]
+
+
+def stored(seed, tid, rows, cols, pad):
+    """A [rows][cols + pad] host array with U[-1, 1) values in the first cols columns."""
+    a = np.zeros((rows, cols + pad), np.float32)
+    a[:, :cols] = 2.0 * workloads.uniform01(seed, tid, (rows, cols)) - 1.0
+    return a
+
+
+def on_device(a, cols):
+    t = torch.from_numpy(a).to("cuda")
+    return t[:, :cols]
+
+
+@pytest.mark.parametrize("form", ["nt", "tn", "nn", "tt"])
+@pytest.mark.parametrize("m,n,k,pad", SHAPES)
+def test_gemm_matches_oracle(form, m, n, k, pad):
+    a_t, b_t = TM.FORMS[form]
+    print(f"[gemm] form={form} m={m} n={n} k={k} pad={pad}", flush=True)
+    seed = 40 + m % 7
+    A = stored(seed, 0, k, m, pad) if a_t else stored(seed, 0, m, k, pad)
+    B = stored(seed, 1, k, n, pad) if b_t else stored(seed, 1, n, k, pad)
+    opA = (A[:, :m].T if a_t else A[:, :k]).astype(np.float64)     # m x k
+    opBt = (B[:, :n].T if b_t else B[:, :k]).astype(np.float64)    # n x k
+    ref = O.fc_fwd(opA, opBt, np.zeros(n), dtype=np.float64)
+    bound = k * U / (1 - k * U) * O.fc_fwd(np.abs(opA), np.abs(opBt), np.zeros(n), dtype=np.float64)
+
+    Ad = on_device(A, m if a_t else k)
+    Bd = on_device(B, n if b_t else k)
+    padc = 5
+    Cfull = torch.full((m, n + padc), float("nan"), device="cuda")
+    Cd = Cfull[:, :n]
+    nbytes = S.gemm_workspace_bytes(m, n, k, a_t, b_t)
+    ws = torch.empty(max(nbytes, 4) // 4, device="cuda")
+    S.gemm(Ad, Bd, Cd, a_t, b_t, ws)
+    torch.cuda.synchronize()
+    got = Cfull.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(got[:, n:])), "padding columns of C were written"
+    err = np.abs(got[:, :n] - ref)
+    assert np.all(np.isfinite(got[:, :n]))
+    worst = float((err / np.maximum(bound, 1e-300)).max())
+    assert np.all(err <= bound), f"max err / bound = {worst:.3f}"
+
+
+def test_gemm_rejects_bad_arguments():
+    """Argument errors are caught on the host, before any launch."""
+    m, n, k = 128, 128, 30000
+    A = torch.zeros(m, k, device="cuda")
+    B = torch.zeros(n, k, device="cuda")
+    Cm = torch.zeros(m, n, device="cuda")
+    need = S.gemm_workspace_bytes(m, n, k)
+    assert need > 0, "a 1 x 1 tile grid with many k-slices is planned with stream-K partial tiles"
+    ws = torch.empty(need // 4 + 64, device="cuda")
+    with pytest.raises(S.SgdError):
+        S.gemm(A, B, Cm, False, False, ws[: need // 8])       # workspace too small
+    with pytest.raises(S.SgdError):
+        S.gemm(A, B, Cm, False, False, ws[1:])                # workspace not 256-byte aligned
+    with pytest.raises(ValueError):
+        S.gemm(A, B, Cm[:0], False, False, ws)                # C's rows do not match op(A)
+    with pytest.raises(S.SgdError):
+        S.gemm(A[:0], B, Cm[:0], False, False, ws)            # m = 0
+    with pytest.raises(ValueError):
+        S.gemm(A[:, :k // 2], B, Cm, False, False, ws)        # k of op(A) and op(B) differ
+
+
+def test_profile_records_carry_product_shapes():
+    """A small MLP's gradient step: every product is recorded once with its
+    (m, n, k) and form, dedw with its ones column (n + 1) for dedb."""
+    batch, inp = 8, 64
+    layers = [("fc", 32), ("relu",), ("fc", 10), ("softmax_ce",)]
+    wl = workloads.WORKLOADS["mlp5000"]
+    net = S.Net((batch, inp, 1, 1), layers)
+    n = net.param_count()
+    W = torch.from_numpy(workloads.normal(wl.seed, 2, n, 0.1)).cuda()
+    X = torch.from_numpy(workloads.uniform01(wl.seed, 0, (batch, inp, 1, 1))).cuda()
+    y = torch.from_numpy(workloads.labels(wl.seed, 1, batch, 10)).cuda()
+    grad = torch.empty(n, device="cuda")
+    loss = torch.empty(1, device="cuda")
+    ws = net.workspace("cuda")
+    net.set_overlap(False)
+    net.profile(True)
+    net.compute_gradient(W, X, y, grad, loss, ws)
+    torch.cuda.synchronize()
+    net.profile(False)
+    recs = net.profile_read()
+    prods, others = TM.products_of(recs)
+    got = sorted((p["form"], p["m"], p["n"], p["k"]) for p in prods)
+    want = sorted([("nt", batch, 32, inp), ("nt", batch, 10, 32),      # forward
+                   ("tn", 10, 33, batch), ("nn", batch, 32, 10),      # layer 2 dedw(+dedb), dedx
+                   ("tn", 32, inp + 1, batch)])                      # layer 1 dedw(+dedb)
+    assert got == want
+    assert others, "the softmax and loss kernels are recorded outside the products"
+    for (name, _l, _p, ms, _f, _b, shape) in recs:
+        assert ms >= 0
+        if shape[3] < 0:
+            assert shape[:3] == (0, 0, 0), name
