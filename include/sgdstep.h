@@ -346,6 +346,95 @@ int sgd_profile_read(sgd_net* net, sgd_kernel_time* out, int max_records);
 int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, float* state, const sgd_rule* rule,
                    float* loss, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * SPRINT on one GPU (SPRINT report section 3.4, Algorithms 1 and 2): worker
+ * threads, each with its own HIP stream, copy of the weights, gradient
+ * array Grad and gradient buffer GradBuf_t with the empty flag, and one
+ * update thread with its own stream, all sharing LatestWeights (W) on one
+ * device.
+ *
+ *   worker t, step i (Algorithm 1): if i % n_fetch == 0 and LatestWeights is
+ *     newer than its copy, copy it (lines 2-6, under the weights lock);
+ *     take the next sub-batch (batch index = a shared counter mod n_batches);
+ *     Grad <- ComputeGradient (line 9), folded into a private sum over
+ *     n_push steps; every n_push steps (and at its last step) lock GradBuf_t,
+ *     copy the sum in if the buffer is empty, else add it (lines 11-17).
+ *   updater (Algorithm 2 with one node): wait until at least min_bufs
+ *     buffers are non-empty (or every worker has finished); take every
+ *     non-empty GradBuf_t in index order, marking it empty (lines 2-14);
+ *     W <- rule(W, sum of the taken buffers) in one fused pass (lines 15-20,
+ *     the momentum of line 16 is the rule's state); publish the new version.
+ *
+ * The locks are host mutexes; the device order behind them is carried by
+ * HIP events (a worker's add is complete before the updater reads the
+ * buffer; the updater's read before the worker refills it; a fetch copy
+ * before the next update overwrites W).  Each worker step ends with a wait
+ * for its stream, as a worker thread of the report waits for its GPU.
+ *
+ * n_fetch and n_push are the DistBelief review's fetch and push intervals
+ * (Downpour SGD); n_fetch = n_push = 1 is SPRINT.  min_bufs = 1 is the
+ * asynchronous SPRINT updater; with min_bufs = workers and sync = 1 (each
+ * worker waits for an update newer than its last push before its next step)
+ * the run is bulk-synchronous SGD on workers x N_Subbatch samples per update.
+ */
+typedef struct sgd_sprint_config {
+  int workers;   /* N_GPU worker threads / streams, 1..16                   */
+  int iters;     /* gradient steps per worker, >= 1                          */
+  int n_fetch;   /* fetch interval (steps), >= 1                             */
+  int n_push;    /* push interval (steps), >= 1                              */
+  int min_bufs;  /* non-empty buffers an update waits for, 1..workers        */
+  int sync;      /* 1: wait for a newer version before each step after a push */
+} sgd_sprint_config;
+
+/* One gradient step of one worker, in the log. */
+typedef struct sgd_sprint_contrib {
+  int worker, iter;      /* which worker, its step index                       */
+  int push;              /* index of the worker's push that carried it         */
+  int64_t batch;         /* sub-batch index into X / y                          */
+  int64_t version;       /* version of W its gradient was computed at (0: the
+                            caller's W, v: after v updates)                    */
+  int64_t update;        /* the update that applied it (it turned version
+                            `update` into `update` + 1), -1 if none           */
+} sgd_sprint_contrib;
+
+typedef struct sgd_sprint_stats {
+  int64_t updates;       /* updates applied (final version of W)               */
+  int64_t steps;         /* worker gradient steps (workers x iters)            */
+  int64_t fetches;       /* weight copies made by workers                      */
+  double wall_ms;        /* the whole run                                      */
+  double t_gpu_ms;       /* mean worker step (T_GPU of eq. 9)                  */
+  double t_update_ms;    /* mean time between update completions (T_Update)    */
+  double n_minibatch_avg;/* measured: sub-batches applied per update x N_Subbatch */
+  double n_minibatch_eq9;/* eq. 9 (one node): workers x N_Subbatch x T_Update / T_GPU */
+  double staleness_mean; /* mean over steps of update - version                */
+  int64_t staleness_max;
+} sgd_sprint_stats;
+
+/* Device bytes sgd_sprint_run needs for `net` (its batch is N_Subbatch) and
+ * cfg: per worker the net's workspace, three parameter-sized arrays (weights
+ * copy, Grad sum, GradBuf_t) and the loss.  0 for invalid arguments. */
+size_t sgd_sprint_workspace_bytes(const sgd_net* net, const sgd_sprint_config* cfg);
+
+/*
+ * Run cfg->workers x cfg->iters worker steps with the update thread as
+ * above; returns when every step has been applied (the last update drains
+ * whatever the buffers hold).  W (param_count floats) is LatestWeights,
+ * updated in place; `state` the rule's state (NULL for plain).  X and y hold
+ * n_batches sub-batches of the net's batch size, consecutive.  `ws` is
+ * device memory of sgd_sprint_workspace_bytes(), 256-byte aligned.  The run
+ * starts after the work queued on `stream` and the caller's stream waits
+ * for its end; the calling thread blocks until the run ends.  `log` (host,
+ * may be NULL) receives up to log_cap records, one per worker step, in
+ * (worker, iter) order; `stats` (host, may be NULL) the figures above.  The
+ * net's own workspace and streams are not used: each worker plans its own
+ * copy of the net.  Errors: SGD_EINVAL (bad config, null pointers,
+ * n_batches < 1, rule without its state), SGD_EWORKSPACE, SGD_EDEVICE; the
+ * first error of any thread stops the run.
+ */
+int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, float* state, const sgd_rule* rule,
+                   const float* X, const int32_t* y, int64_t n_batches, void* ws, size_t ws_bytes, void* stream,
+                   sgd_sprint_stats* stats, sgd_sprint_contrib* log, int64_t log_cap);
+
 /* Thread-local message describing the last failed call ("" if none). */
 const char* sgd_last_error(void);
 

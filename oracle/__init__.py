@@ -367,3 +367,51 @@ class OracleNet:
             elif k == "softmax_ce":
                 return softmax_ce(a, y, self.reduce_sum, dt)[0]
         raise ValueError("network has no softmax_ce layer")
+
+
+# ----------------------------------------------------------------------------
+# SPRINT's workers and updater, replayed from a recorded schedule.
+# ----------------------------------------------------------------------------
+
+def sprint_replay(net, W0, state0, rule, batches, log, eta, mu=0.0, eps=0.0, decay=0.0):
+    """The weights SPRINT reaches on one node for a given schedule (SPRINT report section 3.4,
+    Algorithms 1 and 2).
+
+    log holds one (worker, iter, push, batch, version, update) per worker step: the step's
+    gradient is taken at the weights after `version` updates, on batches[batch] = (X, y)
+    (Algorithm 1 line 9).  A worker's steps with the same push index are summed in iter order
+    (the first stored, the rest added) and that sum goes into its GradBuf: copied when the
+    buffer is empty, else added (lines 11-17).  Update u takes the buffers holding the steps
+    with update == u, in worker order, folds them the same way into one sum, and applies the
+    rule to the weights (Algorithm 2 lines 2-20 with one node).  A buffer taken by update u
+    holds exactly the pushes of its steps, in push order.
+
+    Returns (W, state, versions): the final weights and rule state, and W after each update
+    (versions[0] is W0)."""
+    n = net.param_count()
+    dt = net.dtype
+    W = np.array(W0, dtype=dt, copy=True)
+    st = None if state0 is None else np.array(state0, dtype=dt, copy=True)
+    versions = [W.copy()]
+    if not log:
+        return W, st, versions
+    if any(e[5] < 0 for e in log):
+        raise ValueError("a step was never applied")
+    if any(e[4] > e[5] for e in log):
+        raise ValueError("a step used weights newer than the update that applied it")
+    for u in range(max(e[5] for e in log) + 1):
+        steps = [e for e in log if e[5] == u]
+        send = GradBuf(n, dt)                                 # SendBuf
+        for t in sorted({e[0] for e in steps}):
+            buf = GradBuf(n, dt)                              # GradBuf_t as update u takes it
+            mine = [e for e in steps if e[0] == t]
+            for p in sorted({e[2] for e in mine}):
+                push = GradBuf(n, dt)                         # Grad summed over one push interval
+                for e in sorted((e for e in mine if e[2] == p), key=lambda e: e[1]):
+                    X, y = batches[e[3]]
+                    push.accumulate(net.gradient(versions[e[4]], X, y)[1])
+                buf.accumulate(push.data)
+            send.accumulate(buf.data)
+        apply_rule(rule, W, st, send.data if not send.empty else None, eta, mu, eps, decay)
+        versions.append(W.copy())
+    return W, st, versions

@@ -34,7 +34,7 @@ EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_of
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
            "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
-           "sgd_last_error"]
+           "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_last_error"]
 
 
 class SgdLayer(C.Structure):
@@ -63,6 +63,22 @@ class SgdKernelTime(C.Structure):
     _fields_ = [("kernel", C.c_char_p), ("layer", C.c_int), ("phase", C.c_int), ("ms", C.c_double),
                 ("flops", C.c_double), ("bytes", C.c_double), ("m", C.c_int), ("n", C.c_int), ("k", C.c_int),
                 ("product", C.c_int)]
+
+
+class SgdSprintConfig(C.Structure):
+    _fields_ = [("workers", C.c_int), ("iters", C.c_int), ("n_fetch", C.c_int), ("n_push", C.c_int),
+                ("min_bufs", C.c_int), ("sync", C.c_int)]
+
+
+class SgdSprintContrib(C.Structure):
+    _fields_ = [("worker", C.c_int), ("iter", C.c_int), ("push", C.c_int), ("batch", C.c_int64),
+                ("version", C.c_int64), ("update", C.c_int64)]
+
+
+class SgdSprintStats(C.Structure):
+    _fields_ = [("updates", C.c_int64), ("steps", C.c_int64), ("fetches", C.c_int64), ("wall_ms", C.c_double),
+                ("t_gpu_ms", C.c_double), ("t_update_ms", C.c_double), ("n_minibatch_avg", C.c_double),
+                ("n_minibatch_eq9", C.c_double), ("staleness_mean", C.c_double), ("staleness_max", C.c_int64)]
 
 
 class SgdError(RuntimeError):
@@ -103,6 +119,9 @@ def lib():
             "sgd_gemm_workspace_bytes": (sz, [C.POINTER(SgdGemmArgs)]),
             "sgd_gemm": (i, [C.POINTER(SgdGemmArgs), P, sz, P]),
             "sgd_profile_read": (i, [P, C.POINTER(SgdKernelTime), i]),
+            "sgd_sprint_workspace_bytes": (sz, [P, C.POINTER(SgdSprintConfig)]),
+            "sgd_sprint_run": (i, [P, C.POINTER(SgdSprintConfig), P, P, C.POINTER(SgdRule), P, P, i64, P, sz, P,
+                                   C.POINTER(SgdSprintStats), C.POINTER(SgdSprintContrib), i64]),
             "sgd_last_error": (C.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -346,3 +365,28 @@ def apply_fused(W, state, grads, rule, stream=None):
     _require_cuda(W, state, *grads)
     arr = (C.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
     _check(lib().sgd_apply_fused(_ptr(W), _ptr(state), arr, len(grads), W.numel(), C.byref(rule), _stream(stream)))
+
+
+def SprintConfig(workers, iters, n_fetch=1, n_push=1, min_bufs=1, sync=False):
+    """SPRINT worker/updater settings (see sgd_sprint_run): min_bufs=1, sync=False is the
+    asynchronous SPRINT updater; min_bufs=workers, sync=True is bulk-synchronous SGD."""
+    return SgdSprintConfig(workers, iters, n_fetch, n_push, min_bufs, 1 if sync else 0)
+
+
+def sprint_workspace_bytes(net, cfg):
+    return lib().sgd_sprint_workspace_bytes(net._h, C.byref(cfg))
+
+
+def sprint_run(net, cfg, W, state, rule, X, y, n_batches, ws, stream=None):
+    """SPRINT's workers and updater on this GPU (sgd_sprint_run).  X, y hold n_batches sub-batches of
+    the net's batch.  Returns (stats dict, log) with one log entry per worker step:
+    (worker, iter, push, batch, version, update)."""
+    _require_cuda(W, state, X, y, ws)
+    steps = cfg.workers * cfg.iters
+    log = (SgdSprintContrib * max(steps, 1))()
+    st = SgdSprintStats()
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().sgd_sprint_run(net._h, C.byref(cfg), _ptr(W), _ptr(state), C.byref(rule), _ptr(X), _ptr(y),
+                                int(n_batches), _ptr(ws), nbytes, _stream(stream), C.byref(st), log, steps))
+    stats = {name: getattr(st, name) for name, _ in SgdSprintStats._fields_}
+    return stats, [(c.worker, c.iter, c.push, c.batch, c.version, c.update) for c in log[:steps]]

@@ -14,6 +14,11 @@ namespace sgd {
 // Thread-local error text behind sgd_last_error().
 void set_error(const std::string& msg);
 
+// A new net planned from the same input, layer list, reduction and
+// settings (implicit convolution, dedw overlap) as `src`.
+int clone_net(const sgd_net* src, sgd_net** out);
+sgd_input net_input(const sgd_net* net);
+
 // Records `what` plus the pending HIP error (if any) and returns SGD_EDEVICE,
 // or returns 0 when the last launch succeeded.
 int check_launch(const char* what);

@@ -750,6 +750,8 @@ int sgd_create_net(const sgd_input* input, const sgd_layer* layers, int n_layers
 
 void sgd_destroy_net(sgd_net* net) { delete net; }
 
+
+
 int64_t sgd_param_count(const sgd_net* net) { return net ? net->n_params : -1; }
 
 int sgd_param_offsets(const sgd_net* net, int64_t* w_off, int64_t* b_off, int max_layers) {
@@ -989,3 +991,21 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
 }
 
 }  // extern "C"
+
+namespace sgd {
+sgd_input net_input(const sgd_net* net) { return net->input; }
+
+int clone_net(const sgd_net* src, sgd_net** out) {
+  if (int e = sgd_create_net(&src->input, src->spec.data(), (int)src->spec.size(), src->reduction, out)) return e;
+  (*out)->overlap = src->overlap;
+  if ((*out)->implicit != src->implicit) {
+    (*out)->implicit = src->implicit;
+    if (int e = plan(*out)) {
+      delete *out;
+      *out = nullptr;
+      return e;
+    }
+  }
+  return SGD_OK;
+}
+}  // namespace sgd

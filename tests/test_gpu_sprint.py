@@ -1,0 +1,136 @@
+"""SPRINT's workers and updater on the GPU (sgd_sprint_run) against the oracle's replay.
+
+The schedule of an asynchronous run depends on timing, so the test takes
+the run's own log (which weight version each step used, which sub-batch,
+which push and which update applied it), checks that it is a schedule
+Algorithms 1 and 2 can produce, and replays it in the oracle in fp64
+(SPRINT report section 3.4).  The final weights and rule state must match
+per parameter tensor to 1e-4 of the change the run made, plus the fp32
+rounding of the stored weights (2^-23 of their size per update).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import sgd_cnns_amd as S  # noqa: E402
+
+LAYERS = [("conv", 8, 3, 1), ("relu",), ("pool", 2), ("fc", 24), ("relu",), ("fc", 7), ("softmax_ce",)]
+CHW = (3, 10, 10)
+N = 5
+CLASSES = 7
+
+
+def inputs(n_batches, seed):
+    X = workloads.uniform01(seed, 0, (n_batches * N,) + CHW)
+    y = workloads.labels(seed, 1, n_batches * N, CLASSES)
+    W0 = workloads.he_normal_params(seed, CHW, LAYERS)
+    return X, y, W0
+
+
+def run(cfg, rule, eta, mu, n_batches, seed):
+    X, y, W0 = inputs(n_batches, seed)
+    net = S.Net((N,) + CHW, LAYERS)
+    dev = torch.device("cuda")
+    Wd = torch.from_numpy(W0.copy()).to(dev)
+    Vd = torch.zeros_like(Wd)
+    ws = torch.empty(S.sprint_workspace_bytes(net, cfg), dtype=torch.uint8, device=dev)
+    stats, log = S.sprint_run(net, cfg, Wd, Vd, S.Rule(rule, eta, mu), torch.from_numpy(X).to(dev),
+                              torch.from_numpy(y).to(dev), n_batches, ws)
+    torch.cuda.synchronize()
+    return stats, log, (X, y, W0), Wd.cpu().numpy(), Vd.cpu().numpy()
+
+
+def check_schedule(log, cfg, n_batches):
+    """Properties every schedule of Algorithms 1 and 2 has."""
+    assert len(log) == cfg.workers * cfg.iters
+    assert [(e[0], e[1]) for e in log] == [(t, i) for t in range(cfg.workers) for i in range(cfg.iters)]
+    U = max(e[5] for e in log) + 1
+    assert sorted({e[5] for e in log}) == list(range(U)), "every update applies at least one step"
+    assert sorted(e[3] for e in log) == sorted(i % n_batches for i in range(len(log))), "shared batch counter"
+    for t in range(cfg.workers):
+        mine = log[t * cfg.iters:(t + 1) * cfg.iters]
+        for i, e in enumerate(mine):
+            assert 0 <= e[4] <= e[5], e
+            assert e[2] == i // cfg.n_push, e                     # push interval
+            if i % cfg.n_fetch:
+                assert e[4] == mine[i - 1][4], e                  # no fetch between fetch points
+            if i:
+                assert e[4] >= mine[i - 1][4] and e[5] >= mine[i - 1][5], e
+        for p in {e[2] for e in mine}:
+            assert len({e[5] for e in mine if e[2] == p}) == 1, "a push is applied by one update"
+    return U
+
+
+def close(got, ref, base, U, what):
+    scale = np.abs(ref - base).max()
+    tol = 1e-4 * scale + U * 2.0 ** -23 * np.abs(ref).max()
+    err = np.abs(got.astype(np.float64) - ref).max()
+    assert err <= tol, f"{what}: max|d| {err:.3e} > {tol:.3e} (change {scale:.3e})"
+
+
+def compare(log, data, W, V, rule, eta, mu):
+    X, y, W0 = data
+    onet = O.OracleNet(CHW, LAYERS, dtype=np.float64)
+    n_batches = X.shape[0] // N
+    batches = [(X[b * N:(b + 1) * N], y[b * N:(b + 1) * N]) for b in range(n_batches)]
+    Wr, Vr, vers = O.sprint_replay(onet, W0.astype(np.float64), np.zeros(W0.size), rule, batches, log, eta, mu=mu)
+    U = len(vers) - 1
+    for i in sorted(onet.params):
+        wo, shape, bo, nb = onet.params[i]
+        for a, b in ((wo, wo + int(np.prod(shape))), (bo, bo + nb)):
+            close(W[a:b], Wr[a:b], W0[a:b].astype(np.float64), U, f"W[{a}:{b}]")
+            close(V[a:b], Vr[a:b], np.zeros(b - a), U, f"V[{a}:{b}]")
+
+
+def test_bulk_synchronous_run_matches_replay():
+    cfg = S.SprintConfig(workers=3, iters=3, min_bufs=3, sync=True)
+    print("[sprint] sync 3 workers x 3 steps, momentum", flush=True)
+    stats, log, data, W, V = run(cfg, "momentum", 0.05, 0.9, 9, 81)
+    U = check_schedule(log, cfg, 9)
+    assert U == 3 and stats["updates"] == 3
+    for u in range(3):
+        assert sorted((e[0], e[4]) for e in log if e[5] == u) == [(0, u), (1, u), (2, u)]
+    assert stats["staleness_max"] == 0 and stats["n_minibatch_avg"] == 3 * N
+    assert stats["steps"] == 9 and stats["fetches"] == 9
+    compare(log, data, W, V, "momentum", 0.05, 0.9)
+
+
+@pytest.mark.parametrize("workers,iters,n_fetch,n_push", [(4, 6, 1, 1), (3, 7, 2, 2), (1, 5, 1, 1)])
+def test_asynchronous_run_matches_replay(workers, iters, n_fetch, n_push):
+    cfg = S.SprintConfig(workers=workers, iters=iters, n_fetch=n_fetch, n_push=n_push)
+    print(f"[sprint] async {workers} workers x {iters} steps, fetch {n_fetch}, push {n_push}", flush=True)
+    stats, log, data, W, V = run(cfg, "momentum", 0.05, 0.5, 8, 82 + workers)
+    U = check_schedule(log, cfg, 8)
+    assert stats["updates"] == U and stats["steps"] == workers * iters
+    stale = [e[5] - e[4] for e in log]
+    assert stats["staleness_max"] == max(stale)
+    assert stats["staleness_mean"] == pytest.approx(np.mean(stale))
+    assert stats["n_minibatch_avg"] == pytest.approx(workers * iters * N / U)
+    assert stats["t_gpu_ms"] > 0 and stats["wall_ms"] > 0
+    compare(log, data, W, V, "momentum", 0.05, 0.5)
+
+
+def test_bad_configs_are_rejected_on_the_host():
+    net = S.Net((N,) + CHW, LAYERS)
+    X, y, W0 = inputs(2, 1)
+    dev = torch.device("cuda")
+    Wd = torch.from_numpy(W0).to(dev)
+    Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+    good = S.SprintConfig(workers=2, iters=1)
+    ws = torch.empty(S.sprint_workspace_bytes(net, good), dtype=torch.uint8, device=dev)
+    for bad in (S.SprintConfig(0, 1), S.SprintConfig(17, 1), S.SprintConfig(2, 0), S.SprintConfig(2, 1, n_fetch=0),
+                S.SprintConfig(2, 1, min_bufs=3)):
+        assert S.sprint_workspace_bytes(net, bad) == 0
+        with pytest.raises(S.SgdError):
+            S.sprint_run(net, bad, Wd, Wd.clone(), S.Rule("plain", 0.1), Xd, yd, 2, ws)
+    with pytest.raises(S.SgdError):                      # no sub-batches
+        S.sprint_run(net, good, Wd, Wd.clone(), S.Rule("plain", 0.1), Xd, yd, 0, ws)
+    with pytest.raises(S.SgdError):                      # momentum without its state
+        S.sprint_run(net, good, Wd, None, S.Rule("momentum", 0.1, 0.9), Xd, yd, 2, ws)
+    with pytest.raises(S.SgdError):                      # workspace too small
+        S.sprint_run(net, good, Wd, Wd.clone(), S.Rule("plain", 0.1), Xd, yd, 2, ws[: ws.numel() // 2])
