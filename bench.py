@@ -95,7 +95,7 @@ def gpu_step_bench(wl, steps, warmup):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    net.profile(True)
+    # the timed region: the steps alone, no per-launch events
     wall0 = time.perf_counter()
     t0.record(stream)
     for _ in range(steps):
@@ -103,10 +103,20 @@ def gpu_step_bench(wl, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    net.profile(False)
     total_ms = t0.elapsed_time(t1)
-    recs = net.profile_read()
     loss_v = float(loss.item())
+    # the same number of steps again with an event pair around every launch (sgd_profile): the
+    # per-kernel durations of the roofline and the kernel table.  The events add a few
+    # microseconds per launch, so this pass is not the one the throughput is taken from.
+    net.profile(True)
+    t0.record(stream)
+    for _ in range(steps):
+        step(record=True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    net.profile(False)
+    prof_ms = t0.elapsed_time(t1)
+    recs = net.profile_read()
     if warm_losses:
         print(f"[bench] warmup losses {['%.4g' % v for v in warm_losses]}, last timed step {loss_v:.4g}",
               file=sys.stderr, flush=True)
@@ -146,7 +156,7 @@ def gpu_step_bench(wl, steps, warmup):
         upd_ms += u1.elapsed_time(u2)
     unfused_ms = u0.elapsed_time(u2) / reps
     upd_b = {"plain": 12.0, "momentum": 20.0, "adagrad": 20.0}[wl.rule] * n
-    return dict(total_ms=total_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n,
+    return dict(total_ms=total_ms, prof_ms=prof_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n,
                 loss_first=warm_losses[0] if warm_losses else None,
                 update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * upd_ms / reps,
                         "GB/s": upd_b / (upd_ms / reps / 1e3) / 1e9},
@@ -479,6 +489,92 @@ def timing_model_report(out_path, raw_prefix=None, reps=3):
     print(text)
 
 
+def sprint_report(out_path, workload="mlp5000"):
+    """SPRINT's asynchronous workers and updater on one GPU (section 3.4, Algorithms 1 and 2): for
+    several worker counts and sub-batch sizes, the throughput, T_GPU, T_Update, the measured average
+    minibatch per update against eq. (9), and the staleness of the applied gradients."""
+    import numpy as np
+    import torch
+
+    import sgd_cnns_amd as S
+    import workloads
+
+    def say(msg):
+        print(f"[sprint] {msg}", file=sys.stderr, flush=True)
+
+    base = workloads.WORKLOADS[workload]
+    dev = torch.device("cuda")
+    rows = []
+    t_start = time.perf_counter()
+    for sub in (128, 512):
+        wl = base.with_batch(sub)
+        n_batches = 16
+        X = workloads.uniform01(wl.seed, 0, (n_batches * sub,) + tuple(wl.chw))
+        y = workloads.labels(wl.seed, 1, n_batches * sub, wl.classes)
+        W0 = workloads.he_normal_params(wl.seed, wl.chw, wl.layers)
+        Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+        net = S.Net((sub,) + tuple(wl.chw), wl.layers)
+        rule = S.Rule(wl.rule, wl.eta, wl.mu, wl.eps)
+        # the single-stream step at this sub-batch (sgd_train_step), for reference
+        Wd = torch.from_numpy(W0).to(dev)
+        V = torch.zeros_like(Wd)
+        ws1 = net.workspace(dev)
+        loss = torch.empty(1, device=dev)
+        for _ in range(3):
+            net.train_step(Wd, Xd[:sub], yd[:sub], V, rule, loss, ws1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for r in range(reps):
+            b = r % n_batches
+            net.train_step(Wd, Xd[b * sub:(b + 1) * sub], yd[b * sub:(b + 1) * sub], V, rule, loss, ws1)
+        e1.record()
+        torch.cuda.synchronize()
+        single_ms = e0.elapsed_time(e1) / reps
+        del ws1
+        for workers in (1, 2, 4, 8):
+            iters = max(8, int(round(400.0 / (single_ms * workers))))
+            cfg = S.SprintConfig(workers=workers, iters=iters)
+            ws = torch.empty(S.sprint_workspace_bytes(net, cfg), dtype=torch.uint8, device=dev)
+            Wd.copy_(torch.from_numpy(W0))
+            V.zero_()
+            S.sprint_run(net, S.SprintConfig(workers=workers, iters=2), Wd, V, rule, Xd, yd, n_batches, ws)  # warm-up
+            Wd.copy_(torch.from_numpy(W0))
+            V.zero_()
+            torch.cuda.synchronize()
+            st, log = S.sprint_run(net, cfg, Wd, V, rule, Xd, yd, n_batches, ws)
+            torch.cuda.synchronize()
+            finite = bool(torch.isfinite(Wd).all().item())
+            say(f"sub-batch {sub}, {workers} workers x {iters}: {st['steps'] * sub / st['wall_ms'] * 1e3:.0f} img/s")
+            rows.append(dict(sub=sub, workers=workers, iters=iters, single_ms=single_ms, finite=finite, **st))
+            del ws
+            torch.cuda.empty_cache()
+    L = ["# SPRINT Algorithms 1 and 2 on one MI355X", "",
+         f"Command (from the repository root): `python bench.py --sprint {os.path.relpath(out_path, ROOT)}`", "",
+         f"Workload: {describe(base)} with the sub-batch below per worker step; 16 seeded synthetic sub-batches "
+         "taken in turn by a shared counter.  Asynchronous SPRINT: every worker fetches LatestWeights at every "
+         "step (n_fetch = 1) and pushes every step (n_push = 1); the updater applies whatever buffers are "
+         "non-empty as soon as one is (min_bufs = 1), summing them and applying the momentum rule in one pass.  "
+         f"Run time {time.perf_counter() - t_start:.0f} s.", "",
+         "T_GPU is a worker's mean step (fetch, gradient, push, wait for its stream); T_Update the mean time "
+         "between update completions.  Eq. (9) with one node: N_Minibatch_avg = N_GPU x N_Subbatch x "
+         "T_Update / T_GPU.  Staleness: updates between the version a gradient was computed at and the update "
+         "that applied it.  'single stream' is sgd_train_step at the same sub-batch, one step per update.", "",
+         "| N_Subbatch | workers (N_GPU) | steps | images/s | single stream images/s | T_GPU ms | T_Update ms "
+         "| updates | N_Minibatch_avg measured | eq. (9) | staleness mean | max | weights finite |",
+         "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        L.append(f"| {r['sub']} | {r['workers']} | {r['steps']} | {r['steps'] * r['sub'] / r['wall_ms'] * 1e3:.0f} | "
+                 f"{r['sub'] / r['single_ms'] * 1e3:.0f} | {r['t_gpu_ms']:.3f} | {r['t_update_ms']:.3f} | "
+                 f"{r['updates']} | {r['n_minibatch_avg']:.1f} | {r['n_minibatch_eq9']:.1f} | "
+                 f"{r['staleness_mean']:.2f} | {r['staleness_max']} | {r['finite']} |")
+    text = "\n".join(L) + "\n"
+    with open(out_path, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
 def main():
     import numpy as np
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -495,6 +591,8 @@ def main():
                     help="refit the SPRINT timing model (eqs. 4-6) and write its report instead of the step bench")
     ap.add_argument("--timing-model-raw", metavar="PREFIX", default=None,
                     help="also save the timing model's raw grid times and step records under this prefix")
+    ap.add_argument("--sprint", metavar="OUT_MD", default=None,
+                    help="run SPRINT's asynchronous workers and updater (Algorithms 1 and 2) and write the report")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -502,6 +600,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.sprint:
+        sprint_report(args.sprint)
+        return
     if args.timing_model:
         timing_model_report(args.timing_model, args.timing_model_raw)
         return
@@ -528,7 +629,7 @@ def main():
     g_flops = sum(v["flops"] for v in gemms.values())
     g_ms = sum(v["ms"] for v in gemms.values())
     upd = r["update"]
-    kernels = kernel_table(kern, r["total_ms"])
+    kernels = kernel_table(kern, r["prof_ms"])
     iso = r["kern_iso"].get(dom)
     out = {
         "metric": METRIC,
@@ -550,9 +651,13 @@ def main():
                      "traffic": measured_traffic(dom, wl.name),
                      "launches": d["launches"], "avg_launch_us": 1e3 * d["ms"] / d["launches"],
                      "flops_per_launch": d["flops"] / d["launches"],
-                     "note": "timed region: each layer's dedw product runs on a second stream, overlapping the next "
-                             "layer's dedx product, so avg_launch_us is the launch's duration while it shares the "
-                             "GPU; roofline_isolated is the same kernel with the overlap switched off"},
+                     "ms_per_step_profiled": r["prof_ms"] / args.steps,
+                     "note": "kernel durations from HIP events around every launch over the same number of steps, "
+                             "run right after the timed region (the events cost a few microseconds per launch, so "
+                             "value is timed without them).  Each layer's dedw product runs on a second stream, "
+                             "overlapping the next layer's dedx product, so avg_launch_us is the launch's duration "
+                             "while it shares the GPU; roofline_isolated is the same kernel with the overlap "
+                             "switched off"},
         "roofline_isolated": None if iso is None else {
             "kernel": dom, "achieved": iso["flops"] / (iso["ms"] / 1e3) / 1e12, "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s", "frac": iso["flops"] / (iso["ms"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
@@ -561,7 +666,7 @@ def main():
         "kernels_isolated": kernel_table(r["kern_iso"], r["iso_ms"] * r["iso_reps"])[:8],
         "gemm_mfma_util": {"achieved_TFLOP/s": g_flops / (g_ms / 1e3) / 1e12,
                            "frac_fp32_peak": g_flops / (g_ms / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
-                           "share_of_step": g_ms / r["total_ms"]},
+                           "share_of_step": g_ms / r["prof_ms"]},
         "update_GB/s": {"kernel": upd["kernel"], "GB/s": upd["GB/s"], "frac_hbm_peak": upd["GB/s"] / PEAK_HBM_GBS,
                         "avg_us": upd["avg_us"],
                         "note": "standalone apply after gradient-into-GradBuf; the timed step fuses the update into "
