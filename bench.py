@@ -58,7 +58,7 @@ def describe(wl):
     return f"{wl.name}: {arch}, batch {wl.batch}, {rule}"
 
 
-def gpu_step_bench(wl, steps, warmup):
+def gpu_step_bench(wl, steps, warmup, use_graph=True):
     import numpy as np
     import torch
 
@@ -95,15 +95,34 @@ def gpu_step_bench(wl, steps, warmup):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    # the timed region: the steps alone, no per-launch events
+    # the timed region, twice: the steps launched one call at a time, then (unless disabled) the step
+    # recorded once as a HIP graph (sgd_train_step_graph) and replayed, one launch per step.  Both are
+    # whole steps with no per-launch events; value takes the faster.  The graph removes the host
+    # launch gaps (small networks) but its replay may not overlap the dedw stream with the main one.
     wall0 = time.perf_counter()
     t0.record(stream)
     for _ in range(steps):
-        step(record=True)
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
+    eager_ms = t0.elapsed_time(t1)
+    graph_ms = None
+    graph = None
+    if use_graph:
+        graph = S.StepGraph(net, Wd, Xd, yd, state, rule, loss, ws)
+        graph.launch(stream)
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        t0.record(stream)
+        for _ in range(steps):
+            graph.launch(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = t0.elapsed_time(t1)
+        if graph_ms < eager_ms:
+            wall = time.perf_counter() - g0
+    total_ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
     loss_v = float(loss.item())
     # the same number of steps again with an event pair around every launch (sgd_profile): the
     # per-kernel durations of the roofline and the kernel table.  The events add a few
@@ -156,7 +175,9 @@ def gpu_step_bench(wl, steps, warmup):
         upd_ms += u1.elapsed_time(u2)
     unfused_ms = u0.elapsed_time(u2) / reps
     upd_b = {"plain": 12.0, "momentum": 20.0, "adagrad": 20.0}[wl.rule] * n
-    return dict(total_ms=total_ms, prof_ms=prof_ms, wall_s=wall, kern=kern, loss=loss_v, n_params=n,
+    return dict(total_ms=total_ms, prof_ms=prof_ms, eager_ms=eager_ms, graph_ms=graph_ms,
+                graph=graph_ms is not None and graph_ms < eager_ms, wall_s=wall,
+                kern=kern, loss=loss_v, n_params=n,
                 loss_first=warm_losses[0] if warm_losses else None,
                 update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * upd_ms / reps,
                         "GB/s": upd_b / (upd_ms / reps / 1e3) / 1e9},
@@ -584,6 +605,7 @@ def main():
     ap.add_argument("--workload", default="mlp5000", choices=["mlp5000", "lenet5", "vgg_cifar", "vgg16"])
     ap.add_argument("--cpu-sample", type=int, default=0, help="images in the oracle sample (0 = per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--no-ps-apply", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter scaling)")
@@ -618,7 +640,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     print(f"[bench] {describe(wl)}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    r = gpu_step_bench(wl, args.steps, args.warmup)
+    r = gpu_step_bench(wl, args.steps, args.warmup, use_graph=not args.no_graph)
     ms_step = r["total_ms"] / args.steps
     value = wl.batch * args.steps / (r["total_ms"] / 1e3)
     kern = r["kern"]
@@ -671,6 +693,10 @@ def main():
                         "avg_us": upd["avg_us"],
                         "note": "standalone apply after gradient-into-GradBuf; the timed step fuses the update into "
                                 "the dedw epilogues (sgd_train_step)"},
+        "timed_as": "HIP graph replay of sgd_train_step (one launch per step)" if r["graph"] else
+                    "sgd_train_step launched per step",
+        "eager_ms_per_step": r["eager_ms"] / args.steps,
+        "graph_ms_per_step": None if r["graph_ms"] is None else r["graph_ms"] / args.steps,
         "unfused_ms_per_step": r["unfused_ms"],
         "kernels": kernels,
         "loss_first_step": r["loss_first"],

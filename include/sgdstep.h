@@ -435,6 +435,26 @@ int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, f
                    const float* X, const int32_t* y, int64_t n_batches, void* ws, size_t ws_bytes, void* stream,
                    sgd_sprint_stats* stats, sgd_sprint_contrib* log, int64_t log_cap);
 
+/*
+ * sgd_train_step recorded once as a HIP graph, to be replayed with one
+ * launch per step: the step's 20-100 kernel launches (and the fork/join of
+ * the dedw stream) become graph nodes, which removes the host launch gaps
+ * that dominate small networks.  Recording does not run the step.  The graph
+ * is bound to the pointers given here: every replay reads X, y and the
+ * current contents of W and state, and writes W, state, loss and ws, exactly
+ * as sgd_train_step with those arguments would (bitwise).  While a replay is
+ * in flight neither the graph's buffers nor the net may be used by another
+ * call; the net must outlive the graph.  Profiling must be off.  Errors:
+ * as sgd_train_step, SGD_EINVAL (profiling on, null output), SGD_EDEVICE
+ * (capture or instantiation failed).
+ */
+typedef struct sgd_step_graph sgd_step_graph;
+int sgd_train_step_graph(sgd_net* net, float* W, const float* X, const int32_t* y, float* state,
+                         const sgd_rule* rule, float* loss, void* ws, size_t ws_bytes, sgd_step_graph** out);
+/* One replay of the recorded step on `stream` (asynchronous).  Errors: SGD_EINVAL, SGD_EDEVICE. */
+int sgd_step_graph_launch(sgd_step_graph* g, void* stream);
+void sgd_step_graph_destroy(sgd_step_graph* g);
+
 /* Thread-local message describing the last failed call ("" if none). */
 const char* sgd_last_error(void);
 

@@ -34,7 +34,8 @@ EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_of
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
            "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
-           "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_last_error"]
+           "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_train_step_graph", "sgd_step_graph_launch",
+           "sgd_step_graph_destroy", "sgd_last_error"]
 
 
 class SgdLayer(C.Structure):
@@ -122,6 +123,9 @@ def lib():
             "sgd_sprint_workspace_bytes": (sz, [P, C.POINTER(SgdSprintConfig)]),
             "sgd_sprint_run": (i, [P, C.POINTER(SgdSprintConfig), P, P, C.POINTER(SgdRule), P, P, i64, P, sz, P,
                                    C.POINTER(SgdSprintStats), C.POINTER(SgdSprintContrib), i64]),
+            "sgd_train_step_graph": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P, sz, C.POINTER(P)]),
+            "sgd_step_graph_launch": (i, [P, P]),
+            "sgd_step_graph_destroy": (None, [P]),
             "sgd_last_error": (C.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -293,6 +297,29 @@ class Net:
         _require_cuda(W, X, y, state, loss, ws)
         _check(lib().sgd_train_step(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(state), C.byref(rule), _ptr(loss),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class StepGraph:
+    """sgd_train_step recorded as a HIP graph (sgd_train_step_graph); launch() replays one step.
+    Holds references to the net and the buffers the graph is bound to."""
+
+    def __init__(self, net, W, X, y, state, rule, loss, ws):
+        _require_cuda(W, X, y, state, loss, ws)
+        self._keep = (net, W, X, y, state, loss, ws)
+        self._rule = rule
+        h = C.c_void_p()
+        _check(lib().sgd_train_step_graph(net._h, _ptr(W), _ptr(X), _ptr(y), _ptr(state), C.byref(rule), _ptr(loss),
+                                          _ptr(ws), ws.numel() * ws.element_size(), C.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(lib().sgd_step_graph_launch(self._h, _stream(stream)))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.sgd_step_graph_destroy(h)
+            self._h = None
 
 
 class GradBuf:

@@ -930,6 +930,66 @@ int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, flo
   return step(net, W, X, y, W, false, rule, state, loss, ws, ws_bytes, stream, "sgd_train_step");
 }
 
+struct sgd_step_graph {
+  hipGraphExec_t exec = nullptr;
+};
+
+int sgd_train_step_graph(sgd_net* net, float* W, const float* X, const int32_t* y, float* state,
+                         const sgd_rule* rule, float* loss, void* ws, size_t ws_bytes, sgd_step_graph** out) {
+  const char* who = "sgd_train_step_graph";
+  if (!out) return fail(SGD_EINVAL, std::string(who) + ": null output");
+  *out = nullptr;
+  if (!net) return fail(SGD_EINVAL, std::string(who) + ": null net");
+  if (int e = check_rule(rule, state, who)) return e;
+  if (net->prof.on) return fail(SGD_EINVAL, std::string(who) + ": profiling is on (its timing events cannot be captured)");
+  // the dedw side stream and its fork/join events must exist before the capture starts
+  if (net->overlap && net->side.ready((int)net->w_offs.size()))
+    return fail(SGD_EDEVICE, std::string(who) + ": could not create the side stream");
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
+    return fail(SGD_EDEVICE, std::string(who) + ": hipStreamCreate failed");
+  int e = SGD_OK;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed) != hipSuccess) {
+    e = fail(SGD_EDEVICE, std::string(who) + ": hipStreamBeginCapture failed");
+  } else {
+    e = step(net, W, X, y, W, false, rule, state, loss, ws, ws_bytes, cs, who);
+    hipGraph_t g = nullptr;
+    const hipError_t ce = hipStreamEndCapture(cs, &g);  // always ends the capture
+    if (!e && ce != hipSuccess) e = fail(SGD_EDEVICE, std::string(who) + ": hipStreamEndCapture failed");
+    if (!e) {
+      hipGraphExec_t ex = nullptr;
+      if (hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) != hipSuccess) {
+        e = fail(SGD_EDEVICE, std::string(who) + ": hipGraphInstantiate failed");
+      } else {
+        sgd_step_graph* sg = new (std::nothrow) sgd_step_graph();
+        if (!sg) {
+          (void)hipGraphExecDestroy(ex);
+          e = fail(SGD_EINVAL, std::string(who) + ": out of host memory");
+        } else {
+          sg->exec = ex;
+          *out = sg;
+        }
+      }
+    }
+    if (g) (void)hipGraphDestroy(g);
+  }
+  (void)hipStreamDestroy(cs);
+  return e;
+}
+
+int sgd_step_graph_launch(sgd_step_graph* g, void* stream) {
+  if (!g || !g->exec) return fail(SGD_EINVAL, "sgd_step_graph_launch: null graph");
+  if (hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(SGD_EDEVICE, "sgd_step_graph_launch: hipGraphLaunch failed");
+  return SGD_OK;
+}
+
+void sgd_step_graph_destroy(sgd_step_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  delete g;
+}
+
 int sgd_accumulate_grad(sgd_gradbuf* gb, const float* grad, void* stream) {
   if (!gb || !gb->data || !grad) return fail(SGD_EINVAL, "sgd_accumulate_grad: null pointer");
   if (gb->n <= 0) return fail(SGD_EINVAL, "sgd_accumulate_grad: n must be positive");
