@@ -238,6 +238,87 @@ __global__ void maxpool_bwd_kernel(const float* __restrict__ dy, const uint8_t* 
   }
 }
 
+// Four channels per thread (C % 4 == 0, NHWC in and out, 16-byte aligned,
+// fewer than 2^31 quads): thread i owns output pixel i / (C/4), channels
+// 4*(i % (C/4)) .. +3, so every load and store is a float4 (the argmax a
+// uchar4).  Per channel the same comparisons as maxpool_fwd_kernel.
+__global__ void maxpool_fwd_vec4(const float4* __restrict__ x, float4* __restrict__ y, uchar4* __restrict__ argmax,
+                                 int N, int C4, int H, int W, int p) {
+  const int Ho = H / p, Wo = W / p;
+  const int total = N * Ho * Wo * C4;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int c4 = i % C4;
+    int t = i / C4;
+    const int ox = t % Wo;
+    t /= Wo;
+    const int oy = t % Ho;
+    const int n = t / Ho;
+    const float4* base = x + ((int64_t)(n * H + oy * p) * W + ox * p) * C4 + c4;
+    float b[4], v0[4];
+    int bi[4] = {0, 0, 0, 0};
+    bool nan[4] = {false, false, false, false};
+    {
+      const float4 v = base[0];
+      b[0] = v.x, b[1] = v.y, b[2] = v.z, b[3] = v.w;
+    }
+    for (int ky = 0; ky < p; ++ky)
+      for (int kx = 0; kx < p; ++kx) {
+        const float4 v = base[((int64_t)ky * W + kx) * C4];
+        v0[0] = v.x, v0[1] = v.y, v0[2] = v.z, v0[3] = v.w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (v0[q] != v0[q]) nan[q] = true;
+          if (v0[q] > b[q]) {
+            b[q] = v0[q];
+            bi[q] = ky * p + kx;
+          }
+        }
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (nan[q]) b[q] = __builtin_nanf("");
+    y[i] = make_float4(b[0], b[1], b[2], b[3]);
+    argmax[i] = make_uchar4((unsigned char)bi[0], (unsigned char)bi[1], (unsigned char)bi[2], (unsigned char)bi[3]);
+  }
+}
+
+// The backward pass in the same layout: thread i reads its window's
+// gradient, argmax (and pooled value) once and writes all p x p input
+// positions of the window, so the only large stream is the float4 stores of
+// dx.  Per channel the same rule as maxpool_bwd_kernel.
+__global__ void maxpool_bwd_vec4(const float4* __restrict__ dy, const uchar4* __restrict__ argmax,
+                                 const float4* __restrict__ pooled, float4* __restrict__ dx, int N, int C4, int H,
+                                 int W, int p) {
+  const int Ho = H / p, Wo = W / p;
+  const int total = N * Ho * Wo * C4;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int c4 = i % C4;
+    int t = i / C4;
+    const int ox = t % Wo;
+    t /= Wo;
+    const int oy = t % Ho;
+    const int n = t / Ho;
+    const float4 d = dy[i];
+    const uchar4 am = argmax[i];
+    float g[4] = {d.x, d.y, d.z, d.w};
+    const int a[4] = {am.x, am.y, am.z, am.w};
+    if (pooled) {
+      const float4 pv = pooled[i];
+      const float pq[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (!(pq[q] > 0.f)) g[q] = 0.f;
+    }
+    float4* base = dx + ((int64_t)(n * H + oy * p) * W + ox * p) * C4 + c4;
+    for (int ky = 0; ky < p; ++ky)
+      for (int kx = 0; kx < p; ++kx) {
+        const int l = ky * p + kx;
+        base[((int64_t)ky * W + kx) * C4] =
+            make_float4(a[0] == l ? g[0] : 0.f, a[1] == l ? g[1] : 0.f, a[2] == l ? g[2] : 0.f, a[3] == l ? g[3] : 0.f);
+      }
+  }
+}
+
 // ------------------------------------------------------ softmax + CE loss ----
 // One wavefront per sample row.  lse = m + log(sum exp(z - m)), the row loss
 // lse - z[y], and dz = scale * (exp(z - lse) - [j == y]).  Wavefront
@@ -345,12 +426,27 @@ int repack_weight_dx(const float* w, float* wdx, int Co, int Ci, int c, hipStrea
   return check_launch("repack_weight_dx");
 }
 
+namespace {
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+// The float4 pooling kernels: NHWC output, whole channel quads, aligned
+// pointers (the argmax as uchar4) and a quad count that fits their int math.
+bool pool_vec4_ok(int C, int64_t outputs, bool out_nchw, const void* a, const void* b, const void* am) {
+  return !out_nchw && C % 4 == 0 && outputs / 4 < ((int64_t)1 << 31) && aligned16(a) && aligned16(b) &&
+         (reinterpret_cast<uintptr_t>(am) & 3) == 0;
+}
+}  // namespace
+
 int maxpool_fwd(const float* x, float* y, uint8_t* argmax, int N, int C, int H, int W, int p, bool out_nchw,
                 hipStream_t s) {
   const int64_t total = (int64_t)N * (H / p) * (W / p) * C;
   prof_begin("maxpool_fwd", (double)N * H * W * C, 4.0 * N * H * W * C + 5.0 * total, s);
-  hipLaunchKernelGGL(maxpool_fwd_kernel, dim3(grid_for(total)), dim3(kBlock), 0, s, x, y, argmax, N, C, H, W, p,
-                     (int)out_nchw);
+  if (pool_vec4_ok(C, total, out_nchw, x, y, argmax))
+    hipLaunchKernelGGL(maxpool_fwd_vec4, dim3(grid_for(total / 4)), dim3(kBlock), 0, s,
+                       reinterpret_cast<const float4*>(x), reinterpret_cast<float4*>(y),
+                       reinterpret_cast<uchar4*>(argmax), N, C / 4, H, W, p);
+  else
+    hipLaunchKernelGGL(maxpool_fwd_kernel, dim3(grid_for(total)), dim3(kBlock), 0, s, x, y, argmax, N, C, H, W, p,
+                       (int)out_nchw);
   prof_end(s);
   return check_launch("maxpool_fwd");
 }
@@ -360,8 +456,14 @@ int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, flo
   const int64_t total = (int64_t)N * H * W * C;
   const double pooled_n = (double)total / ((double)p * p);
   prof_begin("maxpool_bwd", 0, 4.0 * total + pooled_n * (pooled ? 9.0 : 5.0), s);
-  hipLaunchKernelGGL(maxpool_bwd_kernel, dim3(grid_for(total)), dim3(kBlock), 0, s, dy, argmax, pooled, dx, N, C,
-                     H, W, p, (int)out_nchw);
+  const int64_t outs = total / ((int64_t)p * p);
+  if (pool_vec4_ok(C, outs, out_nchw, dy, dx, argmax) && (!pooled || aligned16(pooled)))
+    hipLaunchKernelGGL(maxpool_bwd_vec4, dim3(grid_for(outs / 4)), dim3(kBlock), 0, s,
+                       reinterpret_cast<const float4*>(dy), reinterpret_cast<const uchar4*>(argmax),
+                       reinterpret_cast<const float4*>(pooled), reinterpret_cast<float4*>(dx), N, C / 4, H, W, p);
+  else
+    hipLaunchKernelGGL(maxpool_bwd_kernel, dim3(grid_for(total)), dim3(kBlock), 0, s, dy, argmax, pooled, dx, N, C,
+                       H, W, p, (int)out_nchw);
   prof_end(s);
   return check_launch("maxpool_bwd");
 }
