@@ -73,6 +73,40 @@ __global__ void im2col_scalar(const float* __restrict__ x, float* __restrict__ c
   }
 }
 
+// The general im2col one float4 of a column-matrix row per thread (ldk % 4
+// == 0, fewer than 2^31 quads): thread i writes Col[p][4q .. 4q+3] with
+// p = i / (ldk/4), q = i % (ldk/4), so consecutive threads store consecutive
+// 16 bytes; the index math is 32-bit.  Same values as im2col_scalar.
+template <bool NCHW>
+__global__ void im2col_quad(const float* __restrict__ x, float4* __restrict__ col, int N, int Ci, int H, int W,
+                            int c, int P, int Ho, int Wo, int ldk) {
+  const int K = c * c * Ci;
+  const int q4 = ldk / 4;
+  const int total = N * Ho * Wo * q4;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int p = i / q4;
+    const int q = i - p * q4;
+    const int ox = p % Wo;
+    const int t = p / Wo;
+    const int oy = t % Ho;
+    const int n = t / Ho;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kk = 4 * q + e;
+      v[e] = 0.f;
+      if (kk < K) {
+        const int tap = kk / Ci, ci = kk - tap * Ci;
+        const int ky = tap / c, kx = tap - ky * c;
+        const int iy = oy + ky - P, ix = ox + kx - P;
+        if (iy >= 0 && iy < H && ix >= 0 && ix < W)
+          v[e] = NCHW ? x[(((int64_t)n * Ci + ci) * H + iy) * W + ix] : x[(((int64_t)n * H + iy) * W + ix) * Ci + ci];
+      }
+    }
+    col[i] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 // ---------------------------------------------------------------- col2im ----
 // dx[n][iy][ix][ci] = sum over (ky, kx) in row-major order of
 // dcol[(n, iy - ky + P, ix - kx + P)][(ky*c + kx)*Ci + ci] (taps outside the
@@ -380,6 +414,15 @@ int im2col(const float* x, bool x_nchw, float* col, int N, int Ci, int H, int W,
     const int64_t total = (int64_t)N * Ho * Wo * c * c * (Ci / 4);
     hipLaunchKernelGGL(im2col_nhwc_vec4, dim3(grid_for(total)), dim3(kBlock), 0, s, x, col, N, Ci, H, W, c, P, Ho,
                        Wo, ldk);
+  } else if (ldk % 4 == 0 && (reinterpret_cast<uintptr_t>(col) & 15) == 0 &&
+             (int64_t)N * Ho * Wo * (ldk / 4) < ((int64_t)1 << 31)) {
+    const int64_t quads = (int64_t)N * Ho * Wo * (ldk / 4);
+    if (x_nchw)
+      hipLaunchKernelGGL(im2col_quad<true>, dim3(grid_for(quads)), dim3(kBlock), 0, s, x,
+                         reinterpret_cast<float4*>(col), N, Ci, H, W, c, P, Ho, Wo, ldk);
+    else
+      hipLaunchKernelGGL(im2col_quad<false>, dim3(grid_for(quads)), dim3(kBlock), 0, s, x,
+                         reinterpret_cast<float4*>(col), N, Ci, H, W, c, P, Ho, Wo, ldk);
   } else {
     const int64_t total = (int64_t)N * Ho * Wo * ldk;
     if (x_nchw)

@@ -134,3 +134,78 @@ def test_bad_configs_are_rejected_on_the_host():
         S.sprint_run(net, good, Wd, None, S.Rule("momentum", 0.1, 0.9), Xd, yd, 2, ws)
     with pytest.raises(S.SgdError):                      # workspace too small
         S.sprint_run(net, good, Wd, Wd.clone(), S.Rule("plain", 0.1), Xd, yd, 2, ws[: ws.numel() // 2])
+
+
+def library_replay(net, log, W0, S0, rule, Xd, yd, N, dev):
+    """The run's schedule replayed on one stream with the library's own sequential calls:
+    sgd_compute_gradient_into for each step's push sum, sgd_accumulate_grad into the worker's
+    buffer, sgd_apply_fused over an update's buffers in worker order.  Deterministic kernels
+    make this bitwise equal to a correct concurrent run: a missing or misplaced wait between
+    the worker and update streams would show up as a difference."""
+    n = net.param_count()
+    W = torch.from_numpy(W0.copy()).to(dev)
+    St = torch.from_numpy(S0.copy()).to(dev)
+    versions = [W.clone()]
+    ws = net.workspace(dev)
+    loss = torch.empty(1, device=dev)
+    U = max(e[5] for e in log) + 1
+    for u in range(U):
+        steps = [e for e in log if e[5] == u]
+        bufs = []
+        for t in sorted({e[0] for e in steps}):
+            buf = S.GradBuf(n, device=dev)
+            mine = [e for e in steps if e[0] == t]
+            for p in sorted({e[2] for e in mine}):
+                push = S.GradBuf(n, device=dev)
+                for e in sorted((e for e in mine if e[2] == p), key=lambda e: e[1]):
+                    b = e[3]
+                    net.compute_gradient_into(versions[e[4]], Xd[b * N:(b + 1) * N], yd[b * N:(b + 1) * N], push,
+                                              loss, ws)
+                S.accumulate_grad(buf, push.data)
+            bufs.append(buf.data)
+        S.apply_fused(W, St, bufs, rule)
+        versions.append(W.clone())
+    torch.cuda.synchronize()
+    return W.cpu().numpy(), St.cpu().numpy()
+
+
+@pytest.mark.parametrize("workers,iters,n_fetch,n_push,min_bufs", [(4, 6, 1, 1, 1), (3, 6, 2, 3, 2)])
+def test_run_is_bitwise_its_own_sequential_replay(workers, iters, n_fetch, n_push, min_bufs):
+    cfg = S.SprintConfig(workers=workers, iters=iters, n_fetch=n_fetch, n_push=n_push, min_bufs=min_bufs)
+    print(f"[sprint] replay {workers} workers x {iters}, fetch {n_fetch}, push {n_push}, min_bufs {min_bufs}",
+          flush=True)
+    stats, log, (X, y, W0), W, V = run(cfg, "momentum", 0.05, 0.9, 7, 90 + workers)
+    check_schedule(log, cfg, 7)
+    dev = torch.device("cuda")
+    net = S.Net((N,) + CHW, LAYERS)
+    Wr, Vr = library_replay(net, log, W0, np.zeros_like(W0), S.Rule("momentum", 0.05, 0.9),
+                            torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev), N, dev)
+    assert np.array_equal(W, Wr) and np.array_equal(V, Vr)
+
+
+def test_full_size_mlp_run_is_bitwise_its_own_sequential_replay():
+    """The MLP-5000 network at full width (115,435,010 parameters), sub-batch 128, four workers:
+    the schedule must be valid and the result bitwise its sequential replay."""
+    wl = workloads.WORKLOADS["mlp5000"].with_batch(128)
+    n_batches = 6
+    X = workloads.uniform01(wl.seed, 0, (n_batches * wl.batch,) + tuple(wl.chw))
+    y = workloads.labels(wl.seed, 1, n_batches * wl.batch, wl.classes)
+    W0 = workloads.he_normal_params(wl.seed, wl.chw, wl.layers)
+    dev = torch.device("cuda")
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    cfg = S.SprintConfig(workers=4, iters=3)
+    print("[sprint] full-size MLP, 4 workers x 3 steps", flush=True)
+    Wd = torch.from_numpy(W0.copy()).to(dev)
+    Vd = torch.zeros_like(Wd)
+    Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+    rule = S.Rule("momentum", 1e-3, 0.9)
+    ws = torch.empty(S.sprint_workspace_bytes(net, cfg), dtype=torch.uint8, device=dev)
+    stats, log = S.sprint_run(net, cfg, Wd, Vd, rule, Xd, yd, n_batches, ws)
+    torch.cuda.synchronize()
+    del ws
+    check_schedule(log, cfg, n_batches)
+    assert stats["steps"] == 12 and stats["updates"] == max(e[5] for e in log) + 1
+    W, V = Wd.cpu().numpy(), Vd.cpu().numpy()
+    assert np.isfinite(W).all() and not np.array_equal(W, W0)
+    Wr, Vr = library_replay(net, log, W0, np.zeros_like(W0), rule, Xd, yd, wl.batch, dev)
+    assert np.array_equal(W, Wr) and np.array_equal(V, Vr)
