@@ -20,6 +20,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
+#include <cstdlib>
 #include <chrono>
 #include <condition_variable>
 #include <memory>
@@ -102,9 +104,18 @@ struct Run {
   int err = 0;
   std::string msg;
 
+  // Failure injection for the error-path tests (environment variable
+  // SGD_SPRINT_INJECT_FAILURE = "w<t>:<step>" or "u:<update>"): the named
+  // worker fails at that step while it holds its buffer lock, or the updater
+  // fails at that update while it holds the weights lock.  -1: off.
+  int inj_worker = -1, inj_step = -1, inj_update = -1;
+
   std::vector<sgd_sprint_contrib> log;  // one per worker step, (worker, iter) order
   std::vector<Clock::time_point> update_done;
 
+  // Records the first error and stops the run.  Takes no lock but emu, so a
+  // thread may call it while it holds a buffer or weights lock; the thread
+  // wakes the others once it has returned and released its locks.
   void fail_with(int e, const std::string& m) {
     {
       std::lock_guard<std::mutex> g(emu);
@@ -114,7 +125,6 @@ struct Run {
       }
     }
     stop = true;
-    wake_all();
   }
   int hip_fail(const char* what) {
     fail_with(SGD_EDEVICE, std::string("sgd_sprint_run: ") + what + " failed");
@@ -136,7 +146,7 @@ struct Run {
 };
 
 // Algorithm 1 for worker t.
-void worker_main(Run& R, int t) {
+void worker_loop(Run& R, int t) {
   if (hipSetDevice(R.device) != hipSuccess) {
     R.hip_fail("hipSetDevice");
     return;
@@ -175,6 +185,8 @@ void worker_main(Run& R, int t) {
       std::unique_lock<std::mutex> lk(buf.mu);
       buf.cv.wait(lk, [&] { return buf.state != BUF_TAKEN || R.stop; });
       if (R.stop) return;
+      if (t == R.inj_worker && i == R.inj_step)
+        return R.fail_with(SGD_EDEVICE, "sgd_sprint_run: injected failure (worker " + std::to_string(t) + ")");
       const bool was_empty = buf.state == BUF_EMPTY;
       if (was_empty) {
         if (buf.released_valid && hipStreamWaitEvent(w.stream, buf.released, 0) != hipSuccess)
@@ -207,7 +219,7 @@ void worker_main(Run& R, int t) {
 
 // Algorithm 2 with one node: SumGradient over the non-empty buffers, then the
 // update of LatestWeights (momentum, when the rule has it, is the rule's state).
-void updater_main(Run& R) {
+void updater_loop(Run& R) {
   if (hipSetDevice(R.device) != hipSuccess) {
     R.hip_fail("hipSetDevice");
     return;
@@ -241,6 +253,7 @@ void updater_main(Run& R) {
     }
     {  // lines 15-20: the new LatestWeights, after any fetch copy still reading the old one
       std::lock_guard<std::mutex> g(R.wmu);
+      if (R.version == R.inj_update) return R.fail_with(SGD_EDEVICE, "sgd_sprint_run: injected failure (updater)");
       for (int t = 0; t < nw; ++t) {
         if (!R.fetch_pending[t]) continue;
         if (hipStreamWaitEvent(R.us, R.workers[t].fetch_done, 0) != hipSuccess) return (void)R.hip_fail("wait");
@@ -266,6 +279,17 @@ void updater_main(Run& R) {
     if (hipStreamSynchronize(R.us) != hipSuccess) return (void)R.hip_fail("update stream synchronize");
     R.update_done.push_back(Clock::now());
   }
+}
+
+// Thread bodies: after a loop returns (its locks released), a stopped run
+// wakes every thread that may wait on a condition variable.
+void worker_main(Run& R, int t) {
+  worker_loop(R, t);
+  if (R.stop) R.wake_all();
+}
+void updater_main(Run& R) {
+  updater_loop(R);
+  if (R.stop) R.wake_all();
 }
 
 int fail(int code, const std::string& m) {
@@ -294,9 +318,10 @@ size_t sgd_sprint_workspace_bytes(const sgd_net* net, const sgd_sprint_config* c
   return (size_t)(per_worker_bytes(net) * cfg->workers);
 }
 
-int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, float* state, const sgd_rule* rule,
-                   const float* X, const int32_t* y, int64_t n_batches, void* ws, size_t ws_bytes, void* stream,
-                   sgd_sprint_stats* stats, sgd_sprint_contrib* log, int64_t log_cap) {
+namespace {
+int sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, float* state, const sgd_rule* rule,
+               const float* X, const int32_t* y, int64_t n_batches, void* ws, size_t ws_bytes, void* stream,
+               sgd_sprint_stats* stats, sgd_sprint_contrib* log, int64_t log_cap) {
   if (int e = check_config(net, cfg)) return e;
   if (!W || !X || !y || !rule) return fail(SGD_EINVAL, "sgd_sprint_run: null pointer");
   if (n_batches < 1) return fail(SGD_EINVAL, "sgd_sprint_run: n_batches must be >= 1");
@@ -318,6 +343,15 @@ int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, f
   R.X = X;
   R.y = y;
   R.n_batches = n_batches;
+  if (const char* inj = std::getenv("SGD_SPRINT_INJECT_FAILURE")) {
+    int a = -1, b = -1;
+    if (std::sscanf(inj, "w%d:%d", &a, &b) == 2) {
+      R.inj_worker = a;
+      R.inj_step = b;
+    } else if (std::sscanf(inj, "u:%d", &a) == 1) {
+      R.inj_update = a;
+    }
+  }
   const sgd_input in = sgd::net_input(net);
   R.batch = in.batch;
   R.x_floats = (int64_t)in.batch * in.channels * in.height * in.width;
@@ -366,9 +400,14 @@ int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, f
   const Clock::time_point t0 = Clock::now();
   if (ok) {
     std::vector<std::thread> threads;
-    threads.reserve(nw + 1);
-    threads.emplace_back(updater_main, std::ref(R));
-    for (int t = 0; t < nw; ++t) threads.emplace_back(worker_main, std::ref(R), t);
+    try {
+      threads.reserve(nw + 1);
+      threads.emplace_back(updater_main, std::ref(R));
+      for (int t = 0; t < nw; ++t) threads.emplace_back(worker_main, std::ref(R), t);
+    } catch (...) {  // no thread could be started: stop the ones that were
+      R.fail_with(SGD_EDEVICE, "sgd_sprint_run: could not start a thread");
+      R.wake_all();
+    }
     for (auto& th : threads) th.join();
     if (R.err && rc == SGD_OK) rc = fail(R.err, R.msg);
   }
@@ -425,4 +464,15 @@ int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, f
   for (hipEvent_t e : {start, end, R.w_ready})
     if (e) (void)hipEventDestroy(e);
   return rc;
+}
+}  // namespace
+
+int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, float* state, const sgd_rule* rule,
+                   const float* X, const int32_t* y, int64_t n_batches, void* ws, size_t ws_bytes, void* stream,
+                   sgd_sprint_stats* stats, sgd_sprint_contrib* log, int64_t log_cap) {
+  try {
+    return sprint_run(net, cfg, W, state, rule, X, y, n_batches, ws, ws_bytes, stream, stats, log, log_cap);
+  } catch (...) {  // host allocation failed before any thread started
+    return fail(SGD_EINVAL, "sgd_sprint_run: out of host memory");
+  }
 }

@@ -209,3 +209,19 @@ def test_full_size_mlp_run_is_bitwise_its_own_sequential_replay():
     assert np.isfinite(W).all() and not np.array_equal(W, W0)
     Wr, Vr = library_replay(net, log, W0, np.zeros_like(W0), rule, Xd, yd, wl.batch, dev)
     assert np.array_equal(W, Wr) and np.array_equal(V, Vr)
+
+
+@pytest.mark.parametrize("where", ["w1:2", "w0:0", "u:1", "u:0"])
+def test_a_failing_thread_stops_the_run_and_leaves_the_library_usable(where, monkeypatch):
+    """A failure forced from the host (SGD_SPRINT_INJECT_FAILURE) in a worker while it holds its buffer
+    lock, or in the updater while it holds the weights lock: the run returns that error (no thread
+    is left waiting), and the next run on the same buffers succeeds."""
+    cfg = S.SprintConfig(workers=3, iters=4)
+    print(f"[sprint] injected failure at {where}", flush=True)
+    monkeypatch.setenv("SGD_SPRINT_INJECT_FAILURE", where)
+    with pytest.raises(S.SgdError, match="injected failure"):
+        run(cfg, "momentum", 0.05, 0.9, 6, 70)
+    monkeypatch.delenv("SGD_SPRINT_INJECT_FAILURE")
+    stats, log, data, W, V = run(cfg, "momentum", 0.05, 0.9, 6, 70)
+    check_schedule(log, cfg, 6)
+    assert np.isfinite(W).all()
