@@ -728,6 +728,16 @@ extern "C" {
 
 const char* sgd_last_error(void) { return sgd::g_error.c_str(); }
 
+// plan() and the launch sequence allocate host vectors; a failed allocation
+// becomes an error code here instead of an exception crossing the C ABI.
+static int plan_guarded(sgd_net* net) {
+  try {
+    return sgd::plan(net);
+  } catch (...) {
+    return fail(SGD_EINVAL, "out of host memory while planning");
+  }
+}
+
 int sgd_create_net(const sgd_input* input, const sgd_layer* layers, int n_layers, int reduction, sgd_net** out) {
   if (!input || !layers || !out) return fail(SGD_EINVAL, "sgd_create_net: null pointer");
   *out = nullptr;
@@ -738,8 +748,13 @@ int sgd_create_net(const sgd_input* input, const sgd_layer* layers, int n_layers
   if (!net) return fail(SGD_EINVAL, "sgd_create_net: out of host memory");
   net->input = *input;
   net->reduction = reduction;
-  net->spec.assign(layers, layers + n_layers);
-  const int rc = sgd::plan(net);
+  try {
+    net->spec.assign(layers, layers + n_layers);
+  } catch (...) {
+    delete net;
+    return fail(SGD_EINVAL, "sgd_create_net: out of host memory");
+  }
+  const int rc = plan_guarded(net);
   if (rc != SGD_OK) {
     delete net;
     return rc;
@@ -797,8 +812,13 @@ static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error from an unrelated earlier call
   sgd::g_prof = &net->prof;
-  int e = sgd::run_forward(net, W, X, y, loss, ws, st);
-  if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, gscale, ws, st);
+  int e = SGD_OK;
+  try {
+    e = sgd::run_forward(net, W, X, y, loss, ws, st);
+    if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, gscale, ws, st);
+  } catch (...) {
+    e = fail(SGD_EINVAL, std::string(who) + ": out of host memory");
+  }
   sgd::g_prof = nullptr;
   return e;
 }
@@ -880,7 +900,7 @@ int sgd_gemm(const sgd_gemm_args* g, void* ws, size_t ws_bytes, void* stream) {
 int sgd_set_implicit_conv(sgd_net* net, int enable) {
   if (!net) return fail(SGD_EINVAL, "sgd_set_implicit_conv: null net");
   net->implicit = enable != 0;
-  return sgd::plan(net);
+  return plan_guarded(net);
 }
 
 int sgd_set_overlap(sgd_net* net, int enable) {
