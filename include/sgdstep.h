@@ -318,7 +318,8 @@ int sgd_set_overlap(sgd_net* net, int enable);
  */
 typedef struct sgd_kernel_time {
   const char* kernel; /* e.g. "gemm_64x128_nt", "im2col", "softmax_ce"     */
-  int layer;          /* index in the layer list, -1 for an inserted stage */
+  int layer;          /* index in the layer list; -1 for an inserted stage
+                         or the one weight-repack launch of all conv layers */
   int phase;          /* 0 forward, 1 backward                              */
   double ms;          /* event-measured duration of the launch              */
   double flops;       /* algorithmic floating-point operations              */

@@ -22,7 +22,7 @@
 // matrices get an out-of-range buffer offset and read zeros.  LDS layouts are
 // XOR-swizzled so the MFMA operand reads are free of bank conflicts:
 //   K-contiguous operand   [row][16], 16-byte quad q of row r stored at
-//                          q ^ ((r>>1 ^ r>>3) & 3)   -> one ds_read_b128 per
+//                          q ^ ((r>>2) & 3)          -> one ds_read_b128 per
 //                          4 MFMAs
 //   row-contiguous operand [k][R], column c of k-row k stored at
 //                          c ^ (32 * ((k>>2) & 1))   -> ds_read_b32, the two
@@ -585,7 +585,7 @@ template <int R>
 struct DmaK {
   static constexpr int SIZE = R * kDmaBK;
   static constexpr int NI = R * (kDmaBK / 4) / 256;  // 16-byte loads per thread per stage
-  __device__ static __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+  __device__ static __forceinline__ int swz(int r) { return (r >> 2) & 3; }
   // Slice at k offset kk of the item; rows >= rvalid and k >= kvalid read zeros.
   __device__ static __forceinline__ void load(i32x4 rs, float* S, uint32_t ld, int rvalid, int kk, int kvalid) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -11,9 +11,17 @@ int im2col(const float* x, bool x_nchw, float* col, int N, int Ci, int H, int W,
            int ldk, hipStream_t s);
 int col2im(const float* dcol, const float* mask_act, float* dx, int N, int Ci, int H, int W, int c, int P, int Ho,
            int Wo, int ldk, hipStream_t s);
-int repack_weight(const float* w, float* wrep, int Co, int Ci, int c, int ldk, hipStream_t s);
-// wdx[ci][(ky*c + kx)*Co + co] = w[co][ci][ky][kx] (the gather-form dedx's B operand).
-int repack_weight_dx(const float* w, float* wdx, int Co, int Ci, int c, hipStream_t s);
+// One conv layer's weights w[Co][Ci][c][c] and the repacked copies made of
+// them: wrep[co][(ky*c + kx)*Ci + ci] in rows of ldk floats (zero padded) and,
+// when wdx is set, wdx[ci][(ky*c + kx)*Co + co] (the gather-form dedx's B
+// operand).  repack_conv_weights makes all of them in one launch.
+struct RepackLayer {
+  const float* w;
+  float* wrep;
+  float* wdx;
+  int Co, Ci, c, ldk;
+};
+int repack_conv_weights(const RepackLayer* layers, int n, hipStream_t s);
 int maxpool_fwd(const float* x, float* y, uint8_t* argmax, int N, int C, int H, int W, int p, bool out_nchw,
                 hipStream_t s);
 int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, float* dx, int N, int C, int H, int W,

@@ -178,32 +178,75 @@ __global__ void col2im_nhwc_scalar(const float* __restrict__ dcol, const float* 
 }
 
 // ------------------------------------------------------- weight repacking ----
-// wrep[co][(ky*c + kx)*Ci + ci] = w[co][ci][ky][kx]; pad columns set to 0.
-__global__ void repack_conv_weight(const float* __restrict__ w, float* __restrict__ wrep, int Co, int Ci, int c,
-                                   int ldk) {
-  const int K = c * c * Ci;
-  const int64_t total = (int64_t)Co * ldk;
-  GRID_STRIDE(i, total) {
-    const int co = (int)(i / ldk), kk = (int)(i - (int64_t)co * ldk);
-    float v = 0.f;
-    if (kk < K) {
-      const int tap = kk / Ci, ci = kk - tap * Ci;
-      v = w[((int64_t)co * Ci + ci) * c * c + tap];
-    }
-    wrep[i] = v;
-  }
-}
+// Every conv layer's weights W[co][ci][ky][kx] are copied, once per step and
+// in one launch for all layers, to
+//   W'[co][(ky*c + kx)*Ci + ci]   rows of ldk floats, zero past c*c*Ci: the B
+//                                 operand of the forward product (and of the
+//                                 explicit dCol product), im2col's column order
+//   W''[ci][(ky*c + kx)*Co + co]  the B operand of the gather-form dedx
+//                                 product (each input pixel gathers its c*c
+//                                 taps of the output gradient, Co channels each)
+// The per-layer copies are small and latency-bound, so one launch replaces
+// two per layer.  W'' is a transpose (neighbouring outputs come from sources
+// Ci*c*c floats apart), so each block stages a tile of cot output channels x
+// cit input channels x c*c taps in LDS: the tile is read as cot contiguous
+// runs of cit*c*c floats and written as runs of cit floats (W') and cot
+// floats (W'').  Blocks are numbered job by job.
+constexpr int kMaxRepackJobs = 32;
+constexpr int kRepackLds = 12800;  // floats of staged tile: cot * (cit*c*c + 1)
+struct RepackJob {
+  const float* w;
+  float* wrep;
+  float* wdx;        // nullptr: no W''
+  int Co, Ci, c, ldk;
+  int cot, cit;      // tile: output x input channels
+  int tiles_ci;      // tiles along Ci
+  int block0;        // first block of this job
+};
+struct RepackJobs {
+  RepackJob j[kMaxRepackJobs];
+  int n;
+};
 
-// W''[ci][(ky*c + kx)*Co + co] = W[co][ci][ky][kx]: the B operand of the
-// gather-form dedx product (each input pixel gathers its c*c taps of the
-// output gradient, Co channels each, against these rows).
-__global__ void repack_conv_weight_dx(const float* __restrict__ w, float* __restrict__ wdx, int Co, int Ci, int c) {
-  const int64_t ldk = (int64_t)c * c * Co;
-  const int64_t total = (int64_t)Ci * ldk;
-  GRID_STRIDE(i, total) {
-    const int ci = (int)(i / ldk), kk = (int)(i - (int64_t)ci * ldk);
-    const int tap = kk / Co, co = kk - tap * Co;
-    wdx[i] = w[((int64_t)co * Ci + ci) * c * c + tap];
+__global__ __launch_bounds__(kBlock) void repack_conv_weights_kernel(RepackJobs J) {
+  __shared__ float T[kRepackLds];
+  int l = 0;
+  while (l + 1 < J.n && J.j[l + 1].block0 <= (int)blockIdx.x) ++l;
+  const RepackJob b = J.j[l];
+  const int bi = (int)blockIdx.x - b.block0;
+  const int tco = bi / b.tiles_ci, tci = bi - tco * b.tiles_ci;
+  const int co0 = tco * b.cot, ci0 = tci * b.cit;
+  const int cc = b.c * b.c;
+  const int nco = min(b.cot, b.Co - co0), nci = min(b.cit, b.Ci - ci0);
+  const int seg = nci * cc;           // floats of one output channel in the tile
+  const int ld = b.cit * cc + 1;      // LDS row stride (odd: reads along co are conflict-free)
+  // T[co][ci*cc + tap] = W[co0 + co][ci0 + ci][tap]: one contiguous run per row.
+  for (int t = threadIdx.x; t < nco * seg; t += kBlock) {
+    const int co = t / seg, r = t - co * seg;
+    T[co * ld + r] = b.w[((int64_t)(co0 + co) * b.Ci + ci0) * cc + r];
+  }
+  __syncthreads();
+  // W'[co][tap*Ci + ci0 + ci]: runs of nci floats.
+  for (int t = threadIdx.x; t < nco * cc * nci; t += kBlock) {
+    const int r = t / nci, ci = t - r * nci;
+    const int co = r / cc, tap = r - co * cc;
+    b.wrep[(int64_t)(co0 + co) * b.ldk + tap * b.Ci + ci0 + ci] = T[co * ld + ci * cc + tap];
+  }
+  // The zero columns [c*c*Ci, ldk) of W' rows, written by the last tile along Ci.
+  if (tci == b.tiles_ci - 1) {
+    const int pad = b.ldk - cc * b.Ci;
+    for (int t = threadIdx.x; t < nco * pad; t += kBlock) {
+      const int co = t / pad, q = t - co * pad;
+      b.wrep[(int64_t)(co0 + co) * b.ldk + cc * b.Ci + q] = 0.f;
+    }
+  }
+  // W''[ci0 + ci][tap*Co + co0 + co]: runs of nco floats.
+  if (b.wdx) {
+    for (int t = threadIdx.x; t < nci * cc * nco; t += kBlock) {
+      const int r = t / nco, co = t - r * nco;
+      const int ci = r / cc, tap = r - ci * cc;
+      b.wdx[(int64_t)(ci0 + ci) * cc * b.Co + (int64_t)tap * b.Co + co0 + co] = T[co * ld + ci * cc + tap];
+    }
   }
 }
 
@@ -453,20 +496,50 @@ int col2im(const float* dcol, const float* mask_act, float* dx, int N, int Ci, i
   return check_launch("col2im");
 }
 
-int repack_weight(const float* w, float* wrep, int Co, int Ci, int c, int ldk, hipStream_t s) {
-  prof_begin("repack_weight", 0, 4.0 * ((double)Co * c * c * Ci + (double)Co * ldk), s);
-  hipLaunchKernelGGL(repack_conv_weight, dim3(grid_for((int64_t)Co * ldk)), dim3(kBlock), 0, s, w, wrep, Co, Ci, c,
-                     ldk);
-  prof_end(s);
-  return check_launch("repack_weight");
-}
-
-int repack_weight_dx(const float* w, float* wdx, int Co, int Ci, int c, hipStream_t s) {
-  const int64_t total = (int64_t)Ci * c * c * Co;
-  prof_begin("repack_weight_dx", 0, 8.0 * (double)total, s);
-  hipLaunchKernelGGL(repack_conv_weight_dx, dim3(grid_for(total)), dim3(kBlock), 0, s, w, wdx, Co, Ci, c);
-  prof_end(s);
-  return check_launch("repack_weight_dx");
+int repack_conv_weights(const RepackLayer* layers, int n, hipStream_t s) {
+  RepackJobs J{};
+  int blocks = 0;
+  double bytes = 0.0;
+  auto flush = [&]() -> int {
+    if (J.n == 0) return 0;
+    prof_begin("repack_weights", 0, bytes, s);
+    hipLaunchKernelGGL(repack_conv_weights_kernel, dim3(blocks), dim3(kBlock), 0, s, J);
+    prof_end(s);
+    J = RepackJobs{};
+    blocks = 0;
+    bytes = 0.0;
+    return check_launch("repack_conv_weights");
+  };
+  for (int i = 0; i < n; ++i) {
+    const RepackLayer& L = layers[i];
+    const int cc = L.c * L.c;
+    if (cc + 1 > kRepackLds) {
+      set_error("repack_conv_weights: filter too large for the staged repack");
+      return SGD_EUNSUPPORTED;
+    }
+    // Largest tile with cot <= 32 and cit <= 16 whose staging fits.
+    const int cit = std::max(1, std::min(16, (kRepackLds / 32 - 1) / cc));
+    const int cot = std::max(1, std::min(32, kRepackLds / (cit * cc + 1)));
+    const int64_t tiles = ceil_div(L.Co, cot) * ceil_div(L.Ci, cit);
+    if (J.n == kMaxRepackJobs || blocks + tiles > INT32_MAX / 2)
+      if (int e = flush()) return e;
+    RepackJob& b = J.j[J.n++];
+    b.w = L.w;
+    b.wrep = L.wrep;
+    b.wdx = L.wdx;
+    b.Co = L.Co;
+    b.Ci = L.Ci;
+    b.c = L.c;
+    b.ldk = L.ldk;
+    b.cot = cot;
+    b.cit = cit;
+    b.tiles_ci = (int)ceil_div(L.Ci, cit);
+    b.block0 = blocks;
+    blocks += (int)tiles;
+    const double wfl = (double)L.Co * L.Ci * cc;
+    bytes += 4.0 * (wfl + (double)L.Co * L.ldk + (L.wdx ? wfl : 0.0));
+  }
+  return flush();
 }
 
 namespace {

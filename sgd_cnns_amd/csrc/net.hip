@@ -476,16 +476,24 @@ ConvGather conv_gather(const float* src, int rh, int rw, int sh, int sw, int sc,
 int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y, float* loss, void* ws,
                 hipStream_t st) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
+  // Every conv layer's repacked weights, in one launch before the first
+  // product.  The dedx operands are made from the same weights the forward
+  // pass uses (the fused training step updates W during the backward pass).
+  std::vector<RepackLayer> rep;
+  for (const Stage& s : net->stages)
+    if (s.kind == SGD_CONV)
+      rep.push_back({Wt + s.w_off, at<float>(ws, s.wrep), s.implicit_dx ? at<float>(ws, s.wdx) : nullptr, s.Co, s.Ci,
+                     s.c, s.ldk});
+  if (!rep.empty()) {
+    prof_set_layer(-1, 0);
+    if (int e = repack_conv_weights(rep.data(), (int)rep.size(), st)) return e;
+  }
   for (Stage& s : net->stages) {
     const float* xin = input_of(net, s, ws, X);
     int e = 0;
     prof_set_layer(s.spec, 0);
     if (s.kind == SGD_CONV) {
       float* wrep = at<float>(ws, s.wrep);
-      if ((e = repack_weight(Wt + s.w_off, wrep, s.Co, s.Ci, s.c, s.ldk, st))) return e;
-      // the dedx operand is repacked from the weights the forward pass uses
-      // (the fused training step updates W during the backward pass)
-      if (s.implicit_dx && (e = repack_weight_dx(Wt + s.w_off, at<float>(ws, s.wdx), s.Co, s.Ci, s.c, st))) return e;
       GemmDesc g{};
       if (s.implicit) {
         g.gather = 1;

@@ -7,10 +7,17 @@
 // (SPRINT Algorithm 2's SumGradient order); k = 0 is an empty GradBuf, i.e.
 // a zero gradient.
 //
-// Each thread handles two float4 groups per iteration (16-byte loads and
-// stores, all issued before the arithmetic so more bytes are in flight); the
-// data are streamed with non-temporal loads and stores, since every byte is
-// touched once.  A scalar path covers misaligned pointers and the n % 4 tail.
+// Memory shape (measured on MI355X with 8 gradient buffers + W + A, the
+// parameter-server Adagrad apply): a block of 256 threads owns 1024
+// consecutive float4 groups, i.e. 16 KiB of every stream, and each thread
+// issues all of its loads -- 4 groups of every gradient buffer, W and the
+// optimiser state -- before the first addition.  The number of buffers is a
+// template parameter so the compiler can keep every load in flight; with a
+// run-time count the loads of buffer j+1 wait for the sum of buffer j and the
+// kernel ran at 70% of HBM peak instead of 75%.  Loads and stores are
+// non-temporal: every byte is touched once.  Groups past the end re-read
+// group 0 and store nothing; the last block's first n % 4 threads do the
+// scalar tail.  Misaligned pointers take a scalar kernel.
 #include "common.h"
 #include "layers.h"
 #include "rules.h"
@@ -20,7 +27,9 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kBlock = 256;
-constexpr int kUnroll = 2;
+constexpr int kGroups = 4;                      // float4 groups per thread
+constexpr int kChunk = kBlock * kGroups;        // float4 groups per block
+constexpr int kMaxUnrolledK = 8;                // K above this: run-time loop
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -35,85 +44,128 @@ __device__ __forceinline__ void st4(float* p, int64_t i, v4f v) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p) + i);
 }
 
-// Left fold g_0 + g_1 + ... + g_{k-1} (k >= 1), one rounding per addition.
-__device__ __forceinline__ v4f fold4(const Ptrs& P, int k, int64_t i) {
-  v4f s = ld4(P.g[0], i);
-  for (int j = 1; j < k; ++j) s = s + ld4(P.g[j], i);
-  return s;
+// s[u] = x[u] + g_{j0}[u] + ... + g_{k-1}[u] for the thread's groups idx[u],
+// one rounding per addition, left to right.  K > 0: exactly K buffers
+// (k == K), every load issued before the first addition; K < 0: k buffers,
+// loaded one buffer at a time.  `init` says whether s already holds x (else
+// s starts as g_{j0}).
+template <int K>
+__device__ __forceinline__ void fold_groups(v4f (&s)[kGroups], const Ptrs& P, int j0, int k, bool init,
+                                            const int64_t (&idx)[kGroups]) {
+  if constexpr (K > 0) {
+    v4f g[K][kGroups];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) g[j][u] = ld4(P.g[j], idx[u]);
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      v4f acc = init ? s[u] + g[0][u] : g[0][u];
+#pragma unroll
+      for (int j = 1; j < K; ++j) acc = acc + g[j][u];
+      s[u] = acc;
+    }
+  } else {
+    for (int j = j0; j < k; ++j) {
+      v4f g[kGroups];
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) g[u] = ld4(P.g[j], idx[u]);
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) s[u] = (init || j > j0) ? s[u] + g[u] : g[u];
+    }
+  }
 }
-__device__ __forceinline__ float fold1(const Ptrs& P, int k, int64_t i) {
-  float s = P.g[0][i];
-  for (int j = 1; j < k; ++j) s = s + P.g[j][i];
+
+// Scalar left fold of the buffers j0..k-1 at element i onto s.
+__device__ __forceinline__ float fold1(const Ptrs& P, int j0, int k, float s, int64_t i) {
+  for (int j = j0; j < k; ++j) s = s + P.g[j][i];
   return s;
 }
 
-// buf = (first_is_copy ? g_0 : buf + g_0) + g_1 + ... + g_{k-1}, left to right.
-__global__ void accumulate_kernel(float* __restrict__ buf, Ptrs P, int k, int first_is_copy, int64_t n, int vec) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t done = 0;
-  if (vec) {
-    const int64_t n4 = n / 4;
-    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
-      v4f s[kUnroll];
+// buf = (COPY ? g_0 : buf + g_0) + g_1 + ... + g_{k-1}, left to right.
+template <int K, bool COPY>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(float* __restrict__ buf, Ptrs P, int k, int64_t n) {
+  const int64_t n4 = n / 4;
+  if (n4 > 0) {
+    int64_t idx[kGroups], ld[kGroups];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) s[u] = first_is_copy ? ld4(P.g[0], i + u * stride) : ld4(buf, i + u * stride);
-      for (int j = first_is_copy ? 1 : 0; j < k; ++j)
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) s[u] = s[u] + ld4(P.g[j], i + u * stride);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) st4(buf, i + u * stride, s[u]);
+    for (int u = 0; u < kGroups; ++u) {
+      idx[u] = (int64_t)blockIdx.x * kChunk + u * kBlock + threadIdx.x;
+      ld[u] = idx[u] < n4 ? idx[u] : 0;
     }
-    for (; i < n4; i += stride) {
-      v4f s = first_is_copy ? ld4(P.g[0], i) : ld4(buf, i);
-      for (int j = first_is_copy ? 1 : 0; j < k; ++j) s = s + ld4(P.g[j], i);
-      st4(buf, i, s);
+    v4f s[kGroups];
+    if (!COPY) {
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) s[u] = ld4(buf, ld[u]);
     }
-    done = n4 * 4;
-    i = done + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    fold_groups<K>(s, P, 0, k, !COPY, ld);
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u)
+      if (idx[u] < n4) st4(buf, idx[u], s[u]);
   }
-  for (; i < n; i += stride) {
-    float s = first_is_copy ? P.g[0][i] : buf[i];
-    for (int j = first_is_copy ? 1 : 0; j < k; ++j) s = s + P.g[j][i];
-    buf[i] = s;
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - 4 * n4) {
+    const int64_t i = 4 * n4 + threadIdx.x;
+    buf[i] = COPY ? fold1(P, 1, k, P.g[0][i], i) : fold1(P, 0, k, buf[i], i);
+  }
+}
+
+// The same for pointers that are not 16-byte aligned: one element per thread.
+__global__ void accumulate_scalar_kernel(float* __restrict__ buf, Ptrs P, int k, int first_is_copy, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    buf[i] = first_is_copy ? fold1(P, 1, k, P.g[0][i], i) : fold1(P, 0, k, buf[i], i);
+}
+
+// W (and state) <- RULE(W, state, g_0 + ... + g_{k-1}); k = 0 is a zero
+// gradient.  K as for fold_groups, 0 for no buffers.
+template <int RULE, int K>
+__global__ __launch_bounds__(kBlock) void apply_kernel(float* __restrict__ W, float* __restrict__ state, Ptrs P,
+                                                       int k, int64_t n, float eta, float mu, float eps,
+                                                       float decay) {
+  constexpr bool kState = RULE != SGD_PLAIN;
+  const int64_t n4 = n / 4;
+  if (n4 > 0) {
+    int64_t idx[kGroups], ld[kGroups];
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      idx[u] = (int64_t)blockIdx.x * kChunk + u * kBlock + threadIdx.x;
+      ld[u] = idx[u] < n4 ? idx[u] : 0;
+    }
+    v4f w[kGroups], st[kGroups], g[kGroups];
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      w[u] = ld4(W, ld[u]);
+      st[u] = kState ? ld4(state, ld[u]) : v4f{0.f, 0.f, 0.f, 0.f};
+      g[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (K != 0) fold_groups<K>(g, P, 0, k, false, ld);
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      rule1<RULE>(w[u], st[u], g[u], eta, mu, eps, decay);
+      if (idx[u] < n4) {
+        st4(W, idx[u], w[u]);
+        if (kState) st4(state, idx[u], st[u]);
+      }
+    }
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x < n - 4 * n4) {
+    const int64_t i = 4 * n4 + threadIdx.x;
+    const float g = k > 0 ? fold1(P, 1, k, P.g[0][i], i) : 0.f;
+    float w = W[i];
+    float st = kState ? state[i] : 0.f;
+    rule1<RULE>(w, st, g, eta, mu, eps, decay);
+    W[i] = w;
+    if (kState) state[i] = st;
   }
 }
 
 template <int RULE>
-__global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, Ptrs P, int k, int64_t n, float eta,
-                             float mu, float eps, float decay, int vec) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void apply_scalar_kernel(float* __restrict__ W, float* __restrict__ state, Ptrs P, int k, int64_t n,
+                                    float eta, float mu, float eps, float decay) {
   constexpr bool kState = RULE != SGD_PLAIN;
-  if (vec) {
-    const int64_t n4 = n / 4;
-    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
-      v4f w[kUnroll], st[kUnroll], g[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        g[u] = k > 0 ? fold4(P, k, i + u * stride) : v4f{0.f, 0.f, 0.f, 0.f};
-        w[u] = ld4(W, i + u * stride);
-        st[u] = kState ? ld4(state, i + u * stride) : v4f{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        rule1<RULE>(w[u], st[u], g[u], eta, mu, eps, decay);
-        st4(W, i + u * stride, w[u]);
-        if (kState) st4(state, i + u * stride, st[u]);
-      }
-    }
-    for (; i < n4; i += stride) {
-      v4f g = k > 0 ? fold4(P, k, i) : v4f{0.f, 0.f, 0.f, 0.f};
-      v4f w = ld4(W, i);
-      v4f st = kState ? ld4(state, i) : v4f{0.f, 0.f, 0.f, 0.f};
-      rule1<RULE>(w, st, g, eta, mu, eps, decay);
-      st4(W, i, w);
-      if (kState) st4(state, i, st);
-    }
-    i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  }
-  for (; i < n; i += stride) {
-    const float g = k > 0 ? fold1(P, k, i) : 0.f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float g = k > 0 ? fold1(P, 1, k, P.g[0][i], i) : 0.f;
     float w = W[i];
     float st = kState ? state[i] : 0.f;
     rule1<RULE>(w, st, g, eta, mu, eps, decay);
@@ -124,16 +176,48 @@ __global__ void apply_kernel(float* __restrict__ W, float* __restrict__ state, P
 
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// About one unrolled iteration per thread: many waves in flight per CU hide
-// HBM latency better than a few long-running ones.
-int grid_for(int64_t n) {
-  const int64_t want = ceil_div(ceil_div(n, 4), (int64_t)kBlock * kUnroll);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, 1 << 16));
+int vec_grid(int64_t n) { return (int)std::max<int64_t>(1, ceil_div(n / 4, kChunk)); }
+int scalar_grid(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, kBlock), 1 << 16)); }
+
+// Calls f(std::integral_constant<int, K>) with K = k for k <= 8, else K = -1.
+template <typename F>
+void with_k(int k, F&& f) {
+  switch (k) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 5: f(std::integral_constant<int, 5>{}); break;
+    case 6: f(std::integral_constant<int, 6>{}); break;
+    case 7: f(std::integral_constant<int, 7>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    default: f(std::integral_constant<int, -1>{}); break;
+  }
+  static_assert(kMaxUnrolledK == 8, "with_k unrolls k up to 8");
+}
+
+template <int RULE>
+void launch_apply(bool vec, float* W, float* state, const Ptrs& P, int k, int64_t n, float eta, float mu, float eps,
+                  float decay, hipStream_t s) {
+  if (!vec) {
+    hipLaunchKernelGGL(apply_scalar_kernel<RULE>, dim3(scalar_grid(n)), dim3(kBlock), 0, s, W, state, P, k, n, eta,
+                       mu, eps, decay);
+    return;
+  }
+  with_k(k, [&](auto K) {
+    hipLaunchKernelGGL((apply_kernel<RULE, decltype(K)::value>), dim3(vec_grid(n)), dim3(kBlock), 0, s, W, state, P,
+                       k, n, eta, mu, eps, decay);
+  });
 }
 
 }  // namespace
 
 int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy, int64_t n, hipStream_t s) {
+  if (k < 1 || k > kMaxK) {
+    set_error("accumulate: k must be in 1..16");
+    return SGD_EINVAL;
+  }
   Ptrs P{};
   bool vec = a16(buf);
   for (int j = 0; j < k; ++j) {
@@ -143,37 +227,44 @@ int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy,
   const double streams = k + (first_is_copy ? 1 : 2);
   prof_begin(first_is_copy ? "accumulate_copy" : "accumulate_add", (double)(k - (first_is_copy ? 1 : 0)) * n,
              4.0 * streams * n, s);
-  hipLaunchKernelGGL(accumulate_kernel, dim3(grid_for(n)), dim3(kBlock), 0, s, buf, P, k, (int)first_is_copy, n,
-                     (int)vec);
+  if (!vec) {
+    hipLaunchKernelGGL(accumulate_scalar_kernel, dim3(scalar_grid(n)), dim3(kBlock), 0, s, buf, P, k,
+                       (int)first_is_copy, n);
+  } else {
+    with_k(k, [&](auto K) {
+      constexpr int KK = decltype(K)::value;
+      if constexpr (KK != 0) {
+        if (first_is_copy)
+          hipLaunchKernelGGL((accumulate_kernel<KK, true>), dim3(vec_grid(n)), dim3(kBlock), 0, s, buf, P, k, n);
+        else
+          hipLaunchKernelGGL((accumulate_kernel<KK, false>), dim3(vec_grid(n)), dim3(kBlock), 0, s, buf, P, k, n);
+      }
+    });
+  }
   prof_end(s);
   return check_launch("accumulate");
 }
 
 int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t n, int rule, float eta, float mu,
                float eps, float decay, hipStream_t s) {
+  if (k < 0 || k > kMaxK) {
+    set_error("apply_rule: k must be in 0..16");
+    return SGD_EINVAL;
+  }
   Ptrs P{};
   bool vec = a16(W) && (rule == SGD_PLAIN || a16(state));
   for (int j = 0; j < k; ++j) {
     P.g[j] = grads[j];
     vec = vec && a16(grads[j]);
   }
-  const dim3 g(grid_for(n)), b(kBlock);
   static const char* const names[4] = {"apply_plain", "apply_momentum", "apply_adagrad", "apply_nesterov"};
   const double streams = k + (rule == SGD_PLAIN ? 2 : 4);
   prof_begin(names[rule], (double)n * (k + 4), 4.0 * streams * n, s);
   switch (rule) {
-    case SGD_PLAIN:
-      hipLaunchKernelGGL(apply_kernel<SGD_PLAIN>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
-      break;
-    case SGD_MOMENTUM:
-      hipLaunchKernelGGL(apply_kernel<SGD_MOMENTUM>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
-      break;
-    case SGD_NESTEROV:
-      hipLaunchKernelGGL(apply_kernel<SGD_NESTEROV>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
-      break;
-    default:
-      hipLaunchKernelGGL(apply_kernel<SGD_ADAGRAD>, g, b, 0, s, W, state, P, k, n, eta, mu, eps, decay, (int)vec);
-      break;
+    case SGD_PLAIN: launch_apply<SGD_PLAIN>(vec, W, state, P, k, n, eta, mu, eps, decay, s); break;
+    case SGD_MOMENTUM: launch_apply<SGD_MOMENTUM>(vec, W, state, P, k, n, eta, mu, eps, decay, s); break;
+    case SGD_NESTEROV: launch_apply<SGD_NESTEROV>(vec, W, state, P, k, n, eta, mu, eps, decay, s); break;
+    default: launch_apply<SGD_ADAGRAD>(vec, W, state, P, k, n, eta, mu, eps, decay, s); break;
   }
   prof_end(s);
   return check_launch("apply_rule");
