@@ -187,6 +187,12 @@ struct sgd_net {
   // stream (they run concurrently).
   int64_t partial_off = 0, partial_floats = 0;
   int64_t partial_dw_off = 0, partial_dw_floats = 0;
+  // Scratch the first weighted layer's dedw product needs.  That product runs
+  // on the caller's stream (in the caller's-stream buffer, which is at least
+  // this large) when the overlap is on, after the last dedx product, next to
+  // the side stream's remaining dedw products; it is planned with this
+  // capacity in both modes, so its schedule and sum order do not change.
+  int64_t first_dw_floats = 0;
   // dCol of the conv dedx products (dedw reads Col concurrently).
   int64_t dcol_off = 0;
   sgd::Profiler prof;
@@ -363,7 +369,7 @@ int plan(sgd_net* net) {
 
   // Workspace layout and product split factors.
   Bump b;
-  int64_t partial = 0, partial_dw = 0, dcol = 0;
+  int64_t partial = 0, partial_dw = 0, dcol = 0, first_dw = 0;
   for (Stage& s : st) {
     const int64_t N = s.N;
     if (s.kind == SGD_CONV) {
@@ -381,8 +387,11 @@ int plan(sgd_net* net) {
       s.split_dw = gemm_pick_splits(s.Co, s.ldk + 1, (int)P);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)P, s.ldk, s.Co);
       partial = std::max(partial, gemm_scratch_floats((int)P, s.Co, s.ldk, false, false, false, s.split_fwd));
-      for (bool fused : {false, true})
-        partial_dw = std::max(partial_dw, gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw));
+      for (bool fused : {false, true}) {
+        const int64_t need = gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw);
+        partial_dw = std::max(partial_dw, need);
+        if (s.first_weighted) first_dw = std::max(first_dw, need);
+      }
       if (s.implicit_dx) {
         partial = std::max(partial, gemm_scratch_floats((int)Pin, s.Ci, s.c * s.c * s.Co, false, false, false, 1));
       } else if (!s.first_weighted) {
@@ -407,8 +416,11 @@ int plan(sgd_net* net) {
       s.split_dw = gemm_pick_splits(s.Co, s.Ci + 1, (int)N);
       s.split_dx = s.first_weighted ? 1 : gemm_pick_splits((int)N, s.Ci, s.Co);
       partial = std::max(partial, gemm_scratch_floats((int)N, s.Co, s.Ci, false, false, false, s.split_fwd));
-      for (bool fused : {false, true})
-        partial_dw = std::max(partial_dw, gemm_scratch_floats(s.Co, s.Ci + 1, (int)N, true, true, fused, s.split_dw));
+      for (bool fused : {false, true}) {
+        const int64_t need = gemm_scratch_floats(s.Co, s.Ci + 1, (int)N, true, true, fused, s.split_dw);
+        partial_dw = std::max(partial_dw, need);
+        if (s.first_weighted) first_dw = std::max(first_dw, need);
+      }
       if (!s.first_weighted)
         partial = std::max(partial, gemm_scratch_floats((int)N, s.Ci, s.Co, false, true, false, s.split_dx));
     } else if (s.kind == SGD_SOFTMAX_CE) {
@@ -418,6 +430,8 @@ int plan(sgd_net* net) {
       s.dout = st[s.input].dout;
     }
   }
+  partial = std::max(partial, first_dw);
+  net->first_dw_floats = first_dw;
   net->partial_floats = partial;
   net->partial_off = b.take(4 * std::max<int64_t>(partial, 1));
   net->partial_dw_floats = partial_dw;
@@ -555,10 +569,12 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
 // dedx product, which reads that layer's weights, runs before its dedw (a
 // conv layer's dedx reads the repacked copy W').
 //
-// Every dedw product runs on the side stream, forked from the caller's
-// stream once its inputs (the layer's output gradient, and the input
-// activation or Col from the forward pass) are final and, for an fc layer,
-// after the dedx product that reads W.  Nothing on the caller's stream
+// Every dedw product but the first weighted layer's runs on the side stream,
+// forked from the caller's stream once its inputs (the layer's output
+// gradient, and the input activation or Col from the forward pass) are final
+// and, for an fc layer, after the dedx product that reads W.  The first
+// weighted layer has no dedx product, so its dedw runs on the caller's
+// stream (which has nothing else left to do) next to the side stream's tail.  Nothing on the caller's stream
 // writes what a dedw product reads or reads what it writes, and the caller's
 // stream joins the side stream at the end, so the step stays one stream-
 // ordered operation for the caller.
@@ -579,6 +595,20 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
     if (hipEventRecord(ev, st) != hipSuccess || hipStreamWaitEvent(side, ev, 0) != hipSuccess)
       return fail(SGD_EDEVICE, "backward: fork to the side stream failed");
     return 0;
+  };
+  // A dedw product on the side stream (forked once its inputs are final),
+  // except the first weighted layer's: nothing follows it on the caller's
+  // stream, so it runs there, concurrently with the side stream's last ones.
+  auto launch_dw = [&](GemmDesc& g, const Stage& s) -> int {
+    if (s.first_weighted) {
+      g.partial = net->overlap ? partial : partial_dw;
+      g.partial_floats = net->first_dw_floats;
+      return gemm(g, st);
+    }
+    g.partial = partial_dw;
+    g.partial_floats = net->partial_dw_floats;
+    if (int e = fork()) return e;
+    return gemm(g, side);
   };
   int e = 0;
   for (int si = (int)stages.size() - 1; si >= 0 && !e; --si) {
@@ -623,13 +653,11 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.K = s.N;
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
-      g.partial = partial_dw;
-      g.partial_floats = net->partial_dw_floats;
       g.ones_out = grad + s.b_off;
       g.accum = accum;
       g.gscale = gscale;
       set_update(g, rule, state, s);
-      if ((e = fork()) || (e = gemm(g, side))) continue;
+      if ((e = launch_dw(g, s))) continue;
     } else if (s.kind == SGD_MAXPOOL) {
       const Stage& src = stages[s.input];
       const float* pooled = src.relu ? at<float>(ws, s.out) : nullptr;
@@ -659,8 +687,6 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.flops = 2.0 * s.Co * (double)s.K * (double)P;
       g.epi = EPI_STORE;
       g.splits = s.split_dw;
-      g.partial = partial_dw;
-      g.partial_floats = net->partial_dw_floats;
       g.perm_c = s.c;
       g.perm_ci = s.Ci;
       g.perm_k = s.K;
@@ -668,7 +694,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.accum = accum;
       g.gscale = gscale;
       set_update(g, rule, state, s);
-      if ((e = fork()) || (e = gemm(g, side))) continue;
+      if ((e = launch_dw(g, s))) continue;
       if (s.implicit_dx) {
         // dedx_conv as one gather-form product: each input pixel gathers its
         // c*c taps of dout (flipped offsets) against W''; the ReLU mask of
