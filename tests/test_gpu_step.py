@@ -71,6 +71,13 @@ def test_cnn_unpooled_conv_into_fc_and_sum_reduction():
     check((2, 9, 7), layers, 5, 102, 5, x_dist="normal", reduce_sum=True)
 
 
+def test_large_filter_conv_repack_tiles():
+    # a 21x21 conv after a 16-channel one: the weight repack stages 28 output x 1 input channel per tile
+    # (two output-channel tiles, 28 + 4), and the layer takes the gathered forward, dedw and dedx products
+    layers = [("conv", 16, 3, 1), ("relu",), ("conv", 32, 21, 0), ("relu",), ("fc", 7), ("softmax_ce",)]
+    check((3, 22, 22), layers, 2, 106, 7, x_dist="normal")
+
+
 def test_mlp_ragged_tiles():
     layers = [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)]
     check((3072, 1, 1), layers, 70, 103, 10)

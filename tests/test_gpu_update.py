@@ -199,3 +199,39 @@ def test_empty_gradbuf_with_decay_matches_oracle(rule):
     assert not np.array_equal(Wr, W0)
     if rule != "plain":
         np.testing.assert_array_equal(Vd.cpu().numpy(), Vr)
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 4096, 4100, 262147])
+@pytest.mark.parametrize("k", [1, 5, 9, 16])
+def test_k_buffer_fold_and_apply_shapes(n, k):
+    """Every buffer count (unrolled up to 8, a run-time loop above), sizes below one float4 group,
+    exactly one block's 4096 floats, a tail past it, and a fold into a non-empty GradBuf."""
+    print(f"[update] k={k} n={n}", flush=True)
+    gs = [workloads.normal(14, 100 + j, n, 1e-3) for j in range(k)]
+    g0 = workloads.normal(14, 99, n, 1e-3)
+    W0 = workloads.normal(14, 2, n)
+    A0 = np.abs(workloads.normal(14, 3, n)) + np.float32(0.1)
+    gds = [dev(g) for g in gs]
+    # oracle: g0 first (non-empty buffer), then the k buffers in order
+    ob = O.GradBuf(n)
+    ob.accumulate(g0)
+    for g in gs:
+        ob.accumulate(g)
+    of = O.GradBuf(n)
+    for g in gs:
+        of.accumulate(g)
+    Wr, Ar = W0.copy(), A0.copy()
+    O.apply_rule("adagrad", Wr, Ar, of.data, 0.01, 0.0, 1e-8)
+    # GPU: one fold into a non-empty buffer, one into an empty one, and the fused apply
+    gb = S.GradBuf(n)
+    S.accumulate_grad(gb, dev(g0))
+    S.accumulate_grads(gb, gds)
+    ge = S.GradBuf(n)
+    S.accumulate_grads(ge, gds)
+    Wd, Ad = dev(W0), dev(A0)
+    S.apply_fused(Wd, Ad, gds, S.Rule("adagrad", 0.01, 0.0, 1e-8))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gb.data.cpu().numpy(), ob.data)
+    np.testing.assert_array_equal(ge.data.cpu().numpy(), of.data)
+    np.testing.assert_array_equal(Wd.cpu().numpy(), Wr)
+    np.testing.assert_array_equal(Ad.cpu().numpy(), Ar)
