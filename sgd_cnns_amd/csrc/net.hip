@@ -152,6 +152,12 @@ struct Stage {
   int input = -1; // producing stage, -1 = the images
   bool relu = false;
   bool first_weighted = false;
+  int weighted_rank = -1;  // 0 for the first weighted layer, 1 for the next, ...
+  // With the overlap on, this layer's dedw runs on the caller's stream after
+  // its dedx (see run_backward), in the caller's-stream scratch, planned with
+  // capacity dw_cap in both modes so its schedule does not change.
+  bool dw_main = false;
+  int64_t dw_cap = 0;
   int N = 0, Ci = 0, H = 0, W = 0;   // input shape (fc: Ci = input width, H = W = 1)
   int Co = 0, Ho = 0, Wo = 0;        // output shape (fc: Co = output width)
   int c = 0, P = 0, p = 1;           // conv filter / padding, pool window
@@ -187,12 +193,6 @@ struct sgd_net {
   // stream (they run concurrently).
   int64_t partial_off = 0, partial_floats = 0;
   int64_t partial_dw_off = 0, partial_dw_floats = 0;
-  // Scratch the first weighted layer's dedw product needs.  That product runs
-  // on the caller's stream (in the caller's-stream buffer, which is at least
-  // this large) when the overlap is on, after the last dedx product, next to
-  // the side stream's remaining dedw products; it is planned with this
-  // capacity in both modes, so its schedule and sum order do not change.
-  int64_t first_dw_floats = 0;
   // dCol of the conv dedx products (dedw reads Col concurrently).
   int64_t dcol_off = 0;
   sgd::Profiler prof;
@@ -203,6 +203,15 @@ struct sgd_net {
 
 namespace sgd {
 namespace {
+// The dedw products of the first kMainDw weighted layers run on the caller's
+// stream after their layer's dedx (see run_backward).  Once the second
+// weighted layer's dedx is issued, the caller's stream has nothing left but
+// the first layer's dedw, while the side stream still works through the
+// chain of the other layers' dedw products.  Measured on MI355X (ms/step
+// with 1 / 2 / 3 such layers): MLP-5000 3.071 / 3.072 / 3.127, VGG-CIFAR
+// 2.839 / 2.804 / 2.832, VGG-16 25.85 / 25.76 / 26.09, LeNet-5 (launched
+// call by call) 0.239 / 0.166 / 0.203.
+constexpr int kMainDw = 2;
 
 struct Bump {
   int64_t top = 0;
@@ -247,6 +256,7 @@ int plan(sgd_net* net) {
   bool flat = false;
   int64_t off = 0;
   bool seen_weighted = false;
+  int n_weighted = 0;
   for (int i = 0; i < n_layers; ++i) {
     const sgd_layer& L = net->spec[i];
     if (L.kind == SGD_CONV) {
@@ -270,6 +280,7 @@ int plan(sgd_net* net) {
       s.K = s.c * s.c * s.Ci;
       s.ldk = (int)round_up(s.K, 4);
       s.first_weighted = !seen_weighted;
+      s.weighted_rank = n_weighted++;
       seen_weighted = true;
       s.w_off = off;
       off += (int64_t)s.Co * s.K;
@@ -336,6 +347,7 @@ int plan(sgd_net* net) {
       s.Co = L.out;
       s.Ho = s.Wo = 1;
       s.first_weighted = !seen_weighted;
+      s.weighted_rank = n_weighted++;
       seen_weighted = true;
       s.w_off = off;
       off += (int64_t)s.Co * s.Ci;
@@ -369,7 +381,7 @@ int plan(sgd_net* net) {
 
   // Workspace layout and product split factors.
   Bump b;
-  int64_t partial = 0, partial_dw = 0, dcol = 0, first_dw = 0;
+  int64_t partial = 0, partial_dw = 0, dcol = 0;
   for (Stage& s : st) {
     const int64_t N = s.N;
     if (s.kind == SGD_CONV) {
@@ -390,8 +402,10 @@ int plan(sgd_net* net) {
       for (bool fused : {false, true}) {
         const int64_t need = gemm_scratch_floats(s.Co, s.ldk + 1, (int)P, true, true, fused, s.split_dw);
         partial_dw = std::max(partial_dw, need);
-        if (s.first_weighted) first_dw = std::max(first_dw, need);
+        s.dw_cap = std::max(s.dw_cap, need);
       }
+      s.dw_main = s.weighted_rank < kMainDw;
+      if (s.dw_main) partial = std::max(partial, s.dw_cap);
       if (s.implicit_dx) {
         partial = std::max(partial, gemm_scratch_floats((int)Pin, s.Ci, s.c * s.c * s.Co, false, false, false, 1));
       } else if (!s.first_weighted) {
@@ -419,8 +433,10 @@ int plan(sgd_net* net) {
       for (bool fused : {false, true}) {
         const int64_t need = gemm_scratch_floats(s.Co, s.Ci + 1, (int)N, true, true, fused, s.split_dw);
         partial_dw = std::max(partial_dw, need);
-        if (s.first_weighted) first_dw = std::max(first_dw, need);
+        s.dw_cap = std::max(s.dw_cap, need);
       }
+      s.dw_main = s.weighted_rank < kMainDw;
+      if (s.dw_main) partial = std::max(partial, s.dw_cap);
       if (!s.first_weighted)
         partial = std::max(partial, gemm_scratch_floats((int)N, s.Ci, s.Co, false, true, false, s.split_dx));
     } else if (s.kind == SGD_SOFTMAX_CE) {
@@ -430,8 +446,6 @@ int plan(sgd_net* net) {
       s.dout = st[s.input].dout;
     }
   }
-  partial = std::max(partial, first_dw);
-  net->first_dw_floats = first_dw;
   net->partial_floats = partial;
   net->partial_off = b.take(4 * std::max<int64_t>(partial, 1));
   net->partial_dw_floats = partial_dw;
@@ -569,12 +583,13 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
 // dedx product, which reads that layer's weights, runs before its dedw (a
 // conv layer's dedx reads the repacked copy W').
 //
-// Every dedw product but the first weighted layer's runs on the side stream,
-// forked from the caller's stream once its inputs (the layer's output
-// gradient, and the input activation or Col from the forward pass) are final
-// and, for an fc layer, after the dedx product that reads W.  The first
-// weighted layer has no dedx product, so its dedw runs on the caller's
-// stream (which has nothing else left to do) next to the side stream's tail.  Nothing on the caller's stream
+// Every dedw product but those of the first kMainDw weighted layers runs on
+// the side stream, forked from the caller's stream once its inputs (the
+// layer's output gradient, and the input activation or Col from the forward
+// pass) are final and, for an fc layer, after the dedx product that reads W.
+// The first kMainDw layers' dedw products run on the caller's stream after
+// the layer's dedx (little else is left there by then), next to the side
+// stream's tail.  Nothing on the caller's stream
 // writes what a dedw product reads or reads what it writes, and the caller's
 // stream joins the side stream at the end, so the step stays one stream-
 // ordered operation for the caller.
@@ -597,12 +612,13 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
     return 0;
   };
   // A dedw product on the side stream (forked once its inputs are final),
-  // except the first weighted layer's: nothing follows it on the caller's
-  // stream, so it runs there, concurrently with the side stream's last ones.
+  // except those of the first kMainDw weighted layers, which run on the
+  // caller's stream after the layer's dedx, concurrently with the side
+  // stream's last ones.
   auto launch_dw = [&](GemmDesc& g, const Stage& s) -> int {
-    if (s.first_weighted) {
+    if (s.dw_main) {
       g.partial = net->overlap ? partial : partial_dw;
-      g.partial_floats = net->first_dw_floats;
+      g.partial_floats = s.dw_cap;
       return gemm(g, st);
     }
     g.partial = partial_dw;
@@ -694,7 +710,9 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
       g.accum = accum;
       g.gscale = gscale;
       set_update(g, rule, state, s);
-      if ((e = launch_dw(g, s))) continue;
+      // a dedw on the caller's stream goes after the dedx, which the
+      // remaining layers wait for (the dedx reads the repacked W'' or W')
+      if (!s.dw_main && (e = launch_dw(g, s))) continue;
       if (s.implicit_dx) {
         // dedx_conv as one gather-form product: each input pixel gathers its
         // c*c taps of dout (flipped offsets) against W''; the ReLU mask of
@@ -741,6 +759,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         if ((e = col2im(dcol, mask, at<float>(ws, src.dout), s.N, s.Ci, s.H, s.W, s.c, s.P, s.Ho, s.Wo, s.ldk, st)))
           continue;
       }
+      if (s.dw_main && (e = launch_dw(g, s))) continue;
     }
   }
   // Join even after an error, so nothing enqueued on the side stream is left
