@@ -44,13 +44,13 @@ __device__ __forceinline__ void st4(float* p, int64_t i, v4f v) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p) + i);
 }
 
-// s[u] = x[u] + g_{j0}[u] + ... + g_{k-1}[u] for the thread's groups idx[u],
-// one rounding per addition, left to right.  K > 0: exactly K buffers
-// (k == K), every load issued before the first addition; K < 0: k buffers,
-// loaded one buffer at a time.  `init` says whether s already holds x (else
-// s starts as g_{j0}).
+// s[u] = x[u] + g_0[u] + ... + g_{k-1}[u] for the thread's groups idx[u], one
+// rounding per addition, left to right.  K > 0: exactly K buffers (k == K),
+// every load issued before the first addition; K < 0: k buffers, loaded one
+// buffer at a time.  `init` says whether s already holds x (else s starts as
+// g_0).
 template <int K>
-__device__ __forceinline__ void fold_groups(v4f (&s)[kGroups], const Ptrs& P, int j0, int k, bool init,
+__device__ __forceinline__ void fold_groups(v4f (&s)[kGroups], const Ptrs& P, int k, bool init,
                                             const int64_t (&idx)[kGroups]) {
   if constexpr (K > 0) {
     v4f g[K][kGroups];
@@ -66,12 +66,12 @@ __device__ __forceinline__ void fold_groups(v4f (&s)[kGroups], const Ptrs& P, in
       s[u] = acc;
     }
   } else {
-    for (int j = j0; j < k; ++j) {
+    for (int j = 0; j < k; ++j) {
       v4f g[kGroups];
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) g[u] = ld4(P.g[j], idx[u]);
 #pragma unroll
-      for (int u = 0; u < kGroups; ++u) s[u] = (init || j > j0) ? s[u] + g[u] : g[u];
+      for (int u = 0; u < kGroups; ++u) s[u] = (init || j > 0) ? s[u] + g[u] : g[u];
     }
   }
 }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* __restrict__ 
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) s[u] = ld4(buf, ld[u]);
     }
-    fold_groups<K>(s, P, 0, k, !COPY, ld);
+    fold_groups<K>(s, P, k, !COPY, ld);
 #pragma unroll
     for (int u = 0; u < kGroups; ++u)
       if (idx[u] < n4) st4(buf, idx[u], s[u]);
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(float* __restrict__ W, fl
       st[u] = kState ? ld4(state, ld[u]) : v4f{0.f, 0.f, 0.f, 0.f};
       g[u] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    if constexpr (K != 0) fold_groups<K>(g, P, 0, k, false, ld);
+    if constexpr (K != 0) fold_groups<K>(g, P, k, false, ld);
 #pragma unroll
     for (int u = 0; u < kGroups; ++u) {
       rule1<RULE>(w[u], st[u], g[u], eta, mu, eps, decay);
