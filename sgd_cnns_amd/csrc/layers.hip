@@ -250,6 +250,49 @@ __global__ __launch_bounds__(kBlock) void repack_conv_weights_kernel(RepackJobs 
   }
 }
 
+// The same for 3x3 filters (every conv of the VGG networks) with the tile
+// fixed at 32 output x 16 input channels: the index arithmetic is shifts and
+// multiplications by constants, and the 18.5 KiB tile lets more blocks share
+// a CU.  Threads past a partial tile's edge skip their element.
+constexpr int kR3Co = 32, kR3Ci = 16, kR3Ld = kR3Ci * 9 + 1;
+__global__ __launch_bounds__(kBlock) void repack_conv3x3_kernel(RepackJobs J) {
+  __shared__ float T[kR3Co * kR3Ld];
+  int l = 0;
+  while (l + 1 < J.n && J.j[l + 1].block0 <= (int)blockIdx.x) ++l;
+  const RepackJob b = J.j[l];
+  const int bi = (int)blockIdx.x - b.block0;
+  const int tco = bi / b.tiles_ci, tci = bi - tco * b.tiles_ci;
+  const int co0 = tco * kR3Co, ci0 = tci * kR3Ci;
+  const int nco = min(kR3Co, b.Co - co0), nci = min(kR3Ci, b.Ci - ci0);
+  const int seg = nci * 9;
+  for (int t = threadIdx.x; t < kR3Co * kR3Ci * 9; t += kBlock) {
+    const int co = t / (kR3Ci * 9), r = t - co * (kR3Ci * 9);
+    if (co < nco && r < seg) T[co * kR3Ld + r] = b.w[((int64_t)(co0 + co) * b.Ci + ci0) * 9 + r];
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < kR3Co * 9 * kR3Ci; t += kBlock) {
+    const int ci = t & (kR3Ci - 1), r = t / kR3Ci;
+    const int co = r / 9, tap = r - co * 9;
+    if (co < nco && ci < nci)
+      b.wrep[(int64_t)(co0 + co) * b.ldk + tap * b.Ci + ci0 + ci] = T[co * kR3Ld + ci * 9 + tap];
+  }
+  if (tci == b.tiles_ci - 1) {
+    const int pad = b.ldk - 9 * b.Ci;
+    for (int t = threadIdx.x; t < nco * pad; t += kBlock) {
+      const int co = t / pad, q = t - co * pad;
+      b.wrep[(int64_t)(co0 + co) * b.ldk + 9 * b.Ci + q] = 0.f;
+    }
+  }
+  if (b.wdx) {
+    for (int t = threadIdx.x; t < kR3Ci * 9 * kR3Co; t += kBlock) {
+      const int co = t & (kR3Co - 1), r = t / kR3Co;
+      const int ci = r / 9, tap = r - ci * 9;
+      if (co < nco && ci < nci)
+        b.wdx[(int64_t)(ci0 + ci) * 9 * b.Co + (int64_t)tap * b.Co + co0 + co] = T[co * kR3Ld + ci * 9 + tap];
+    }
+  }
+}
+
 // --------------------------------------------------------------- max pool ----
 // p x p windows, stride p, over NHWC input.  The window is scanned row-major
 // and a strict '>' keeps the first maximum; a NaN in the window makes the
@@ -497,49 +540,58 @@ int col2im(const float* dcol, const float* mask_act, float* dx, int N, int Ci, i
 }
 
 int repack_conv_weights(const RepackLayer* layers, int n, hipStream_t s) {
-  RepackJobs J{};
-  int blocks = 0;
-  double bytes = 0.0;
-  auto flush = [&]() -> int {
-    if (J.n == 0) return 0;
-    prof_begin("repack_weights", 0, bytes, s);
-    hipLaunchKernelGGL(repack_conv_weights_kernel, dim3(blocks), dim3(kBlock), 0, s, J);
-    prof_end(s);
-    J = RepackJobs{};
-    blocks = 0;
-    bytes = 0.0;
-    return check_launch("repack_conv_weights");
-  };
-  for (int i = 0; i < n; ++i) {
-    const RepackLayer& L = layers[i];
-    const int cc = L.c * L.c;
-    if (cc + 1 > kRepackLds) {
-      set_error("repack_conv_weights: filter too large for the staged repack");
-      return SGD_EUNSUPPORTED;
+  // Two launch tables: 3x3 filters (fixed tile) and everything else.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool three = pass == 0;
+    RepackJobs J{};
+    int blocks = 0;
+    double bytes = 0.0;
+    auto flush = [&]() -> int {
+      if (J.n == 0) return 0;
+      prof_begin("repack_weights", 0, bytes, s);
+      if (three)
+        hipLaunchKernelGGL(repack_conv3x3_kernel, dim3(blocks), dim3(kBlock), 0, s, J);
+      else
+        hipLaunchKernelGGL(repack_conv_weights_kernel, dim3(blocks), dim3(kBlock), 0, s, J);
+      prof_end(s);
+      J = RepackJobs{};
+      blocks = 0;
+      bytes = 0.0;
+      return check_launch("repack_conv_weights");
+    };
+    for (int i = 0; i < n; ++i) {
+      const RepackLayer& L = layers[i];
+      if ((L.c == 3) != three) continue;
+      const int cc = L.c * L.c;
+      if (cc + 1 > kRepackLds) {
+        set_error("repack_conv_weights: filter too large for the staged repack");
+        return SGD_EUNSUPPORTED;
+      }
+      // Largest tile with cot <= 32 and cit <= 16 whose staging fits.
+      const int cit = three ? kR3Ci : std::max(1, std::min(16, (kRepackLds / 32 - 1) / cc));
+      const int cot = three ? kR3Co : std::max(1, std::min(32, kRepackLds / (cit * cc + 1)));
+      const int64_t tiles = ceil_div(L.Co, cot) * ceil_div(L.Ci, cit);
+      if (J.n == kMaxRepackJobs || blocks + tiles > INT32_MAX / 2)
+        if (int e = flush()) return e;
+      RepackJob& b = J.j[J.n++];
+      b.w = L.w;
+      b.wrep = L.wrep;
+      b.wdx = L.wdx;
+      b.Co = L.Co;
+      b.Ci = L.Ci;
+      b.c = L.c;
+      b.ldk = L.ldk;
+      b.cot = cot;
+      b.cit = cit;
+      b.tiles_ci = (int)ceil_div(L.Ci, cit);
+      b.block0 = blocks;
+      blocks += (int)tiles;
+      const double wfl = (double)L.Co * L.Ci * cc;
+      bytes += 4.0 * (wfl + (double)L.Co * L.ldk + (L.wdx ? wfl : 0.0));
     }
-    // Largest tile with cot <= 32 and cit <= 16 whose staging fits.
-    const int cit = std::max(1, std::min(16, (kRepackLds / 32 - 1) / cc));
-    const int cot = std::max(1, std::min(32, kRepackLds / (cit * cc + 1)));
-    const int64_t tiles = ceil_div(L.Co, cot) * ceil_div(L.Ci, cit);
-    if (J.n == kMaxRepackJobs || blocks + tiles > INT32_MAX / 2)
-      if (int e = flush()) return e;
-    RepackJob& b = J.j[J.n++];
-    b.w = L.w;
-    b.wrep = L.wrep;
-    b.wdx = L.wdx;
-    b.Co = L.Co;
-    b.Ci = L.Ci;
-    b.c = L.c;
-    b.ldk = L.ldk;
-    b.cot = cot;
-    b.cit = cit;
-    b.tiles_ci = (int)ceil_div(L.Ci, cit);
-    b.block0 = blocks;
-    blocks += (int)tiles;
-    const double wfl = (double)L.Co * L.Ci * cc;
-    bytes += 4.0 * (wfl + (double)L.Co * L.ldk + (L.wdx ? wfl : 0.0));
+    if (int e = flush()) return e;
   }
-  return flush();
+  return 0;
 }
 
 namespace {
