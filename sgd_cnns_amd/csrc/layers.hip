@@ -202,6 +202,7 @@ struct RepackJob {
   int cot, cit;      // tile: output x input channels
   int tiles_ci;      // tiles along Ci
   int block0;        // first block of this job
+  int vec;           // 3x3 kernel: Ci, Co multiples of 4 and w 16-byte aligned
 };
 struct RepackJobs {
   RepackJob j[kMaxRepackJobs];
@@ -253,7 +254,9 @@ __global__ __launch_bounds__(kBlock) void repack_conv_weights_kernel(RepackJobs 
 // The same for 3x3 filters (every conv of the VGG networks) with the tile
 // fixed at 32 output x 16 input channels: the index arithmetic is shifts and
 // multiplications by constants, and the 18.5 KiB tile lets more blocks share
-// a CU.  Threads past a partial tile's edge skip their element.
+// a CU.  Threads past a partial tile's edge skip their element.  When Ci and
+// Co are multiples of 4 and the pointers 16-byte aligned (vec), every global
+// load and store moves a float4.
 constexpr int kR3Co = 32, kR3Ci = 16, kR3Ld = kR3Ci * 9 + 1;
 __global__ __launch_bounds__(kBlock) void repack_conv3x3_kernel(RepackJobs J) {
   __shared__ float T[kR3Co * kR3Ld];
@@ -265,16 +268,44 @@ __global__ __launch_bounds__(kBlock) void repack_conv3x3_kernel(RepackJobs J) {
   const int co0 = tco * kR3Co, ci0 = tci * kR3Ci;
   const int nco = min(kR3Co, b.Co - co0), nci = min(kR3Ci, b.Ci - ci0);
   const int seg = nci * 9;
-  for (int t = threadIdx.x; t < kR3Co * kR3Ci * 9; t += kBlock) {
-    const int co = t / (kR3Ci * 9), r = t - co * (kR3Ci * 9);
-    if (co < nco && r < seg) T[co * kR3Ld + r] = b.w[((int64_t)(co0 + co) * b.Ci + ci0) * 9 + r];
+  if (b.vec) {
+    // Whole float4s: nci, nco, seg, the source rows, ldk and every run start
+    // are multiples of 4.
+    for (int t = threadIdx.x; t < kR3Co * kR3Ci * 9 / 4; t += kBlock) {
+      const int co = t / (kR3Ci * 9 / 4), r = 4 * (t - co * (kR3Ci * 9 / 4));
+      if (co < nco && r < seg) {
+        const float4 v = *reinterpret_cast<const float4*>(b.w + ((int64_t)(co0 + co) * b.Ci + ci0) * 9 + r);
+        float* d = T + co * kR3Ld + r;
+        d[0] = v.x;
+        d[1] = v.y;
+        d[2] = v.z;
+        d[3] = v.w;
+      }
+    }
+  } else {
+    for (int t = threadIdx.x; t < kR3Co * kR3Ci * 9; t += kBlock) {
+      const int co = t / (kR3Ci * 9), r = t - co * (kR3Ci * 9);
+      if (co < nco && r < seg) T[co * kR3Ld + r] = b.w[((int64_t)(co0 + co) * b.Ci + ci0) * 9 + r];
+    }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < kR3Co * 9 * kR3Ci; t += kBlock) {
-    const int ci = t & (kR3Ci - 1), r = t / kR3Ci;
-    const int co = r / 9, tap = r - co * 9;
-    if (co < nco && ci < nci)
-      b.wrep[(int64_t)(co0 + co) * b.ldk + tap * b.Ci + ci0 + ci] = T[co * kR3Ld + ci * 9 + tap];
+  if (b.vec) {
+    for (int t = threadIdx.x; t < kR3Co * 9 * kR3Ci / 4; t += kBlock) {
+      const int ci = 4 * (t & (kR3Ci / 4 - 1)), r = t / (kR3Ci / 4);
+      const int co = r / 9, tap = r - co * 9;
+      if (co < nco && ci < nci) {
+        const float* src = T + co * kR3Ld + ci * 9 + tap;
+        *reinterpret_cast<float4*>(b.wrep + (int64_t)(co0 + co) * b.ldk + tap * b.Ci + ci0 + ci) =
+            make_float4(src[0], src[9], src[18], src[27]);
+      }
+    }
+  } else {
+    for (int t = threadIdx.x; t < kR3Co * 9 * kR3Ci; t += kBlock) {
+      const int ci = t & (kR3Ci - 1), r = t / kR3Ci;
+      const int co = r / 9, tap = r - co * 9;
+      if (co < nco && ci < nci)
+        b.wrep[(int64_t)(co0 + co) * b.ldk + tap * b.Ci + ci0 + ci] = T[co * kR3Ld + ci * 9 + tap];
+    }
   }
   if (tci == b.tiles_ci - 1) {
     const int pad = b.ldk - 9 * b.Ci;
@@ -283,7 +314,17 @@ __global__ __launch_bounds__(kBlock) void repack_conv3x3_kernel(RepackJobs J) {
       b.wrep[(int64_t)(co0 + co) * b.ldk + 9 * b.Ci + q] = 0.f;
     }
   }
-  if (b.wdx) {
+  if (b.wdx && b.vec) {
+    for (int t = threadIdx.x; t < kR3Ci * 9 * kR3Co / 4; t += kBlock) {
+      const int co = 4 * (t & (kR3Co / 4 - 1)), r = t / (kR3Co / 4);
+      const int ci = r / 9, tap = r - ci * 9;
+      if (co < nco && ci < nci) {
+        const float* src = T + co * kR3Ld + ci * 9 + tap;
+        *reinterpret_cast<float4*>(b.wdx + (int64_t)(ci0 + ci) * 9 * b.Co + (int64_t)tap * b.Co + co0 + co) =
+            make_float4(src[0], src[kR3Ld], src[2 * kR3Ld], src[3 * kR3Ld]);
+      }
+    }
+  } else if (b.wdx) {
     for (int t = threadIdx.x; t < kR3Ci * 9 * kR3Co; t += kBlock) {
       const int co = t & (kR3Co - 1), r = t / kR3Co;
       const int ci = r / 9, tap = r - ci * 9;
@@ -585,6 +626,9 @@ int repack_conv_weights(const RepackLayer* layers, int n, hipStream_t s) {
       b.cit = cit;
       b.tiles_ci = (int)ceil_div(L.Ci, cit);
       b.block0 = blocks;
+      b.vec = three && L.Ci % 4 == 0 && L.Co % 4 == 0 && L.ldk % 4 == 0 &&
+              reinterpret_cast<uintptr_t>(L.w) % 16 == 0 && reinterpret_cast<uintptr_t>(L.wrep) % 16 == 0 &&
+              (!L.wdx || reinterpret_cast<uintptr_t>(L.wdx) % 16 == 0);
       blocks += (int)tiles;
       const double wfl = (double)L.Co * L.Ci * cc;
       bytes += 4.0 * (wfl + (double)L.Co * L.ldk + (L.wdx ? wfl : 0.0));

@@ -78,6 +78,15 @@ def test_large_filter_conv_repack_tiles():
     check((3, 22, 22), layers, 2, 106, 7, x_dist="normal")
 
 
+def test_conv3x3_repack_ragged_channel_tiles():
+    # 3x3 weights are repacked in tiles of 32 output x 16 input channels: 20 and 40 input channels end
+    # in a short input tile (4, 8), 40, 48 and 36 output channels in a short output tile (8, 16, 4);
+    # the 48-channel layer also writes the dedx copy W'' (its dedx is the gathered product)
+    layers = [("conv", 40, 3, 1), ("relu",), ("conv", 48, 3, 1), ("relu",), ("conv", 36, 3, 0), ("relu",),
+              ("fc", 5), ("softmax_ce",)]
+    check((20, 7, 7), layers, 3, 107, 5, x_dist="normal")
+
+
 def test_mlp_ragged_tiles():
     layers = [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)]
     check((3072, 1, 1), layers, 70, 103, 10)
