@@ -180,7 +180,7 @@ int sgd_compute_gradient_into(sgd_net* net, const float* W, const float* X, cons
 
 /*
  * sgd_compute_gradient_into with the worker-side scaling of SPRINT Algorithm
- * 1 (its line 10, Grad <- -eta * grad): every gradient value is multiplied
+ * 1 (the worker stores Grad <- -eta * grad): every gradient value is multiplied
  * by `scale` (one rounding) before it is stored in or added to the buffer.
  * scale = -eta makes the buffer hold the step itself; applying it with
  * sgd_apply_update and eta = -1 then gives bitwise the unscaled path's
@@ -355,16 +355,16 @@ int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, flo
  * device.
  *
  *   worker t, step i (Algorithm 1): if i % n_fetch == 0 and LatestWeights is
- *     newer than its copy, copy it (lines 2-6, under the weights lock);
+ *     newer than its copy, copy it (the fetch, under the weights lock);
  *     take the next sub-batch (batch index = a shared counter mod n_batches);
- *     Grad <- ComputeGradient (line 9), folded into a private sum over
- *     n_push steps; every n_push steps (and at its last step) lock GradBuf_t,
- *     copy the sum in if the buffer is empty, else add it (lines 11-17).
+ *     Grad <- ComputeGradient, folded into a private sum over n_push steps;
+ *     every n_push steps (and at its last step) lock GradBuf_t, copy the sum
+ *     in if the buffer is empty, else add it (the push).
  *   updater (Algorithm 2 with one node): wait until at least min_bufs
  *     buffers are non-empty (or every worker has finished); take every
- *     non-empty GradBuf_t in index order, marking it empty (lines 2-14);
- *     W <- rule(W, sum of the taken buffers) in one fused pass (lines 15-20,
- *     the momentum of line 16 is the rule's state); publish the new version.
+ *     non-empty GradBuf_t in index order, marking it empty; W <- rule(W, sum
+ *     of the taken buffers) in one fused pass (the algorithm's momentum is
+ *     the rule's state); publish the new version.
  *
  * The locks are host mutexes; the device order behind them is carried by
  * HIP events (a worker's add is complete before the updater reads the
@@ -431,6 +431,12 @@ size_t sgd_sprint_workspace_bytes(const sgd_net* net, const sgd_sprint_config* c
  * copy of the net.  Errors: SGD_EINVAL (bad config, null pointers,
  * n_batches < 1, rule without its state), SGD_EWORKSPACE, SGD_EDEVICE; the
  * first error of any thread stops the run.
+ *
+ * For tests of that error path, the environment variable
+ * SGD_SPRINT_INJECT_FAILURE makes one thread fail with SGD_EDEVICE from the
+ * host, with no GPU fault: "w<t>:<i>" fails worker t at its step i while it
+ * holds its buffer, "u:<v>" fails the updater at update v while it holds
+ * the weights.  Any other value is ignored.
  */
 int sgd_sprint_run(const sgd_net* net, const sgd_sprint_config* cfg, float* W, float* state, const sgd_rule* rule,
                    const float* X, const int32_t* y, int64_t n_batches, void* ws, size_t ws_bytes, void* stream,

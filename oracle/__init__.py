@@ -379,11 +379,11 @@ def sprint_replay(net, W0, state0, rule, batches, log, eta, mu=0.0, eps=0.0, dec
 
     log holds one (worker, iter, push, batch, version, update) per worker step: the step's
     gradient is taken at the weights after `version` updates, on batches[batch] = (X, y)
-    (Algorithm 1 line 9).  A worker's steps with the same push index are summed in iter order
-    (the first stored, the rest added) and that sum goes into its GradBuf: copied when the
-    buffer is empty, else added (lines 11-17).  Update u takes the buffers holding the steps
-    with update == u, in worker order, folds them the same way into one sum, and applies the
-    rule to the weights (Algorithm 2 lines 2-20 with one node).  A buffer taken by update u
+    (Algorithm 1's gradient).  A worker's steps with the same push index are summed in iter
+    order (the first stored, the rest added) and that sum goes into its GradBuf: copied when
+    the buffer is empty, else added (Algorithm 1's push).  Update u takes the buffers holding
+    the steps with update == u, in worker order, folds them the same way into one sum, and
+    applies the rule to the weights (Algorithm 2 with one node).  A buffer taken by update u
     holds exactly the pushes of its steps, in push order.
 
     Returns (W, state, versions): the final weights and rule state, and W after each update

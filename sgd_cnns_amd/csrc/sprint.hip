@@ -160,7 +160,7 @@ void worker_loop(Run& R, int t) {
   std::vector<int64_t> pending;
   for (int i = 0; i < c.iters && !R.stop; ++i) {
     const Clock::time_point t0 = Clock::now();
-    if (i % c.n_fetch == 0) {  // lines 2-6: take LatestWeights if it is newer
+    if (i % c.n_fetch == 0) {  // the worker's fetch: take LatestWeights if it is newer
       std::lock_guard<std::mutex> g(R.wmu);
       if (R.version > have) {
         if (R.w_ready_valid && hipStreamWaitEvent(w.stream, R.w_ready, 0) != hipSuccess) return (void)R.hip_fail("wait");
@@ -175,13 +175,13 @@ void worker_loop(Run& R, int t) {
     const int64_t b = R.next_batch.fetch_add(1) % R.n_batches;
     const int64_t idx = (int64_t)t * c.iters + i;
     R.log[idx] = sgd_sprint_contrib{t, i, push, b, have, -1};
-    // line 9, the gradient, summed over the push interval
+    // the worker's gradient, summed over the push interval
     int e = sgd_compute_gradient_into(w.net, w.w, R.X + b * R.x_floats, R.y + b * R.batch, &sum, w.loss, w.ws,
                                       w.ws_bytes, w.stream);
     if (e) return R.fail_with(e, sgd_last_error());
     pending.push_back(idx);
     const bool pushing = (i + 1) % c.n_push == 0 || i + 1 == c.iters;
-    if (pushing) {  // lines 11-17: GradBuf_t <- Grad if empty, else GradBuf_t + Grad
+    if (pushing) {  // the push: GradBuf_t <- Grad if empty, else GradBuf_t + Grad
       std::unique_lock<std::mutex> lk(buf.mu);
       buf.cv.wait(lk, [&] { return buf.state != BUF_TAKEN || R.stop; });
       if (R.stop) return;
@@ -235,7 +235,7 @@ void updater_loop(Run& R) {
     if (R.stop) return;
     taken.clear();
     ptrs.clear();
-    for (int t = 0; t < nw; ++t) {  // lines 2-14, in buffer index order
+    for (int t = 0; t < nw; ++t) {  // the updater takes the non-empty buffers, in buffer index order
       Buf& b = *R.bufs[t];
       std::lock_guard<std::mutex> g(b.mu);
       if (b.state != BUF_FULL) continue;
@@ -251,7 +251,7 @@ void updater_loop(Run& R) {
       if (R.finished == nw && R.n_full == 0) break;  // every step applied
       continue;
     }
-    {  // lines 15-20: the new LatestWeights, after any fetch copy still reading the old one
+    {  // the update: the new LatestWeights, after any fetch copy still reading the old one
       std::lock_guard<std::mutex> g(R.wmu);
       if (R.version == R.inj_update) return R.fail_with(SGD_EDEVICE, "sgd_sprint_run: injected failure (updater)");
       for (int t = 0; t < nw; ++t) {

@@ -87,6 +87,17 @@ def test_conv3x3_repack_ragged_channel_tiles():
     check((20, 7, 7), layers, 3, 107, 5, x_dist="normal")
 
 
+def test_conv3x3_repack_misaligned_weights():
+    # two 1x1 convs (5 x (2+1) and 8 x (5+1) parameters) put the 3x3 layer's weights at float offset 63:
+    # its channel counts are multiples of 4 but the repack must take the one-float path; the 1x1 layers go
+    # to the generic repack kernel in a launch of their own
+    layers = [("conv", 5, 1, 0), ("relu",), ("conv", 8, 1, 0), ("relu",), ("conv", 12, 3, 1), ("relu",),
+              ("fc", 4), ("softmax_ce",)]
+    offs = sorted(O.OracleNet((2, 6, 6), layers).params.items())
+    assert offs[2][1][0] % 4 == 3, offs
+    check((2, 6, 6), layers, 3, 108, 4, x_dist="normal")
+
+
 def test_mlp_ragged_tiles():
     layers = [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)]
     check((3072, 1, 1), layers, 70, 103, 10)
@@ -273,7 +284,7 @@ def test_overlap_on_and_off_bitwise_equal(case):
 
 @pytest.mark.parametrize("case", ["mlp_ragged", "vgg_cifar_b2"])
 def test_prescaled_gradient(case):
-    # SPRINT Algorithm 1 line 10: the worker stores Grad = -eta * grad.  The
+    # SPRINT Algorithm 1: the worker stores Grad = -eta * grad.  The
     # scaled product rounds fl(scale * g) of the very g the unscaled path
     # stores, added into a non-empty buffer the same way; applied with
     # eta = -1 it gives the unscaled step's W and V bitwise; against the

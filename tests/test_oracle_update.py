@@ -207,7 +207,7 @@ def test_relu_of_negative_zero_is_positive_zero():
 
 # ------------------------------------------------ rule variants (NEXT f4) ----
 # The PIPE report's appendix A trains with weight decay (5e-4) and Nesterov
-# momentum and SPRINT Algorithm 1 (line 10) scales the worker's gradient by
+# momentum and SPRINT Algorithm 1 has the worker scale its gradient by
 # -eta; the pages give no formulas, so these pin the readings the oracle
 # implements: decay adds decay*W to the gradient before any rule, Nesterov
 # moves W by mu times the new change plus the gradient step.
@@ -297,7 +297,7 @@ def test_empty_gradbuf_with_decay_still_decays():
 
 
 def test_prescaled_gradient_applied_with_minus_one_is_bitwise_the_unscaled_step():
-    # SPRINT Algorithm 1 line 10 stores Grad = -eta * grad; applying that
+    # the SPRINT Algorithm 1 worker stores Grad = -eta * grad; applying that
     # buffer with eta = -1 rounds exactly like applying grad with eta
     # (-1 * fl(-eta g) = fl(eta g), negation is exact)
     W0, g, V0 = _rand(300, 22), _rand(300, 23, 1e-2), _rand(300, 24, 1e-3)
