@@ -793,6 +793,27 @@ __device__ __forceinline__ int64_t slot_index(int wave, int a, int c, int q, int
   return ((((int64_t)(wave * TM + a) * TN + c) * 4 + q) * 64 + lane) * 4;
 }
 
+// Tile t of a gemm_dma product.  A product more than kBandN tiles wide is
+// ordered in bands of kBandN tile columns, along N first within a band, so
+// an XCD's run of consecutive tiles (about 96 resident at once) reads about
+// 12 A and 8 B panels rather than one A panel per tile.  Narrower products
+// and conv weight gradients (permuted stores) run along M: the bands made
+// the VGG networks' steps no faster and VGG-CIFAR's slower.  The stream-K
+// fixup uses the same order.
+constexpr int kBandN = 8;
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, bool banded, int& tm_i, int& tn_i) {
+  if (!banded || tiles_n <= kBandN) {
+    tn_i = t / tiles_m;
+    tm_i = t - tn_i * tiles_m;
+    return;
+  }
+  const int band = t / (tiles_m * kBandN);
+  const int in_band = t - band * tiles_m * kBandN;
+  const int cols = min(kBandN, tiles_n - band * kBandN);
+  tm_i = in_band / cols;
+  tn_i = band * kBandN + (in_band - tm_i * cols);
+}
+
 // GA: the A operand is a K-contiguous convolution gather (DmaKg); GB: the B
 // operand is a row-contiguous one (DmaTg).
 template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
@@ -810,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
 
   // Blocks are dealt round-robin to the 8 XCDs; renumber so each XCD holds a
   // contiguous run of block indices, i.e. neighbouring tiles (which share
-  // operand panels in that XCD's L2).  Tiles are ordered along M first.
+  // operand panels in that XCD's L2), in the band order of tile_coords.
   const int G = gridDim.x;
   int b = blockIdx.x;
   if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
@@ -847,7 +868,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     } else {
       break;
     }
-    const int tn_i = t / tiles_m, tm_i = t - tn_i * tiles_m;
+    int tm_i, tn_i;
+    tile_coords(t, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
     const int m0 = tm_i * BM, n0 = tn_i * BN;
     const int kbeg = k0 * kDmaBK;
     const int kval = min(p.K, k1 * kDmaBK) - kbeg;
@@ -961,7 +983,8 @@ __global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int
   __syncthreads();
   const int t = s.dp_tiles + j;
   const int tiles_m = p.tiles / p.tiles_n;
-  const int tn_i = t / tiles_m, tm_i = t - tn_i * tiles_m;
+  int tm_i, tn_i;
+  tile_coords(t, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
   const int m0 = tm_i * BM, n0 = tn_i * BN;
   const int grp = threadIdx.x % TS, v4 = threadIdx.x / TS;
   const int idx = (blockIdx.y * (kThreads / TS) + v4) * 4;  // the float4's first element in the slot
