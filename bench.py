@@ -189,13 +189,21 @@ def gpu_step_bench(wl, steps, warmup, use_graph=True):
 
 
 def kernel_totals(recs):
+    # per kernel name: launches, event ms, algorithmic flops and bytes, and the roofline time
+    # sum over launches of max(flops / fp32 MFMA peak, bytes / HBM peak), with how many launches
+    # the flop term bounds
     kern = {}
     for (name, layer, phase, ms, flops, nbytes, _shape) in recs:
-        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0, "bound_ms": 0.0,
+                                   "flop_bound": 0})
         k["launches"] += 1
         k["ms"] += ms
         k["flops"] += flops
         k["bytes"] += nbytes
+        t_f = flops / (PEAK_FP32_TFLOPS * 1e9)
+        t_b = nbytes / (PEAK_HBM_GBS * 1e6)
+        k["bound_ms"] += max(t_f, t_b)
+        k["flop_bound"] += t_f >= t_b and flops > 0
     return kern
 
 
@@ -207,6 +215,11 @@ def kernel_table(kern, total_ms):
         if v["flops"] and name.startswith("gemm_"):
             e["TFLOP/s"] = v["flops"] / (v["ms"] / 1e3) / 1e12
             e["frac_fp32_peak"] = e["TFLOP/s"] / PEAK_FP32_TFLOPS
+            # against each launch's attainable time min(peak, AI * 8 TB/s), AI from its algorithmic
+            # operand bytes (A, B and C once)
+            e["frac_attainable"] = v["bound_ms"] / v["ms"] if v["ms"] > 0 else None
+            e["attainable_bound"] = ("mfma" if v["flop_bound"] == v["launches"] else
+                                     "hbm" if v["flop_bound"] == 0 else "mixed")
         if v["bytes"]:
             e["GB/s"] = v["bytes"] / (v["ms"] / 1e3) / 1e9
             e["frac_hbm_peak"] = e["GB/s"] / PEAK_HBM_GBS
