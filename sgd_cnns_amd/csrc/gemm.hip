@@ -1468,7 +1468,12 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
   }
   a.cv = d.cv;
   const double flops = d.flops > 0 ? d.flops : 2.0 * d.M * d.N * (double)d.K;
-  const double bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * a.Nt);
+  // Algorithmic bytes: both operands once, and the output: written once, read
+  // too when accumulated, and with the fused update the parameters (and the
+  // rule's state, if any) read and written in place of the store.
+  const double out_words = (double)d.M * a.Nt;
+  const double out_passes = d.urule >= 0 ? (d.urule == SGD_PLAIN ? 2.0 : 4.0) : d.accum ? 2.0 : 1.0;
+  const double bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + out_passes * out_words);
 
   // gemm_dma schedule.  The plan depends only on the shape and the machine
   // (the instance without an update rule sets the occupancy), so a product
