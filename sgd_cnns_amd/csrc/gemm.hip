@@ -1080,9 +1080,10 @@ struct Cfg {
 // gemm_staged configurations: 0: 128x128x16  1: 128x64x32  2: 64x128x32
 constexpr int kStagedConfigs = 3;
 const Cfg kCfg[kStagedConfigs] = {{128, 128, 16}, {128, 64, 32}, {64, 128, 32}};
-// gemm_dma configurations: 0: 128x128  1: 128x64  2: 64x128
-constexpr int kDmaConfigs = 3;
-const Cfg kDma[kDmaConfigs] = {{128, 128, kDmaBK}, {128, 64, kDmaBK}, {64, 128, kDmaBK}};
+// gemm_dma configurations: 0: 128x128  1: 128x64  2: 64x128  3: 64x64 (weight
+// gradients with both output sides <= 64 only: a first conv layer's)
+constexpr int kDmaConfigs = 4;
+const Cfg kDma[kDmaConfigs] = {{128, 128, kDmaBK}, {128, 64, kDmaBK}, {64, 128, kDmaBK}, {64, 64, kDmaBK}};
 
 const char* const kNames[kStagedConfigs][4] = {
     {"gemm_staged_128x128_nt", "gemm_staged_128x128_tn", "gemm_staged_128x128_nn", "gemm_staged_128x128_tt"},
@@ -1094,11 +1095,13 @@ const char* const kConvNames[kDmaConfigs][3] = {
     {"gemm_conv_fwd_128x128", "gemm_conv_dx_128x128", "gemm_conv_dw_128x128"},
     {"gemm_conv_fwd_128x64", "gemm_conv_dx_128x64", "gemm_conv_dw_128x64"},
     {"gemm_conv_fwd_64x128", "gemm_conv_dx_64x128", "gemm_conv_dw_64x128"},
+    {"gemm_conv_fwd_64x64", "gemm_conv_dx_64x64", "gemm_conv_dw_64x64"},
 };
 const char* const kDmaNames[kDmaConfigs][4] = {
     {"gemm_dma_128x128_nt", "gemm_dma_128x128_tn", "gemm_dma_128x128_nn", "gemm_dma_128x128_tt"},
     {"gemm_dma_128x64_nt", "gemm_dma_128x64_tn", "gemm_dma_128x64_nn", "gemm_dma_128x64_tt"},
     {"gemm_dma_64x128_nt", "gemm_dma_64x128_tn", "gemm_dma_64x128_nn", "gemm_dma_64x128_tt"},
+    {"gemm_dma_64x64_nt", "gemm_dma_64x64_tn", "gemm_dma_64x64_nn", "gemm_dma_64x64_tt"},
 };
 
 typedef void (*StagedKernel)(KArgs);
@@ -1181,11 +1184,21 @@ DmaFns dma_fns_of(int form, int em, int gather) {
       return dma_inst<BM, BN, true, false, EM_GENERIC>();
   }
 }
+// 64x64 is instantiated for the one product dma_cfg gives it: dedw (A^T B,
+// not gathered); anything else gets no kernel.
+DmaFns dma_fns_64x64(int form, int em, int gather) {
+  if (gather || form != 1) return {nullptr, nullptr, 0, 0};
+  if (em == EM_DW) return dma_inst<64, 64, true, true, EM_DW>();
+  if (em == EM_UPDATE) return dma_inst<64, 64, true, true, EM_UPDATE>();
+  if (em == EM_STORE) return dma_inst<64, 64, true, true, EM_STORE>();
+  return dma_inst<64, 64, true, true, EM_GENERIC>();
+}
 DmaFns dma_fns(int cfg, int form, int em, int gather) {
   switch (cfg) {
     case 0: return dma_fns_of<128, 128>(form, em, gather);
     case 1: return dma_fns_of<128, 64>(form, em, gather);
-    default: return dma_fns_of<64, 128>(form, em, gather);
+    case 2: return dma_fns_of<64, 128>(form, em, gather);
+    default: return dma_fns_64x64(form, em, gather);
   }
 }
 
@@ -1319,8 +1332,12 @@ int staged_cfg(int M, int Nt) {
   return 0;
 }
 
-// Tile choice for gemm_dma: 128x128 unless one side of the output is narrow.
-int dma_cfg(int M, int Nt) {
+// Tile choice for gemm_dma: 128x128 unless one side of the output is narrow;
+// a weight gradient (form A^T B, not gathered) with both sides <= 64 -- a
+// first conv layer's, 64 x (27 + 1) at VGG -- takes 64x64, which wastes half
+// the matrix-core work 128x64 would.
+int dma_cfg(int M, int Nt, int form, bool gather) {
+  if (form == 1 && !gather && M <= 64 && Nt <= 64) return 3;
   if (Nt <= 64) return 1;
   if (M <= 64) return 2;
   return 0;
@@ -1387,7 +1404,7 @@ int gemm_pick_splits(int M, int Nt, int K) {
 int64_t gemm_scratch_floats(int M, int Nt, int K, bool a_t, bool b_t, bool fused, int splits) {
   const int64_t staged = splits > 1 ? (int64_t)splits * M * Nt : 0;
   (void)fused;
-  const int cfg = dma_cfg(M, Nt);
+  const int cfg = dma_cfg(M, Nt, form_of(a_t, b_t), false);
   const Cfg& c = kDma[cfg];
   const SkPlan p = sk_choose(tiles_of(c, M, Nt), ceil_div(K, kDmaBK), machine_for(cfg), (int64_t)c.bm * c.bn, INT64_MAX);
   const int64_t sk = p.sk_iters > 0 ? 2 * (int64_t)p.grid * c.bm * c.bn : 0;
@@ -1443,7 +1460,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
   a.a_vec = aligned16(d.A) && d.lda % 4 == 0;
   a.b_vec = aligned16(d.B) && d.ldb % 4 == 0;
   const int form = form_of(d.a_t, d.b_t);
-  // d.cfg selects a gemm_dma configuration (0..2) or, as 3 + c, gemm_staged
+  // d.cfg selects a gemm_dma configuration (0..3) or, as 4 + c, gemm_staged
   // configuration c; -1 picks from the shape, preferring gemm_dma.
   bool dma;
   int cfg;
@@ -1454,7 +1471,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     dma = false;
     cfg = d.cfg - kDmaConfigs;
   } else {
-    cfg = dma_cfg(d.M, a.Nt);
+    cfg = dma_cfg(d.M, a.Nt, form, d.gather != 0);
     dma = dma_ok(d);
     if (!dma) cfg = staged_cfg(d.M, a.Nt);
   }
@@ -1525,6 +1542,10 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     a.split = 0;
     a.k_per_split = (int)round_up(d.K, kDmaBK);
     const DmaFns f = dma_fns(cfg, form, epi_mode(d, form), d.gather);
+    if (!f.main) {
+      set_error("gemm: no 64x64 kernel for this product form");
+      return SGD_EINVAL;
+    }
     const int64_t T = a.tiles, ipt = ceil_div(d.K, kDmaBK), tile = (int64_t)c.bm * c.bn;
     const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial};
     prof_begin(d.gather ? kConvNames[cfg][d.gather == 2 ? 2 : (d.cv.flip ? 1 : 0)] : kDmaNames[cfg][form], flops, bytes, s);
