@@ -1,27 +1,40 @@
 #!/usr/bin/env python3
-"""Benchmark one data-parallel worker's full SGD step on one MI355X.
+"""Benchmark one data-parallel worker's full SGD step on one MI355X, for the five workloads.
 
-A step is the gradient (forward, softmax-CE, backward through every layer)
-and the update rule applied to the weights (sgd_train_step: each layer's
-update is applied in the epilogue of its dedw product, bitwise equal to
+A step is the gradient (forward, softmax-CE, backward through every layer) and
+the update rule applied to the weights (sgd_train_step: each layer's update is
+applied in the epilogue of its dedw product, bitwise equal to
 gradient-into-GradBuf + apply_update), through the C ABI on one stream, with
-inputs already resident in HBM.  The unfused pair is timed too, for
-reference.  The default
-workload is the 5000-unit MLP (fc 3072-5000x5-10, ReLU, softmax-CE, batch 512,
-momentum SGD mu = 0.9, eta = 0.01), synthetic inputs from the seeded
-generators, He-normal weights.
+inputs resident in HBM.  Before every step -- warm-up, timed, profiled -- the
+weights and optimiser state are restored from a pristine device copy (outside
+the step's events), so every timed step is the same first step from the
+workload's He-normal weights, and every step's loss is checked to be finite.
+Each step is bracketed by its own HIP events on the caller's stream; the
+figures are the mean and median of the steps' event times (images/s =
+batch / mean step time, SPRINT report eq. (9) with one GPU).
 
-Printed: one JSON line with images/s (value), the roofline of the dominant
-kernel (HIP-event durations of every launch inside the timed region,
-algorithmic flops per launch), per-kernel totals, the parameter-server Adagrad
-apply in GB/s, and the CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+Workloads (seeded synthetic inputs):
+  lenet5     LeNet-5, batch 16 of 1x28x28, plain SGD eta 0.01
+  mlp5000    fc 3072-5000x5-10, batch 512, momentum mu 0.9 eta 0.01 (the headline `value`)
+  vgg_cifar  VGG-style 13 conv + 5 pool + fc 512-512-10 at 3x32x32, batch 128, plain SGD
+  vgg16      VGG-16 at 3x224x224, batch 32, 1000 classes, plain SGD
+  ps_adagrad the parameter-server apply: 138,357,544 parameters, 8 fresh seeded gradient buffers
+             left-folded + Adagrad, 100 steps; beside it the unfused chain and plain streaming
+             kernels with the same read and write streams (the memory-traffic ceiling)
 
-    python bench.py [--steps 50] [--warmup 5] [--workload mlp5000] [--no-cpu-baseline]
+Printed: one JSON line.  Top level: the MLP's images/s (value), the roofline
+of its dominant kernel (HIP-event durations of every launch in an
+event-bracketed pass over the same steps, algorithmic flops per launch), its
+CPU-oracle baseline.  `configs`: one record per workload with the same
+figures, the isolated (no-overlap) roofline, and eq. (4)'s prediction from the
+committed timing-model fit.
+
+    python bench.py [--steps 20] [--warmup 5] [--workload all|mlp5000|...] [--no-cpu-baseline]
 """
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,21 +44,46 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix (MFMA) peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "images/sec per fwd+bwd+update SGD step (fp32); GEMM MFMA util %, update GB/s"
+STEP_WORKLOADS = ["mlp5000", "lenet5", "vgg_cifar", "vgg16"]
+
+
+def say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE counter runs, or None
-    when there is no record for it or the kernel sources changed since the counters were taken."""
+    """(HBM bytes per launch, source) of `kernel` from the committed FETCH_SIZE/WRITE_SIZE counter
+    runs, or (None, reason) when there is no record for it or the kernel sources changed since the
+    counters were taken (the record stores a SHA-256 of the sources)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, "no counter record"
     rec = json.load(open(path))
+    recs = rec if isinstance(rec, list) else [rec]
     src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", f), "rb").read() for f in ("gemm.hip", "update.hip"))
-    if rec.get("workload") != workload or rec.get("source_sha256(gemm.hip+update.hip)") != hashlib.sha256(src).hexdigest():
-        return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k["traffic_bytes"]
+    digest = hashlib.sha256(src).hexdigest()
+    for r in recs:
+        if r.get("workload") != workload:
+            continue
+        if r.get("source_sha256(gemm.hip+update.hip)") != digest:
+            return None, f"profiles/traffic.json ({workload}) predates the current kernel sources"
+        k = r.get("kernels", {}).get(kernel)
+        if k is None:
+            return None, f"no counter record for {kernel}"
+        return k["traffic_bytes"], (f"profiles/traffic.json: rocprofv3 FETCH_SIZE x {r['fetch_scale']:.3f} + "
+                                    f"WRITE_SIZE x {r['write_scale']:.3f} per dispatch ({r['calibration']})")
+    return None, f"no counter record for {workload}"
 
 
 def describe(wl):
@@ -58,7 +96,14 @@ def describe(wl):
     return f"{wl.name}: {arch}, batch {wl.batch}, {rule}"
 
 
-def gpu_step_bench(wl, steps, warmup, use_graph=True):
+def _stats(ms):
+    return {"mean": statistics.fmean(ms), "median": statistics.median(ms), "min": min(ms), "max": max(ms)}
+
+
+def step_bench(wl, steps, warmup, use_graph=True):
+    """Time `steps` training steps of workload wl (each from the pristine weights), eagerly and as HIP
+    graph replays, then the same steps with per-launch events (overlapped and isolated) and the
+    unfused gradient + apply pair."""
     import numpy as np
     import torch
 
@@ -69,123 +114,120 @@ def gpu_step_bench(wl, steps, warmup, use_graph=True):
     X, y, W = workloads.make_inputs(wl)
     net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
     n = net.param_count()
-    Wd = torch.from_numpy(W).to(dev)
+    W0 = torch.from_numpy(W).to(dev)
+    Wd = W0.clone()
     Xd = torch.from_numpy(X).to(dev)
     yd = torch.from_numpy(y).to(dev)
-    grad = torch.empty(n, device=dev)
     loss = torch.empty(1, device=dev)
     ws = net.workspace(dev)
-    gb = S.GradBuf(n, device=dev)
-    state = None
+    st0 = None
     if wl.rule == "momentum":
-        state = torch.zeros(n, device=dev)
+        st0 = torch.zeros(n, device=dev)
     elif wl.rule == "adagrad":
-        state = torch.full((n,), 0.1, device=dev)
+        st0 = torch.full((n,), 0.1, device=dev)
+    state = None if st0 is None else st0.clone()
     rule = S.Rule(wl.rule, wl.eta, wl.mu, wl.eps)
     stream = torch.cuda.current_stream()
+    hist = torch.full((5 * steps + warmup + 64,), float("nan"), device=dev)
+    n_hist = [0]
 
-    def step(record=False):
-        # one sub-batch per update: gradient and rule fused (sgd_train_step)
+    def restore():
+        Wd.copy_(W0)
+        if state is not None:
+            state.copy_(st0)
+
+    def keep_loss():
+        i = n_hist[0]
+        hist[i:i + 1].copy_(loss)
+        n_hist[0] += 1
+
+    def eager():
         net.train_step(Wd, Xd, yd, state, rule, loss, ws, stream)
 
-    warm_losses = []
+    def timed(run, count):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+        first = n_hist[0]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            restore()
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            keep_loss()
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs], hist[first:n_hist[0]].cpu().numpy()
+
     for _ in range(warmup):
-        step()
-        warm_losses.append(float(loss.item()))
+        restore()
+        eager()
+        keep_loss()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    # the timed region, twice: the steps launched one call at a time, then (unless disabled) the step
-    # recorded once as a HIP graph (sgd_train_step_graph) and replayed, one launch per step.  Both are
-    # whole steps with no per-launch events; value takes the faster.  The graph removes the host
-    # launch gaps (small networks) but its replay may not overlap the dedw stream with the main one.
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    eager_ms = t0.elapsed_time(t1)
-    graph_ms = None
-    graph = None
+    warm_losses = hist[:n_hist[0]].cpu().numpy()
+    eager_ms, eager_loss = timed(eager, steps)
+    graph_ms = graph_loss = None
     if use_graph:
         graph = S.StepGraph(net, Wd, Xd, yd, state, rule, loss, ws)
+        restore()
         graph.launch(stream)
         torch.cuda.synchronize()
-        g0 = time.perf_counter()
-        t0.record(stream)
-        for _ in range(steps):
-            graph.launch(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = t0.elapsed_time(t1)
-        if graph_ms < eager_ms:
-            wall = time.perf_counter() - g0
-    total_ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
-    loss_v = float(loss.item())
-    # the same number of steps again with an event pair around every launch (sgd_profile): the
-    # per-kernel durations of the roofline and the kernel table.  The events add a few
-    # microseconds per launch, so this pass is not the one the throughput is taken from.
-    net.profile(True)
-    t0.record(stream)
-    for _ in range(steps):
-        step(record=True)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    net.profile(False)
-    prof_ms = t0.elapsed_time(t1)
-    recs = net.profile_read()
-    if warm_losses:
-        print(f"[bench] warmup losses {['%.4g' % v for v in warm_losses]}, last timed step {loss_v:.4g}",
-              file=sys.stderr, flush=True)
+        graph_ms, graph_loss = timed(lambda: graph.launch(stream), steps)
+        del graph
+    losses = np.concatenate([warm_losses, eager_loss] + ([graph_loss] if graph_loss is not None else []))
+    if not np.isfinite(losses).all():
+        raise RuntimeError(f"{wl.name}: non-finite loss in a warm-up or timed step: {losses.tolist()}")
+    use_g = graph_ms is not None and statistics.fmean(graph_ms) < statistics.fmean(eager_ms)
+    ms = graph_ms if use_g else eager_ms
 
-    # per-kernel totals over the timed region
-    kern = kernel_totals(recs)
-    # the same step with the dedw products on the caller's stream (no
-    # overlap): each kernel then has the GPU to itself, so its event time is
-    # its own duration
+    # the same steps with an event pair around every launch (sgd_profile): the per-kernel durations of
+    # the roofline and the kernel table.  The events cost a few microseconds per launch, so the
+    # throughput is not taken from this pass.
+    net.profile(True)
+    prof_ms, _ = timed(eager, steps)
+    net.profile(False)
+    kern = kernel_totals(net.profile_read())
+    # the same with the dedw products on the caller's stream (no overlap): each kernel has the GPU to
+    # itself, so its event time is its own duration; eq. (4) models this serial sum
     reps = max(3, min(steps, 10))
     net.set_overlap(False)
-    step()
-    torch.cuda.synchronize()
-    i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    restore()
+    eager()
     net.profile(True)
-    i0.record(stream)
-    for _ in range(reps):
-        step()
-    i1.record(stream)
-    torch.cuda.synchronize()
+    iso_ms, _ = timed(eager, reps)
     net.profile(False)
+    iso_recs = net.profile_read()
     net.set_overlap(True)
-    kern_iso = kernel_totals(net.profile_read())
-    iso_ms = i0.elapsed_time(i1) / reps
-    # the unfused pair for reference: gradient into the GradBuf, then the
-    # standalone apply kernel (its bandwidth is the update kernel's figure)
-    u0, u1, u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    upd_ms = 0.0
-    # one untimed pair first: the timed step never launches the standalone
-    # update kernels, so their first launch (code-object load) is kept out
+    kern_iso = kernel_totals(iso_recs)
+    # the unfused pair for reference: gradient into the GradBuf, then the standalone apply kernel
+    gb = S.GradBuf(n, device=dev)
+    restore()
     net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws, stream)
     S.apply_update(Wd, gb, state, rule, stream)
     torch.cuda.synchronize()
-    u0.record(stream)
+    unf = []
+    upd = []
     for _ in range(reps):
+        u0, u1, u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        restore()
+        u0.record(stream)
         net.compute_gradient_into(Wd, Xd, yd, gb, loss, ws, stream)
         u1.record(stream)
         S.apply_update(Wd, gb, state, rule, stream)
         u2.record(stream)
+        keep_loss()
         torch.cuda.synchronize()
-        upd_ms += u1.elapsed_time(u2)
-    unfused_ms = u0.elapsed_time(u2) / reps
+        unf.append(u0.elapsed_time(u2))
+        upd.append(u1.elapsed_time(u2))
     upd_b = {"plain": 12.0, "momentum": 20.0, "adagrad": 20.0}[wl.rule] * n
-    return dict(total_ms=total_ms, prof_ms=prof_ms, eager_ms=eager_ms, graph_ms=graph_ms,
-                graph=graph_ms is not None and graph_ms < eager_ms, wall_s=wall,
-                kern=kern, loss=loss_v, n_params=n,
-                loss_first=warm_losses[0] if warm_losses else None,
-                update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * upd_ms / reps,
-                        "GB/s": upd_b / (upd_ms / reps / 1e3) / 1e9},
-                unfused_ms=unfused_ms, kern_iso=kern_iso, iso_ms=iso_ms, iso_reps=reps)
+    final = hist[:n_hist[0]].cpu().numpy()
+    if not np.isfinite(final).all():
+        raise RuntimeError(f"{wl.name}: non-finite loss in a profiled step")
+    del ws, gb
+    torch.cuda.empty_cache()
+    return dict(ms=ms, eager_ms=eager_ms, graph_ms=graph_ms, graph=use_g, prof_ms=prof_ms, iso_ms=iso_ms,
+                kern=kern, kern_iso=kern_iso, iso_recs=iso_recs, n_params=n, losses=losses,
+                update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * statistics.fmean(upd),
+                        "GB/s": upd_b / (statistics.fmean(upd) / 1e3) / 1e9},
+                unfused_ms=unf)
 
 
 def kernel_totals(recs):
@@ -207,7 +249,11 @@ def kernel_totals(recs):
     return kern
 
 
-def kernel_table(kern, total_ms):
+def is_product(name):
+    return name.startswith(("gemm_dma_", "gemm_staged_", "gemm_conv_"))
+
+
+def kernel_table(kern, total_ms, top=10):
     rows = []
     for name, v in sorted(kern.items(), key=lambda kv: -kv[1]["ms"]):
         e = {"kernel": name, "launches": v["launches"], "avg_us": 1e3 * v["ms"] / v["launches"],
@@ -224,73 +270,66 @@ def kernel_table(kern, total_ms):
             e["GB/s"] = v["bytes"] / (v["ms"] / 1e3) / 1e9
             e["frac_hbm_peak"] = e["GB/s"] / PEAK_HBM_GBS
         rows.append(e)
-    return rows
+    return rows[:top]
 
 
-def variant_apply_bench(n, reps=20):
-    """Standalone update kernels for the rule variants (weight decay, Nesterov) on n parameters."""
-    import torch
+def dominant(kern):
+    """The kernel with the largest total time: a matrix product if any product is within a factor
+    of two of the largest kernel, else the largest kernel."""
+    top = max(kern, key=lambda k: kern[k]["ms"])
+    prods = {k: v for k, v in kern.items() if is_product(k)}
+    if prods:
+        p = max(prods, key=lambda k: prods[k]["ms"])
+        if 2 * prods[p]["ms"] >= kern[top]["ms"]:
+            return p
+    return top
 
-    import sgd_cnns_amd as S
 
-    dev = torch.device("cuda")
-    W = torch.randn(n, device=dev)
-    V = torch.zeros(n, device=dev)
-    G = torch.randn(n, device=dev) * 1e-3
-    stream = torch.cuda.current_stream()
-    out = {}
-    for name, rule, nbytes in (("apply_nesterov_decay", S.Rule("nesterov", 0.01, 0.9, 0.0, 5e-4), 20.0),
-                               ("apply_plain_decay", S.Rule("plain", 0.01, 0.0, 0.0, 5e-4), 12.0)):
-        st = V if name.startswith("apply_nesterov") else None
-        S.apply_fused(W, st, [G], rule, stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            S.apply_fused(W, st, [G], rule, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        out[name] = {"params": n, "bytes_per_param": nbytes, "avg_us": 1e3 * ms,
-                     "GB/s": nbytes * n / ms / 1e6, "frac_hbm_peak": nbytes * n / ms / 1e6 / PEAK_HBM_GBS}
+def roofline_of(kern, name, steps):
+    d = kern[name]
+    if is_product(name) or (d["flops"] and d["flop_bound"] == d["launches"]):
+        ach = d["flops"] / (d["ms"] / 1e3) / 1e12
+        out = {"bound": "mfma", "kernel": name, "achieved": ach, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+               "frac": ach / PEAK_FP32_TFLOPS, "flops_per_launch": d["flops"] / d["launches"]}
+    else:
+        ach = d["bytes"] / (d["ms"] / 1e3) / 1e9
+        out = {"bound": "hbm", "kernel": name, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": ach / PEAK_HBM_GBS, "bytes_per_launch": d["bytes"] / d["launches"]}
+    out.update({"launches": d["launches"], "launches_per_step": d["launches"] / steps,
+                "avg_launch_us": 1e3 * d["ms"] / d["launches"]})
     return out
 
 
-def ps_apply_bench(steps=100, pool=16):
-    """Parameter-server apply: 138,357,544 params, K = 8 buffers left-folded + Adagrad, fresh buffers per step."""
-    import torch
-
-    import sgd_cnns_amd as S
-    import workloads
-
-    ps = workloads.PS_APPLY
-    n, k = ps["n"], ps["k"]
-    dev = torch.device("cuda")
-    g = torch.Generator(device=dev)
-    g.manual_seed(ps["seed"])
-    W = torch.randn(n, device=dev, generator=g)
-    A = torch.full((n,), ps["acc0"], device=dev)
-    bufs = [torch.randn(n, device=dev, generator=g) * ps["grad_std"] for _ in range(pool)]
-    rule = S.Rule("adagrad", ps["eta"], 0.0, ps["eps"])
-    stream = torch.cuda.current_stream()
-    evs = []
-    for s in range(steps + 2):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        S.apply_fused(W, A, [bufs[(k * s + i) % pool] for i in range(k)], rule, stream)
-        e1.record(stream)
-        if s >= 2:
-            evs.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    nbytes = (k + 4) * 4.0 * n
-    del bufs
-    return {"workload": f"{n} params, K={k} gradient buffers (fresh each step, pool {pool}) left-folded + Adagrad",
-            "kernel": "apply_fused_adagrad", "ms_per_step": ms, "bytes_per_step": nbytes,
-            "GB/s": nbytes / ms / 1e6, "frac_of_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS, "steps": steps}
+def load_timing_fit():
+    path = os.path.join(ROOT, "profiles", "timing_model_fit.json")
+    if not os.path.exists(path):
+        return None
+    return json.load(open(path))
 
 
-def cpu_baseline(wl, sample):
-    """The CPU oracle on a bounded sample: gradient of `sample` images + a full accumulate + apply."""
+def eq4_record(fit, iso_recs, reps, iso_step_ms, step_ms):
+    """Eq. (4) of the SPRINT report with the committed eq. (6) / CUDA-kernel fit, for the products and
+    kernels this step launches, against the measured serial (no-overlap) step and the timed step."""
+    if fit is None:
+        return {"pred_ms": None, "note": "no committed timing-model fit (profiles/timing_model_fit.json)"}
+    from sgd_cnns_amd import timing_model as TM
+    per = max(1, len(iso_recs) // reps)
+    recs = iso_recs[:per]
+    try:
+        p = TM.predict_step(recs, fit["alphas"], {k: tuple(v) for k, v in fit["kernel_models"].items()})
+    except KeyError as e:
+        return {"pred_ms": None, "note": f"fit does not cover this step: {e}"}
+    return {"pred_ms": p["pred"], "sgemm_pred_ms": p["sgemm_pred"], "cuda_pred_ms": p["cuda_pred"],
+            "kernels_sum_ms": p["meas"], "no_overlap_step_ms": iso_step_ms, "timed_step_ms": step_ms,
+            "err_vs_no_overlap": (p["pred"] - iso_step_ms) / iso_step_ms,
+            "err_vs_timed_step": (p["pred"] - step_ms) / step_ms,
+            "fit": "profiles/timing_model_fit.json (eq. 6 per kernel family and form, eq. 5-form CUDA kernels)"}
+
+
+def cpu_baseline_step(wl, sample, min_seconds=2.0):
+    """The CPU oracle on a bounded sample: the gradient of `sample` images (repeated until about
+    min_seconds have passed when the sample is small) scaled per image to the full batch, plus one
+    accumulate + apply over all parameters."""
     import numpy as np
 
     import oracle as O
@@ -299,9 +338,15 @@ def cpu_baseline(wl, sample):
     X, y, W = workloads.make_inputs(wl)
     net = O.OracleNet(wl.chw, wl.layers)
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    reps = 0
     t0 = time.perf_counter()
+    while True:
+        net.gradient(W, X[:sample], y[:sample])
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds or reps >= 1000:
+            break
+    t_grad = (time.perf_counter() - t0) / reps
     _, g = net.gradient(W, X[:sample], y[:sample])
-    t_grad = time.perf_counter() - t0
     gb = O.GradBuf(W.size)
     state = np.zeros_like(W) if wl.rule != "adagrad" else np.full_like(W, 0.1)
     t0 = time.perf_counter()
@@ -309,9 +354,144 @@ def cpu_baseline(wl, sample):
     O.apply_rule(wl.rule, W, state, gb.data, wl.eta, wl.mu, wl.eps)
     t_upd = time.perf_counter() - t0
     t_step = t_grad * wl.batch / sample + t_upd
-    return {"value": wl.batch / t_step, "unit": "images/s", "cores": cores, "kind": "oracle",
-            "sample": (f"gradient of the first {sample} of {wl.batch} images ({t_grad:.1f} s) scaled per image to the "
-                       f"full batch, plus one accumulate+apply over all {W.size} parameters ({t_upd:.2f} s)")}
+    return {"value": wl.batch / t_step, "unit": "images/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle", "ms_per_step": 1e3 * t_step,
+            "sample": (f"gradient of the first {sample} of {wl.batch} images ({1e3 * t_grad:.1f} ms, mean of {reps}) "
+                       f"scaled per image to the full batch, plus one accumulate+apply over all {W.size} "
+                       f"parameters ({1e3 * t_upd:.1f} ms)")}
+
+
+def ps_bench(steps=100, reps=20):
+    """Parameter-server apply (config 5): 138,357,544 parameters, K = 8 gradient buffers from the
+    seeded pool of 16 (step s folds buffers 8s .. 8s+7 mod 16), left-folded + Adagrad in one pass,
+    one event pair per step.  Beside it, in the same run: the unfused chain (copy + 7 adds into a
+    GradBuf, then the standalone apply: 112 B per parameter) and plain streaming kernels with the
+    apply's read and write streams (sgd_stream_ref), the memory-traffic ceiling of that mix."""
+    import numpy as np
+    import torch
+
+    import sgd_cnns_amd as S
+    import workloads
+
+    ps = workloads.PS_APPLY
+    n, k = ps["n"], ps["k"]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    pool_h = workloads.ps_pool(ps, threads=min(16, len(os.sched_getaffinity(0))))
+    bufs = [torch.from_numpy(g).to(dev) for g in pool_h]
+    del pool_h
+    W0 = torch.from_numpy(workloads.normal(ps["seed"], 2, n)).to(dev)
+    say(f"ps_adagrad: pool of {len(bufs)} seeded buffers ready in {time.perf_counter() - t0:.1f} s")
+    W = W0.clone()
+    A = torch.full((n,), ps["acc0"], device=dev)
+    rule = S.Rule("adagrad", ps["eta"], 0.0, ps["eps"])
+
+    def events(count):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+
+    def fused(s):
+        S.apply_fused(W, A, [bufs[i] for i in workloads.ps_step_buffers(s, k, len(bufs))], rule, stream)
+
+    fused(0)
+    W.copy_(W0)
+    A.fill_(ps["acc0"])
+    torch.cuda.synchronize()
+    evs = events(steps)
+    for s, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        fused(s)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    finite = bool(torch.isfinite(W).all().item()) and bool(torch.isfinite(A).all().item())
+    if not finite:
+        raise RuntimeError("ps_adagrad: non-finite weights after 100 steps")
+    nbytes = (k + 4) * 4.0 * n
+    st = _stats(ms)
+    # unfused chain: GradBuf <- g_0 (copy), += g_1 .. g_7, then the standalone Adagrad apply
+    gb = S.GradBuf(n, device=dev)
+
+    def unfused(s):
+        for i in workloads.ps_step_buffers(s, k, len(bufs)):
+            S.accumulate_grad(gb, bufs[i], stream)
+        S.apply_update(W, gb, A, rule, stream)
+
+    unfused(0)
+    torch.cuda.synchronize()
+    evs = events(reps)
+    for s, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        unfused(s)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ums = [a.elapsed_time(b) for a, b in evs]
+    ubytes = (8.0 + 12.0 * (k - 1) + 20.0) * n
+    # the plain streaming references with the same streams (on the same buffers)
+    ref = {}
+    for name, outs, ins, groups in (("copy_1r1w", [gb.data], [bufs[0]], 1),
+                                    ("read_10r", [], bufs[:8] + [W, A], 1),
+                                    ("stream_10r2w_g1", [W, A], bufs[:8] + [W, A], 1),
+                                    ("stream_10r2w_g4", [W, A], bufs[:8] + [W, A], 4)):
+        S.stream_ref(outs, ins, groups, stream)
+        torch.cuda.synchronize()
+        evs = events(reps)
+        for s, (e0, e1) in enumerate(evs):
+            sh = [bufs[(j + 8 * s) % len(bufs)] for j in range(len(ins) - 2)] + ins[-2:] if len(ins) == 10 else ins
+            e0.record(stream)
+            S.stream_ref(outs, sh, groups, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        rms = statistics.fmean(a.elapsed_time(b) for a, b in evs)
+        rb = 4.0 * (len(ins) + len(outs)) * n
+        ref[name] = {"reads": len(ins), "writes": len(outs), "floats_per_thread": 4 * groups, "avg_us": 1e3 * rms,
+                     "GB/s": rb / rms / 1e6, "frac_hbm_peak": rb / rms / 1e6 / PEAK_HBM_GBS}
+    ceiling = max(ref["stream_10r2w_g1"]["GB/s"], ref["stream_10r2w_g4"]["GB/s"])
+    gbs = nbytes / st["mean"] / 1e6
+    del bufs, gb
+    torch.cuda.empty_cache()
+    return {"workload": (f"ps_adagrad: {n} parameters, K={k} fresh seeded gradient buffers N(0, 1e-3^2) per step "
+                         f"(pool {ps['pool']}), left-folded + Adagrad eta={ps['eta']} eps={ps['eps']} A0={ps['acc0']}, "
+                         f"{steps} steps"),
+            "metric": "update GB/s (48 B per parameter: 8 gradients + W + A read, W + A written)",
+            "steps": steps, "ms_per_step": st["mean"], "median_ms_per_step": st["median"],
+            "min_ms_per_step": st["min"], "max_ms_per_step": st["max"],
+            "bytes_per_step": nbytes, "GB/s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+            "roofline": {"bound": "hbm", "kernel": "apply_kernel<2, 8> (sgd_apply_fused, Adagrad, K = 8)",
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                         "bytes_per_launch": nbytes, "avg_launch_us": 1e3 * st["mean"]},
+            "frac_of_stream_10r2w_ceiling": gbs / ceiling,
+            "stream_ref": ref,
+            "unfused": {"chain": "accumulate copy + 7 accumulate adds + apply_update (Adagrad)",
+                        "bytes_per_param": ubytes / n, "ms_per_step": statistics.fmean(ums),
+                        "GB/s": ubytes / statistics.fmean(ums) / 1e6,
+                        "frac_hbm_peak": ubytes / statistics.fmean(ums) / 1e6 / PEAK_HBM_GBS},
+            "weights_finite_after_100_steps": finite}
+
+
+def cpu_baseline_ps(frac=16):
+    """The oracle's 8-buffer fold + Adagrad on 1/frac of the parameters, scaled to all of them."""
+    import numpy as np
+
+    import oracle as O
+    import workloads
+
+    ps = workloads.PS_APPLY
+    n, k = ps["n"], ps["k"]
+    m = n // frac
+    gs = [workloads.normal(ps["seed"], 100 + j, m, ps["grad_std"]) for j in range(k)]
+    W = workloads.normal(ps["seed"], 2, m)
+    A = np.full(m, ps["acc0"], np.float32)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    gb = O.GradBuf(m)
+    for g in gs:
+        gb.accumulate(g)
+    O.apply_adagrad(W, A, gb.data, ps["eta"], ps["eps"])
+    t = (time.perf_counter() - t0) * n / m
+    return {"value": 48.0 * n / t / 1e9, "unit": "GB/s", "ms_per_step": 1e3 * t, "cores": cores,
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"one step (8-buffer fold + Adagrad) on the first {m} of {n} parameters, scaled to all"}
 
 
 def timing_model_report(out_path, raw_prefix=None, reps=3):
@@ -524,6 +704,17 @@ def timing_model_report(out_path, raw_prefix=None, reps=3):
     text = "\n".join(L) + "\n"
     with open(out_path, "w") as fh:
         fh.write(text)
+    # the fit itself, for the step benchmark's per-workload eq. (4) prediction
+    import hashlib
+    src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", f), "rb").read()
+                   for f in ("gemm.hip", "layers.hip", "update.hip"))
+    fit = {"command": f"python bench.py --timing-model {os.path.relpath(out_path, ROOT)}",
+           "alphas": {fam: {f: [float(v) for v in alphas[fam][f]] for f in alphas[fam]} for fam in alphas},
+           "eq6_terms": list(TM.EQ6_TERMS),
+           "kernel_models": {k: [float(a), float(b)] for k, (a, b) in kmodels.items()},
+           "source_sha256(gemm.hip+layers.hip+update.hip)": hashlib.sha256(src).hexdigest()}
+    with open(os.path.splitext(out_path)[0] + ".json", "w") as fh:
+        json.dump(fit, fh, indent=1)
     print(text)
 
 
@@ -585,7 +776,25 @@ def sprint_report(out_path, workload="mlp5000"):
             torch.cuda.synchronize()
             finite = bool(torch.isfinite(Wd).all().item())
             say(f"sub-batch {sub}, {workers} workers x {iters}: {st['steps'] * sub / st['wall_ms'] * 1e3:.0f} img/s")
-            rows.append(dict(sub=sub, workers=workers, iters=iters, single_ms=single_ms, finite=finite, **st))
+            diverged = None
+            if not finite:
+                # where it diverged: shorter runs from the same start, doubling the steps per worker, until
+                # the weights are non-finite (the schedule is asynchronous, so this brackets the update)
+                last_ok = 0
+                it = 1
+                while it <= iters:
+                    Wd.copy_(torch.from_numpy(W0))
+                    V.zero_()
+                    st2, _ = S.sprint_run(net, S.SprintConfig(workers=workers, iters=it), Wd, V, rule, Xd, yd,
+                                          n_batches, ws)
+                    torch.cuda.synchronize()
+                    if not bool(torch.isfinite(Wd).all().item()):
+                        diverged = (last_ok, st2["updates"], it)
+                        break
+                    last_ok = st2["updates"]
+                    it *= 2
+            rows.append(dict(sub=sub, workers=workers, iters=iters, single_ms=single_ms, finite=finite,
+                             diverged=diverged, **st))
             del ws
             torch.cuda.empty_cache()
     L = ["# SPRINT Algorithms 1 and 2 on one MI355X", "",
@@ -607,27 +816,92 @@ def sprint_report(out_path, workload="mlp5000"):
                  f"{r['sub'] / r['single_ms'] * 1e3:.0f} | {r['t_gpu_ms']:.3f} | {r['t_update_ms']:.3f} | "
                  f"{r['updates']} | {r['n_minibatch_avg']:.1f} | {r['n_minibatch_eq9']:.1f} | "
                  f"{r['staleness_mean']:.2f} | {r['staleness_max']} | {r['finite']} |")
+    div = [r for r in rows if not r["finite"]]
+    if div:
+        L += ["", "Rows whose weights were not finite at the end, re-run from the same weights with 1, 2, 4, ... "
+                  "steps per worker until they were not finite (an asynchronous schedule, so this brackets the "
+                  "update at which the run diverged; each update applies the sum of the buffers it takes, so "
+                  "more workers put more summed samples into one update):", "",
+              "| N_Subbatch | workers | finite after (updates) | non-finite after (updates) | steps per worker |",
+              "|---|---|---|---|---|"]
+        for r in div:
+            d = r["diverged"]
+            if d is None:
+                L.append(f"| {r['sub']} | {r['workers']} | - | only in the full run | - |")
+            else:
+                L.append(f"| {r['sub']} | {r['workers']} | {d[0]} | {d[1]} | {d[2]} |")
     text = "\n".join(L) + "\n"
     with open(out_path, "w") as fh:
         fh.write(text)
     print(text)
 
 
+
+
+def step_record(wl, r, steps, fit, cpu):
+    """The JSON record of one step workload."""
+    ms = r["ms"]
+    st = _stats(ms)
+    kern, kern_iso = r["kern"], r["kern_iso"]
+    dom = dominant(kern)
+    prof_total = sum(r["prof_ms"])
+    roof = roofline_of(kern, dom, steps)
+    traffic, source = measured_traffic(dom, wl.name)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = source if traffic is not None else f"null: {source}"
+    roof["ms_per_step_profiled"] = prof_total / steps
+    roof["note"] = ("durations from HIP events around every launch over the same steps, right after the timed "
+                    "steps (the events cost a few microseconds per launch, so value is timed without them); with "
+                    "the dedw products on a second stream, a launch's duration is its time while it shares the GPU")
+    iso = None
+    if dom in kern_iso:
+        iso = roofline_of(kern_iso, dom, len(r["iso_ms"]))
+        iso["ms_per_step_no_overlap"] = statistics.fmean(r["iso_ms"])
+    gflops = sum(v["flops"] for k, v in kern.items() if is_product(k)) / steps
+    rec = {
+        "workload": describe(wl), "name": wl.name, "batch": wl.batch, "params": r["n_params"], "update": wl.rule,
+        "images_per_s": wl.batch / (st["mean"] / 1e3), "ms_per_step": st["mean"],
+        "median_ms_per_step": st["median"], "min_ms_per_step": st["min"], "max_ms_per_step": st["max"],
+        "steps": steps, "timed_as": "HIP graph replay of sgd_train_step" if r["graph"] else "sgd_train_step per call",
+        "eager_ms_per_step": statistics.fmean(r["eager_ms"]),
+        "eager_median_ms_per_step": statistics.median(r["eager_ms"]),
+        "graph_ms_per_step": None if r["graph_ms"] is None else statistics.fmean(r["graph_ms"]),
+        "graph_median_ms_per_step": None if r["graph_ms"] is None else statistics.median(r["graph_ms"]),
+        "no_overlap_ms_per_step": statistics.fmean(r["iso_ms"]),
+        "unfused_ms_per_step": statistics.fmean(r["unfused_ms"]),
+        "loss_first": float(r["losses"][0]), "loss_last": float(r["losses"][-1]),
+        "losses_finite": True,
+        "gemm_step_util": {"gemm_gflop_per_step": gflops / 1e9,
+                           "TFLOP/s": gflops / (st["mean"] / 1e3) / 1e12,
+                           "frac_fp32_peak": gflops / (st["mean"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
+                           "note": "sum of 2mnk over the step's products / ms_per_step"},
+        "roofline": roof, "roofline_isolated": iso,
+        "kernels": kernel_table(kern, prof_total), "kernels_isolated": kernel_table(kern_iso, sum(r["iso_ms"])),
+        "update_GB/s": {"kernel": r["update"]["kernel"], "GB/s": r["update"]["GB/s"],
+                        "frac_hbm_peak": r["update"]["GB/s"] / PEAK_HBM_GBS, "avg_us": r["update"]["avg_us"],
+                        "note": "standalone apply after gradient-into-GradBuf (the unfused pair); the timed step "
+                                "applies the rule in the dedw epilogues"},
+        "eq4": eq4_record(fit, r["iso_recs"], len(r["iso_ms"]), statistics.fmean(r["iso_ms"]), st["mean"]),
+        "cpu_baseline": cpu,
+    }
+    return rec
+
+
 def main():
-    import numpy as np
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mlp5000", choices=["mlp5000", "lenet5", "vgg_cifar", "vgg16"])
-    ap.add_argument("--cpu-sample", type=int, default=0, help="images in the oracle sample (0 = per workload)")
+    ap.add_argument("--workload", default="all", choices=["all", "ps_adagrad"] + STEP_WORKLOADS,
+                    help="one workload only (the headline fields then describe it), or all five")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP-graph replays")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP-graph replays)")
     ap.add_argument("--no-ps-apply", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter scaling)")
     ap.add_argument("--timing-model", metavar="OUT_MD", default=None,
-                    help="refit the SPRINT timing model (eqs. 4-6) and write its report instead of the step bench")
+                    help="refit the SPRINT timing model (eqs. 4-6) and write its report (and a .json of the fit "
+                         "beside it) instead of the step bench")
     ap.add_argument("--timing-model-raw", metavar="PREFIX", default=None,
                     help="also save the timing model's raw grid times and step records under this prefix")
     ap.add_argument("--sprint", metavar="OUT_MD", default=None,
@@ -635,10 +909,12 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}); the multi-GPU path is not built",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this build runs the step on a "
+              "single MI355X; the multi-GPU exchange is a design, not code", file=sys.stderr)
         sys.exit(2)
-
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.sprint:
         sprint_report(args.sprint)
         return
@@ -646,7 +922,6 @@ def main():
         timing_model_report(args.timing_model, args.timing_model_raw)
         return
     import workloads
-    wl = workloads.WORKLOADS[args.workload]
     if args.copy_calibration_mib:
         import torch
         n = args.copy_calibration_mib * 2 ** 20 // 4
@@ -656,77 +931,68 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    print(f"[bench] {describe(wl)}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    r = gpu_step_bench(wl, args.steps, args.warmup, use_graph=not args.no_graph)
-    ms_step = r["total_ms"] / args.steps
-    value = wl.batch * args.steps / (r["total_ms"] / 1e3)
-    kern = r["kern"]
-    gemms = {k: v for k, v in kern.items() if k.startswith("gemm_")}
-    dom = max(gemms, key=lambda k: gemms[k]["ms"])
-    d = gemms[dom]
-    achieved = d["flops"] / (d["ms"] / 1e3) / 1e12
-    g_flops = sum(v["flops"] for v in gemms.values())
-    g_ms = sum(v["ms"] for v in gemms.values())
-    upd = r["update"]
-    kernels = kernel_table(kern, r["prof_ms"])
-    iso = r["kern_iso"].get(dom)
+    names = STEP_WORKLOADS if args.workload == "all" else [w for w in STEP_WORKLOADS if w == args.workload]
+    fit = load_timing_fit()
+    cpu_sample = {"mlp5000": 64, "lenet5": 16, "vgg_cifar": 8, "vgg16": 1}
+    configs = []
+    t_start = time.perf_counter()
+    for name in names:
+        wl = workloads.WORKLOADS[name]
+        say(f"{describe(wl)}; warmup {args.warmup}, steps {args.steps}")
+        r = step_bench(wl, args.steps, args.warmup, use_graph=not args.no_graph)
+        say(f"{name}: {statistics.fmean(r['ms']):.3f} ms/step ({'graph' if r['graph'] else 'eager'}), "
+            f"losses {r['losses'][0]:.4g} .. {r['losses'][-1]:.4g}")
+        cpu = None
+        if not args.no_cpu_baseline:
+            say(f"{name}: CPU oracle baseline on {cpu_sample[name]} images")
+            cpu = cpu_baseline_step(wl, cpu_sample[name])
+        configs.append(step_record(wl, r, args.steps, fit, cpu))
+    ps = None
+    if not args.no_ps_apply and args.workload in ("all", "ps_adagrad"):
+        say("ps_adagrad: parameter-server apply, 100 steps")
+        ps = ps_bench()
+        if not args.no_cpu_baseline:
+            say("ps_adagrad: CPU oracle baseline")
+            ps["cpu_baseline"] = cpu_baseline_ps()
+        ps["name"] = "ps_adagrad"
+        configs.append(ps)
+    say(f"all workloads done in {time.perf_counter() - t_start:.0f} s")
+    head = next((c for c in configs if c["name"] == "mlp5000"), configs[0])
+    if head["name"] == "ps_adagrad":
+        out = {"metric": METRIC, "value": head["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": head["steps"],
+               "warmup": 1, "ms_per_step": head["ms_per_step"], "median_ms_per_step": head["median_ms_per_step"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+               "data": "synthetic (seeded Philox gradient buffers and weights)",
+               "config": {"workload": head["workload"]}, "roofline": head["roofline"],
+               "cpu_baseline": head.get("cpu_baseline"), "configs": configs}
+        print(json.dumps(out))
+        return
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["images_per_s"],
         "unit": "images/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
+        "median_ms_per_step": head["median_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded Philox inputs of the workload's shape; He-normal random-init weights)",
-        "config": {"workload": describe(wl), "global_batch": wl.batch, "params": r["n_params"],
-                   "update": wl.rule},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
-                     "traffic": measured_traffic(dom, wl.name),
-                     "launches": d["launches"], "avg_launch_us": 1e3 * d["ms"] / d["launches"],
-                     "flops_per_launch": d["flops"] / d["launches"],
-                     "ms_per_step_profiled": r["prof_ms"] / args.steps,
-                     "note": "kernel durations from HIP events around every launch over the same number of steps, "
-                             "run right after the timed region (the events cost a few microseconds per launch, so "
-                             "value is timed without them).  Each layer's dedw product runs on a second stream, "
-                             "overlapping the next layer's dedx product, so avg_launch_us is the launch's duration "
-                             "while it shares the GPU; roofline_isolated is the same kernel with the overlap "
-                             "switched off"},
-        "roofline_isolated": None if iso is None else {
-            "kernel": dom, "achieved": iso["flops"] / (iso["ms"] / 1e3) / 1e12, "peak": PEAK_FP32_TFLOPS,
-            "unit": "TFLOP/s", "frac": iso["flops"] / (iso["ms"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
-            "launches": iso["launches"], "avg_launch_us": 1e3 * iso["ms"] / iso["launches"],
-            "ms_per_step_no_overlap": r["iso_ms"]},
-        "kernels_isolated": kernel_table(r["kern_iso"], r["iso_ms"] * r["iso_reps"])[:8],
-        "gemm_mfma_util": {"achieved_TFLOP/s": g_flops / (g_ms / 1e3) / 1e12,
-                           "frac_fp32_peak": g_flops / (g_ms / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
-                           "share_of_step": g_ms / r["prof_ms"]},
-        "update_GB/s": {"kernel": upd["kernel"], "GB/s": upd["GB/s"], "frac_hbm_peak": upd["GB/s"] / PEAK_HBM_GBS,
-                        "avg_us": upd["avg_us"],
-                        "note": "standalone apply after gradient-into-GradBuf; the timed step fuses the update into "
-                                "the dedw epilogues (sgd_train_step)"},
-        "timed_as": "HIP graph replay of sgd_train_step (one launch per step)" if r["graph"] else
-                    "sgd_train_step launched per step",
-        "eager_ms_per_step": r["eager_ms"] / args.steps,
-        "graph_ms_per_step": None if r["graph_ms"] is None else r["graph_ms"] / args.steps,
-        "unfused_ms_per_step": r["unfused_ms"],
-        "kernels": kernels,
-        "loss_first_step": r["loss_first"],
-        "loss_last_step": r["loss"] if np.isfinite(r["loss"]) else str(r["loss"]),
+        "data": "synthetic (seeded Philox inputs of the workload's shape; He-normal random-init weights, restored "
+                "before every step)",
+        "config": {"workload": head["workload"], "global_batch": head["batch"], "params": head["params"],
+                   "update": head["update"]},
+        "roofline": head["roofline"],
+        "roofline_isolated": head["roofline_isolated"],
+        "cpu_baseline": head["cpu_baseline"],
+        "gemm_step_util": head["gemm_step_util"],
+        "timed_as": head["timed_as"],
+        "loss_first": head["loss_first"],
+        "loss_last": head["loss_last"],
+        "configs": configs,
     }
-    out["update_variants"] = variant_apply_bench(r["n_params"])
-    if not args.no_ps_apply:
-        print("[bench] parameter-server apply", file=sys.stderr, flush=True)
-        out["ps_apply"] = ps_apply_bench()
-    if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mlp5000": 512, "lenet5": 16, "vgg_cifar": 16, "vgg16": 1}[wl.name]
-        print(f"[bench] CPU oracle baseline on {sample} images", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, sample)
     print(json.dumps(out))
 
 

@@ -138,8 +138,10 @@ int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offs
  * One sub-batch gradient (SPRINT Algorithm 1, Grad = ComputeGradient(Weights)).
  *  W     [param_count] weights, flat layout above.
  *  X     [N][C][H][W] images, float32, NCHW.
- *  y     [N] int32 labels in [0, classes); out-of-range labels are caller error
- *        (not checked on the device).
+ *  y     [N] int32 labels in [0, classes).  An out-of-range label is caller
+ *        error: the softmax kernel never indexes with it (that row's loss and
+ *        logit gradient become NaN, so the loss and gradients are NaN), and
+ *        with sgd_set_debug on the call returns SGD_EINVAL before any launch.
  *  grad  [param_count] output: the full gradient (every element written).
  *  loss  device float scalar output: softmax cross-entropy, reduced per the
  *        net's reduction.
@@ -247,6 +249,22 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
                     const sgd_rule* rule, void* stream);
 
 /*
+ * Memory-traffic reference for the update kernels (measurement only; it is
+ * not a step of the method).  For every element i < n:
+ * outs[j][i] = ins[0][i] + ... + ins[n_in-1][i] for each j < n_out -- the
+ * read and write streams of an update pass (the parameter-server apply
+ * reads 8 gradient buffers, W and A and writes W and A: 10 reads, 2 writes)
+ * without the rule's arithmetic or the GradBuf semantics.  Supported
+ * (n_in, n_out): (1, 1) a copy, (10, 0) reads only, (10, 2).  `groups` is the
+ * number of float4 groups per thread: 1 (one float4 per thread) or 4 (the
+ * update kernels' block-contiguous layout).  ins and outs are host arrays of
+ * device pointers, 16-byte aligned; n a positive multiple of 4; outputs may
+ * alias inputs.  Errors: SGD_EINVAL, SGD_EDEVICE.
+ */
+int sgd_stream_ref(float* const* outs, int n_out, const float* const* ins, int n_in, int64_t n, int groups,
+                   void* stream);
+
+/*
  * One fp32 matrix product on the library's matrix-core kernels, the SGEMM of
  * the SPRINT report's section 3.3 table: C[m][n] = op(A) * op(B), row-major
  * C with row stride ldc.
@@ -289,6 +307,19 @@ int sgd_gemm(const sgd_gemm_args* g, void* ws, size_t ws_bytes, void* stream);
  * sums its terms in another order.  Errors: SGD_EINVAL (null net).
  */
 int sgd_set_implicit_conv(sgd_net* net, int enable);
+
+/*
+ * Debug mode (off by default).  While it is on, sgd_compute_gradient,
+ * sgd_compute_gradient_into(_scaled) and sgd_train_step copy the labels y to
+ * the host before launching anything (a synchronous read on `stream`, which
+ * therefore waits for the work already queued there) and return SGD_EINVAL,
+ * with the first bad row named in sgd_last_error(), when a label lies outside
+ * [0, classes); nothing is launched then.  sgd_train_step_graph checks the
+ * labels once when it records the step (replays are not checked).  The pages
+ * give no error convention; this is the plain C-library choice of validating
+ * caller data only on request.  Errors: SGD_EINVAL (null net).
+ */
+int sgd_set_debug(sgd_net* net, int enable);
 
 /*
  * Backward-pass concurrency.  With overlap on (the default) each layer's

@@ -33,9 +33,9 @@ LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
-           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
+           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_debug", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
            "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_train_step_graph", "sgd_step_graph_launch",
-           "sgd_step_graph_destroy", "sgd_last_error"]
+           "sgd_step_graph_destroy", "sgd_stream_ref", "sgd_last_error"]
 
 
 class SgdLayer(C.Structure):
@@ -116,6 +116,7 @@ def lib():
             "sgd_train_step": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P, sz, P]),
             "sgd_profile": (i, [P, i]),
             "sgd_set_overlap": (i, [P, i]),
+            "sgd_set_debug": (i, [P, i]),
             "sgd_set_implicit_conv": (i, [P, i]),
             "sgd_gemm_workspace_bytes": (sz, [C.POINTER(SgdGemmArgs)]),
             "sgd_gemm": (i, [C.POINTER(SgdGemmArgs), P, sz, P]),
@@ -126,6 +127,7 @@ def lib():
             "sgd_train_step_graph": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P, sz, C.POINTER(P)]),
             "sgd_step_graph_launch": (i, [P, P]),
             "sgd_step_graph_destroy": (None, [P]),
+            "sgd_stream_ref": (i, [C.POINTER(P), i, C.POINTER(P), i, i64, i, P]),
             "sgd_last_error": (C.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -155,6 +157,19 @@ def _require_cuda(*tensors, rows=False):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors" + (" (matrices: unit column stride)"
                                                                             if rows else ""))
+
+
+def _expect(t, numel, dtype, name):
+    """t is a tensor of `dtype` with exactly `numel` elements (None passes: the C side rejects a
+    missing required pointer)."""
+    import torch
+    if t is None:
+        return
+    dt = {"f32": torch.float32, "i32": torch.int32, "u8": torch.uint8}[dtype]
+    if t.dtype != dt:
+        raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
 
 
 def _stream(stream):
@@ -251,6 +266,28 @@ class Net:
         """Implicit-GEMM convolutions where the shapes allow (default on); re-plans the workspace."""
         _check(lib().sgd_set_implicit_conv(self._h, 1 if enable else 0))
 
+    def _check_step(self, W, X, y, loss, ws, state=None, grad=None, need_state=False):
+        n = self.param_count()
+        N = self.nchw[0]
+        nx = 1
+        for d in self.nchw:
+            nx *= int(d)
+        _expect(W, n, "f32", "W")
+        _expect(X, nx, "f32", "X")
+        _expect(y, N, "i32", "y")
+        _expect(loss, None, "f32", "loss")
+        if loss is not None and loss.numel() < 1:
+            raise ValueError("loss must hold at least one float")
+        _expect(ws, None, "u8", "ws")
+        _expect(state, n, "f32", "state")
+        _expect(grad, n, "f32", "grad")
+        if need_state and state is None:
+            raise ValueError("this rule needs a state tensor")
+
+    def set_debug(self, enable):
+        """Validate the labels on the host before every step (sgd_set_debug)."""
+        _check(lib().sgd_set_debug(self._h, 1 if enable else 0))
+
     def set_overlap(self, enable):
         """Run the dedw products on a second stream, overlapping the next layer (default on)."""
         _check(lib().sgd_set_overlap(self._h, 1 if enable else 0))
@@ -274,6 +311,7 @@ class Net:
 
     def compute_gradient(self, W, X, y, grad, loss, ws, stream=None):
         _require_cuda(W, X, y, grad, loss, ws)
+        self._check_step(W, X, y, loss, ws, grad=grad)
         _check(lib().sgd_compute_gradient(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(grad), _ptr(loss), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -281,6 +319,7 @@ class Net:
     def compute_gradient_into(self, W, X, y, gb, loss, ws, stream=None):
         """Gradient stored into an empty GradBuf, or added into a non-empty one."""
         _require_cuda(W, X, y, gb.data, loss, ws)
+        self._check_step(W, X, y, loss, ws, grad=gb.data)
         _check(lib().sgd_compute_gradient_into(self._h, _ptr(W), _ptr(X), _ptr(y), C.byref(gb._c), _ptr(loss),
                                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -288,6 +327,7 @@ class Net:
     def compute_gradient_into_scaled(self, W, X, y, gb, scale, loss, ws, stream=None):
         """As compute_gradient_into with every gradient value multiplied by `scale` first."""
         _require_cuda(W, X, y, gb.data, loss, ws)
+        self._check_step(W, X, y, loss, ws, grad=gb.data)
         _check(lib().sgd_compute_gradient_into_scaled(self._h, _ptr(W), _ptr(X), _ptr(y), C.byref(gb._c),
                                                       C.c_float(scale), _ptr(loss), _ptr(ws),
                                                       ws.numel() * ws.element_size(), _stream(stream)))
@@ -295,6 +335,7 @@ class Net:
     def train_step(self, W, X, y, state, rule, loss, ws, stream=None):
         """Gradient + update in one pass: W (and state) updated in place."""
         _require_cuda(W, X, y, state, loss, ws)
+        self._check_step(W, X, y, loss, ws, state=state, need_state=rule.rule != PLAIN)
         _check(lib().sgd_train_step(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(state), C.byref(rule), _ptr(loss),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -305,6 +346,7 @@ class StepGraph:
 
     def __init__(self, net, W, X, y, state, rule, loss, ws):
         _require_cuda(W, X, y, state, loss, ws)
+        net._check_step(W, X, y, loss, ws, state=state, need_state=rule.rule != PLAIN)
         self._keep = (net, W, X, y, state, loss, ws)
         self._rule = rule
         h = C.c_void_p()
@@ -360,18 +402,31 @@ def gemm(A, B, C_, a_t=False, b_t=False, ws=None, stream=None):
     """C = op(A) op(B) on the GPU: A is [m][k] (a_t: [k][m]); B is [n][k] (b_t: [k][n])."""
     _require_cuda(A, B, C_, rows=True)
     _require_cuda(ws)
+    for t, name in ((A, "A"), (B, "B"), (C_, "C")):
+        _expect(t, None, "f32", name)
     g = _gemm_args(A, B, C_, a_t, b_t)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().sgd_gemm(C.byref(g), _ptr(ws), nbytes, _stream(stream)))
 
 
+def _check_gradbuf(gb):
+    _expect(gb.data, None, "f32", "GradBuf data")
+    if gb.data.numel() < gb._c.n:
+        raise ValueError(f"GradBuf data holds {gb.data.numel()} floats, the buffer says {gb._c.n}")
+
+
 def accumulate_grad(gb, grad, stream=None):
     _require_cuda(gb.data, grad)
+    _check_gradbuf(gb)
+    _expect(grad, gb._c.n, "f32", "grad")
     _check(lib().sgd_accumulate_grad(C.byref(gb._c), _ptr(grad), _stream(stream)))
 
 
 def accumulate_grads(gb, grads, stream=None):
     _require_cuda(gb.data, *grads)
+    _check_gradbuf(gb)
+    for j, g in enumerate(grads):
+        _expect(g, gb._c.n, "f32", f"grads[{j}]")
     arr = (C.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
     _check(lib().sgd_accumulate_grads(C.byref(gb._c), arr, len(grads), _stream(stream)))
 
@@ -385,11 +440,18 @@ def Rule(rule, eta, mu=0.0, eps=0.0, decay=0.0):
 
 def apply_update(W, gb, state, rule, stream=None):
     _require_cuda(W, gb.data, state)
+    _check_gradbuf(gb)
+    _expect(W, gb._c.n, "f32", "W")
+    _expect(state, gb._c.n, "f32", "state")
     _check(lib().sgd_apply_update(_ptr(W), C.byref(gb._c), _ptr(state), C.byref(rule), _stream(stream)))
 
 
 def apply_fused(W, state, grads, rule, stream=None):
     _require_cuda(W, state, *grads)
+    _expect(W, None, "f32", "W")
+    _expect(state, W.numel(), "f32", "state")
+    for j, g in enumerate(grads):
+        _expect(g, W.numel(), "f32", f"grads[{j}]")
     arr = (C.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
     _check(lib().sgd_apply_fused(_ptr(W), _ptr(state), arr, len(grads), W.numel(), C.byref(rule), _stream(stream)))
 
@@ -409,6 +471,17 @@ def sprint_run(net, cfg, W, state, rule, X, y, n_batches, ws, stream=None):
     the net's batch.  Returns (stats dict, log) with one log entry per worker step:
     (worker, iter, push, batch, version, update)."""
     _require_cuda(W, state, X, y, ws)
+    n = net.param_count()
+    per = 1
+    for d in net.nchw:
+        per *= int(d)
+    _expect(W, n, "f32", "W")
+    _expect(state, n, "f32", "state")
+    _expect(X, None, "f32", "X")
+    _expect(y, None, "i32", "y")
+    _expect(ws, None, "u8", "ws")
+    if n_batches >= 1 and (X.numel() < per * int(n_batches) or y.numel() < net.nchw[0] * int(n_batches)):
+        raise ValueError(f"X and y must hold {n_batches} sub-batches of {net.nchw[0]}")
     steps = cfg.workers * cfg.iters
     log = (SgdSprintContrib * max(steps, 1))()
     st = SgdSprintStats()
@@ -417,3 +490,14 @@ def sprint_run(net, cfg, W, state, rule, X, y, n_batches, ws, stream=None):
                                 int(n_batches), _ptr(ws), nbytes, _stream(stream), C.byref(st), log, steps))
     stats = {name: getattr(st, name) for name, _ in SgdSprintStats._fields_}
     return stats, [(c.worker, c.iter, c.push, c.batch, c.version, c.update) for c in log[:steps]]
+
+
+def stream_ref(outs, ins, groups=1, stream=None):
+    """Reference streaming pass (sgd_stream_ref): every output = left-fold sum of the inputs."""
+    _require_cuda(*outs, *ins)
+    n = ins[0].numel()
+    for t in list(outs) + list(ins):
+        _expect(t, n, "f32", "stream tensor")
+    o = (C.c_void_p * max(1, len(outs)))(*[t.data_ptr() for t in outs])
+    i = (C.c_void_p * len(ins))(*[t.data_ptr() for t in ins])
+    _check(lib().sgd_stream_ref(o, len(outs), i, len(ins), n, groups, _stream(stream)))

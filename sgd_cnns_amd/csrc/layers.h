@@ -33,5 +33,7 @@ int softmax_ce(const float* z, const int32_t* y, float* dz, float* row_loss, flo
 int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy, int64_t n, hipStream_t s);
 int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t n, int rule, float eta, float mu,
                float eps, float decay, hipStream_t s);
+int stream_ref(float* const* outs, int n_out, const float* const* ins, int n_in, int64_t n, int groups,
+               hipStream_t s);
 
 }  // namespace sgd

@@ -511,10 +511,13 @@ __global__ void softmax_ce_kernel(const float* __restrict__ z, const int32_t* __
   for (int j = lane; j < C; j += 64) se += expf(zr[j] - m);
   se = wave_sum(se);
   nan = __any(nan);
-  const float lse = nan ? __builtin_nanf("") : m + logf(se);
   const int lbl = y[row];
+  // A label outside [0, C) is never used as an index: the row's loss and
+  // logit gradient become NaN instead.
+  const bool ok = (unsigned)lbl < (unsigned)C;
+  const float lse = (nan || !ok) ? __builtin_nanf("") : m + logf(se);
   for (int j = lane; j < C; j += 64) dz[(int64_t)row * C + j] = scale * (expf(zr[j] - lse) - (j == lbl ? 1.f : 0.f));
-  if (lane == 0) row_loss[row] = lse - zr[lbl];
+  if (lane == 0) row_loss[row] = lse - zr[ok ? lbl : 0];
 }
 
 // loss = scale * sum of row losses, one block, fixed reduction tree.

@@ -199,6 +199,7 @@ struct sgd_net {
   sgd::SideStream side;
   bool overlap = true;   // dedw products on the side stream
   bool implicit = true;  // implicit-GEMM convolutions where the shapes allow
+  bool debug = false;    // validate labels on the host before launching
 };
 
 namespace sgd {
@@ -854,9 +855,30 @@ int sgd_tensor_info(const sgd_net* net, int layer, int which, int64_t* byte_offs
   return SGD_OK;
 }
 
+// Debug mode: read the labels back (synchronously on `st`; null is the
+// default stream) and reject any outside [0, classes) before anything is
+// launched.
+static int check_labels(const sgd_net* net, const int32_t* y, hipStream_t st, const char* who) {
+  const int N = net->input.batch;
+  std::vector<int32_t> h;
+  try {
+    h.resize((size_t)N);
+  } catch (...) {
+    return fail(SGD_EINVAL, std::string(who) + ": out of host memory");
+  }
+  if (hipMemcpyAsync(h.data(), y, (size_t)N * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(SGD_EDEVICE, std::string(who) + ": reading the labels back failed");
+  for (int i = 0; i < N; ++i)
+    if (h[i] < 0 || h[i] >= net->classes)
+      return fail(SGD_EINVAL, std::string(who) + ": label " + std::to_string(h[i]) + " at row " + std::to_string(i) +
+                                  " is outside [0, " + std::to_string(net->classes) + ")");
+  return SGD_OK;
+}
+
 static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, bool accum,
                 const sgd_rule* rule, float* state, float* loss, void* ws, size_t ws_bytes, void* stream,
-                const char* who, float gscale = 1.f) {
+                const char* who, float gscale = 1.f, bool labels_checked = false) {
   if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, std::string(who) + ": null pointer");
   if ((int64_t)ws_bytes < net->ws_bytes)
     return fail(SGD_EWORKSPACE, std::string(who) + ": workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
@@ -864,6 +886,8 @@ static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, 
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SGD_EINVAL, std::string(who) + ": workspace not 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error from an unrelated earlier call
+  if (net->debug && !labels_checked)
+    if (int e = check_labels(net, y, st, who)) return e;
   sgd::g_prof = &net->prof;
   int e = SGD_OK;
   try {
@@ -956,6 +980,12 @@ int sgd_set_implicit_conv(sgd_net* net, int enable) {
   return plan_guarded(net);
 }
 
+int sgd_set_debug(sgd_net* net, int enable) {
+  if (!net) return fail(SGD_EINVAL, "sgd_set_debug: null net");
+  net->debug = enable != 0;
+  return SGD_OK;
+}
+
 int sgd_set_overlap(sgd_net* net, int enable) {
   if (!net) return fail(SGD_EINVAL, "sgd_set_overlap: null net");
   net->overlap = enable != 0;
@@ -1018,6 +1048,10 @@ int sgd_train_step_graph(sgd_net* net, float* W, const float* X, const int32_t* 
   // the dedw side stream and its fork/join events must exist before the capture starts
   if (net->overlap && net->side.ready((int)net->w_offs.size()))
     return fail(SGD_EDEVICE, std::string(who) + ": could not create the side stream");
+  // debug mode: the labels are checked once here, before the capture (a
+  // captured stream cannot be synchronised)
+  if (net->debug && y)
+    if (int e = check_labels(net, y, nullptr, who)) return e;
   hipStream_t cs = nullptr;
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
     return fail(SGD_EDEVICE, std::string(who) + ": hipStreamCreate failed");
@@ -1025,7 +1059,7 @@ int sgd_train_step_graph(sgd_net* net, float* W, const float* X, const int32_t* 
   if (hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed) != hipSuccess) {
     e = fail(SGD_EDEVICE, std::string(who) + ": hipStreamBeginCapture failed");
   } else {
-    e = step(net, W, X, y, W, false, rule, state, loss, ws, ws_bytes, cs, who);
+    e = step(net, W, X, y, W, false, rule, state, loss, ws, ws_bytes, cs, who, 1.f, true);
     hipGraph_t g = nullptr;
     const hipError_t ce = hipStreamEndCapture(cs, &g);  // always ends the capture
     if (!e && ce != hipSuccess) e = fail(SGD_EDEVICE, std::string(who) + ": hipStreamEndCapture failed");
@@ -1124,6 +1158,13 @@ int sgd_apply_fused(float* W, float* state, const float* const* grads, int k, in
 }
 
 }  // extern "C"
+
+extern "C" int sgd_stream_ref(float* const* outs, int n_out, const float* const* ins, int n_in, int64_t n,
+                              int groups, void* stream) {
+  if (!ins || (n_out > 0 && !outs)) return fail(SGD_EINVAL, "sgd_stream_ref: null pointer array");
+  (void)hipGetLastError();
+  return sgd::stream_ref(outs, n_out, ins, n_in, n, groups, static_cast<hipStream_t>(stream));
+}
 
 namespace sgd {
 sgd_input net_input(const sgd_net* net) { return net->input; }

@@ -174,6 +174,42 @@ __global__ void apply_scalar_kernel(float* __restrict__ W, float* __restrict__ s
   }
 }
 
+// Reference streaming kernel: outs[j] = ins[0] + ... + ins[K-1] (left fold)
+// for every output j < NOUT; with NOUT == 0 the sum is only kept live (a
+// store that never fires).  G float4 groups per thread, block-contiguous as
+// in the update kernels when G > 1, one float4 per thread when G == 1.  It
+// has the memory shape of the update kernels without their arithmetic or
+// state, and measures what that mix of read and write streams can reach.
+template <int K, int NOUT, int G>
+__global__ __launch_bounds__(kBlock) void stream_ref_kernel(Ptrs in, float* o0, float* o1,
+                                                            int64_t n4) {
+  int64_t idx[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    idx[u] = (int64_t)blockIdx.x * kBlock * G + u * kBlock + threadIdx.x;
+    if (idx[u] >= n4) idx[u] = -1;
+  }
+  v4f s[G];
+  v4f g[K][G];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int u = 0; u < G; ++u) g[j][u] = ld4(in.g[j], idx[u] < 0 ? 0 : idx[u]);
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    s[u] = g[0][u];
+#pragma unroll
+    for (int j = 1; j < K; ++j) s[u] = s[u] + g[j][u];
+  }
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    if (idx[u] < 0) continue;
+    if (NOUT >= 1) st4(o0, idx[u], s[u]);
+    if (NOUT >= 2) st4(o1, idx[u], s[u]);
+    if (NOUT == 0 && s[u].x == 1234567.f && s[u].y == -7654321.f) st4(o0, idx[u], s[u]);
+  }
+}
+
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int vec_grid(int64_t n) { return (int)std::max<int64_t>(1, ceil_div(n / 4, kChunk)); }
@@ -243,6 +279,53 @@ int accumulate(float* buf, const float* const* grads, int k, bool first_is_copy,
   }
   prof_end(s);
   return check_launch("accumulate");
+}
+
+int stream_ref(float* const* outs, int n_out, const float* const* ins, int n_in, int64_t n, int groups,
+               hipStream_t s) {
+  if (n <= 0 || n % 4) {
+    set_error("stream_ref: n must be a positive multiple of 4");
+    return SGD_EINVAL;
+  }
+  if (groups != 1 && groups != 4) {
+    set_error("stream_ref: groups per thread must be 1 or 4");
+    return SGD_EINVAL;
+  }
+  const bool shape_ok = (n_in == 1 && n_out == 1) || (n_in == 10 && (n_out == 0 || n_out == 2));
+  if (!shape_ok) {
+    set_error("stream_ref: supported (reads, writes): (1, 1), (10, 0), (10, 2)");
+    return SGD_EINVAL;
+  }
+  Ptrs P{};
+  for (int j = 0; j < n_in; ++j) {
+    if (!ins[j] || !a16(ins[j])) {
+      set_error("stream_ref: inputs must be 16-byte aligned device pointers");
+      return SGD_EINVAL;
+    }
+    P.g[j] = ins[j];
+  }
+  for (int j = 0; j < n_out; ++j)
+    if (!outs[j] || !a16(outs[j])) {
+      set_error("stream_ref: outputs must be 16-byte aligned device pointers");
+      return SGD_EINVAL;
+    }
+  float* o0 = n_out >= 1 ? outs[0] : const_cast<float*>(ins[0]);
+  float* o1 = n_out >= 2 ? outs[1] : o0;
+  const int64_t n4 = n / 4;
+  const int grid = (int)ceil_div(n4, (int64_t)kBlock * groups);
+  prof_begin("stream_ref", 0.0, 4.0 * (n_in + n_out) * (double)n, s);
+  auto go = [&](auto kc, auto oc) {
+    constexpr int K = decltype(kc)::value, NO = decltype(oc)::value;
+    if (groups == 1)
+      hipLaunchKernelGGL((stream_ref_kernel<K, NO, 1>), dim3(grid), dim3(kBlock), 0, s, P, o0, o1, n4);
+    else
+      hipLaunchKernelGGL((stream_ref_kernel<K, NO, 4>), dim3(grid), dim3(kBlock), 0, s, P, o0, o1, n4);
+  };
+  if (n_in == 1) go(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+  else if (n_out == 0) go(std::integral_constant<int, 10>{}, std::integral_constant<int, 0>{});
+  else go(std::integral_constant<int, 10>{}, std::integral_constant<int, 2>{});
+  prof_end(s);
+  return check_launch("stream_ref");
 }
 
 int apply_rule(float* W, float* state, const float* const* grads, int k, int64_t n, int rule, float eta, float mu,

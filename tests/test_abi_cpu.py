@@ -106,3 +106,53 @@ def test_host_side_argument_errors():
     assert L.sgd_apply_fused(dummy, dummy, arr, 3, 0, C.byref(mom), None) == S.EINVAL      # n = 0
     assert L.sgd_param_count(None) == -1
     assert L.sgd_workspace_bytes(None) == 0
+
+
+def test_empty_batch_and_sizes_rejected():
+    for nchw in ((0, 1, 28, 28), (16, 0, 28, 28), (16, 1, 0, 28)):
+        with pytest.raises(S.SgdError) as e:
+            S.Net(nchw, workloads.LENET5)
+        assert e.value.code == S.ESHAPE
+
+
+def test_set_debug_flag():
+    L = S.lib()
+    assert L.sgd_set_debug(None, 1) == S.EINVAL
+    wl = workloads.WORKLOADS["lenet5"]
+    net = S.Net((16,) + wl.chw, wl.layers)
+    net.set_debug(True)
+    net.set_debug(False)
+
+
+def test_binding_rejects_wrong_dtypes_and_lengths():
+    # argument marshalling checks, on host tensors (no compute call is made)
+    torch = pytest.importorskip("torch")
+    wl = workloads.WORKLOADS["lenet5"]
+    net = S.Net((16,) + wl.chw, wl.layers)
+    n = net.param_count()
+    W = torch.zeros(n)
+    X = torch.zeros(16, 1, 28, 28)
+    y = torch.zeros(16, dtype=torch.int32)
+    loss = torch.zeros(1)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    net._check_step(W, X, y, loss, ws)                       # well-formed: passes
+    bad = [
+        dict(y=torch.zeros(16, dtype=torch.int64)),          # torch.randint's default dtype
+        dict(y=torch.zeros(15, dtype=torch.int32)),
+        dict(W=torch.zeros(n - 1)),
+        dict(W=torch.zeros(n, dtype=torch.float64)),
+        dict(X=torch.zeros(16, 1, 28, 27)),
+        dict(loss=torch.zeros(0)),
+        dict(ws=torch.zeros(4)),
+    ]
+    for b in bad:
+        args = dict(W=W, X=X, y=y, loss=loss, ws=ws)
+        args.update(b)
+        with pytest.raises(ValueError):
+            net._check_step(args["W"], args["X"], args["y"], args["loss"], args["ws"])
+    with pytest.raises(ValueError):
+        net._check_step(W, X, y, loss, ws, state=torch.zeros(n - 4))
+    with pytest.raises(ValueError):
+        net._check_step(W, X, y, loss, ws, grad=torch.zeros(n + 1))
+    with pytest.raises(ValueError):
+        net._check_step(W, X, y, loss, ws, need_state=True)

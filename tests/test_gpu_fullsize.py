@@ -1,31 +1,37 @@
 """Full-size GPU parity, layer by layer, at the workloads' real shapes.
 
-The oracle cannot run these steps end to end in seconds, so each layer is
+The oracle cannot run the VGG steps end to end in seconds, so each layer is
 checked locally: the GPU's own input activation and upstream gradient (read
-from the workspace) are fed to the oracle's definitions, and the GPU's
-outputs are compared
-  * at sampled points for convolution / fc forward, dedw, dedb, dedx (the
-    oracle's single-output sums, or the fc loops on a row / column subset),
-    to max|d| <= 1e-4 max|ref| per layer;
-  * exactly over whole tensors for max-pooling forward (values and argmax)
-    and backward (routing and the ReLU mask), which involve no rounding;
-  * loss to 1e-5 relative and the logits' gradient from the GPU logits.
-Together these cover every step of the forward and backward pass at the
-sizes and launch configurations the benchmark times.
+from the workspace) are fed to the oracle's definitions (the direct
+convolution sums, the naive fc loops), and the GPU's outputs are compared to
+max|d| <= 1e-4 max|ref| with the scale taken from the oracle's values only:
+
+  * fc layers (forward, dW, db, dX): whole tensors;
+  * conv layers: whole output maps of a subset of output channels (forward),
+    whole dW rows [co][ci][ky][kx] and db of a subset of output channels (the
+    whole dW and db where the oracle's cost allows), whole input-gradient maps
+    of a subset of input channels (dedx_conv + col2im or the gathered dedx,
+    with the ReLU mask);
+  * max-pooling forward (values and argmax) and backward (routing and the
+    ReLU mask): exactly, over whole tensors;
+  * loss to 1e-5 relative, and the logits' gradient over the whole tensor.
+
+The timed path, sgd_train_step with the workload's rule in the dedw
+epilogues, is run from the same weights: its updated weights (and momentum)
+are compared with the oracle's rule applied to the oracle's dW and db, for
+every fc tensor and every checked conv row (tests/_util.update_tolerance).
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads
-from tests._util import LOSS_RTOL, nhwc_to_nchw
+from tests._util import GRAD_RTOL, LOSS_RTOL, check_update, nhwc_to_nchw
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import sgd_cnns_amd as S  # noqa: E402
-
-RTOL = 1e-4
 
 
 def _to_nchw(t, layout):
@@ -35,17 +41,21 @@ def _to_nchw(t, layout):
     return np.ascontiguousarray(a)
 
 
-def _close(name, got, ref, scale):
+def _close(name, got, ref):
+    """max|got - ref| <= 1e-4 max|ref|, the scale from the oracle's values alone."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite GPU values"
     err = np.abs(got - ref).max() if got.size else 0.0
-    scale = max(scale, np.abs(ref).max() if ref.size else 0.0)
-    assert err <= RTOL * scale + 1e-30, f"{name}: max|d| {err:.3e} > {RTOL} * {scale:.3e}"
+    scale = np.abs(ref).max() if ref.size else 0.0
+    assert err <= GRAD_RTOL * scale + 1e-30, f"{name}: max|d| {err:.3e} > {GRAD_RTOL} * {scale:.3e}"
     return err / scale if scale else 0.0
 
 
 class Step:
-    """One compute_gradient on the GPU with every workspace tensor readable."""
+    """One compute_gradient on the GPU with every workspace tensor readable, and the fused training
+    step (the benchmark's call) from the same weights."""
 
     def __init__(self, wl):
         self.wl = wl
@@ -59,10 +69,24 @@ class Step:
         assert bo == [self.onet.params[i][2] for i in sorted(self.onet.params)]
         dev = torch.device("cuda")
         self.ws = self.net.workspace()
+        Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+        # the timed call first: W1 (and V1) after one step with the workload's rule, state zero
+        self.rule = (wl.rule, wl.eta, wl.mu, wl.eps, 0.0)
+        W1 = torch.from_numpy(W).to(dev)
+        self.st0 = None if wl.rule == "plain" else np.zeros(W.size, np.float32) if wl.rule != "adagrad" else \
+            np.full(W.size, 0.1, np.float32)
+        st = None if self.st0 is None else torch.from_numpy(self.st0).to(dev)
+        loss1 = torch.empty(1, device=dev)
+        self.net.train_step(W1, Xd, yd, st, S.Rule(*self.rule), loss1, self.ws)
+        torch.cuda.synchronize()
+        self.W1 = W1.cpu().numpy()
+        self.st1 = None if st is None else st.cpu().numpy()
+        self.loss1 = float(loss1.item())
+        del W1, st
+        # then the gradient, whose workspace tensors are inspected
         grad = torch.empty(W.size, device=dev)
         loss = torch.empty(1, device=dev)
-        self.net.compute_gradient(torch.from_numpy(W).to(dev), torch.from_numpy(X).to(dev),
-                                  torch.from_numpy(y).to(dev), grad, loss, self.ws)
+        self.net.compute_gradient(torch.from_numpy(W).to(dev), Xd, yd, grad, loss, self.ws)
         torch.cuda.synchronize()
         self.grad = grad.cpu().numpy()
         self.loss = float(loss.item())
@@ -94,8 +118,35 @@ class Step:
             j -= 1
         return self.out_nchw(j), j
 
+    def check_update_rows(self, name, off, rows, g_ref_rows):
+        """The fused step's W (and state) at parameter rows `rows` of a tensor starting at `off`
+        (rows of length g_ref_rows.shape[1]) against the oracle's rule on the oracle's gradient."""
+        rule, eta, mu, eps, decay = self.rule
+        L = g_ref_rows.shape[1]
+        idx = (off + np.asarray(rows)[:, None] * L + np.arange(L)[None, :]).ravel()
+        g = np.ascontiguousarray(g_ref_rows, np.float32).ravel()
+        W0 = self.W[idx]
+        st0 = None if self.st0 is None else self.st0[idx]
+        W_ref = W0.copy()
+        st_ref = None if st0 is None else st0.copy()
+        O.apply_rule(rule, W_ref, st_ref, g, eta, mu, eps, decay)
+        return check_update(name, rule, g, W0, st0, W_ref, st_ref, self.W1[idx],
+                            None if self.st1 is None else self.st1[idx], eta, mu, decay)
 
-def check_step(wl, samples=24, seed=0):
+
+def _pick(r, n, count, always=()):
+    """`count` distinct indices in [0, n): the given ones (edges) first, then seeded random ones."""
+    if count == "all" or count >= n:
+        return list(range(n))
+    out = [a % n for a in always]
+    for v in r.permutation(n):
+        if len(set(out)) >= count:
+            break
+        out.append(int(v))
+    return sorted(set(out))
+
+
+def check_step(wl, fwd_ch=4, dw_ch=4, dx_ch=2, seed=0):
     st = Step(wl)
     r = np.random.default_rng(seed)
     layers = wl.layers
@@ -106,7 +157,8 @@ def check_step(wl, samples=24, seed=0):
     logits = st.out_nchw(last_fc)
     l_ref, dz_ref = O.softmax_ce(logits, st.y)
     assert abs(st.loss - l_ref) <= LOSS_RTOL * abs(l_ref), (st.loss, l_ref)
-    report["loss"] = _close("dlogits", st.dout_nchw(last_fc), dz_ref, 0.0)
+    assert st.loss1 == st.loss, "the fused step's forward pass differs from the gradient call's"
+    report["dlogits"] = _close("dlogits", st.dout_nchw(last_fc), dz_ref)
     for i, L in enumerate(layers):
         kind = L[0]
         if kind in ("relu", "softmax_ce"):
@@ -123,39 +175,32 @@ def check_step(wl, samples=24, seed=0):
             y_gpu = st.out_nchw(i)
             dy = st.dout_nchw(i)
             N, Ci, H, Wd = x_in.shape
-            Ho, Wo = y_gpu.shape[2:]
             xin = np.ascontiguousarray(x_in, np.float32)
-            # forward
-            pts = [(r.integers(N), r.integers(co_n), r.integers(Ho), r.integers(Wo)) for _ in range(samples)]
-            pts += [(0, 0, 0, 0), (N - 1, co_n - 1, Ho - 1, Wo - 1)]
-            ref = [O.conv_fwd_point(xin, w, b, P, *p) for p in pts]
+            # forward: whole output maps of a channel subset
+            cos = _pick(r, co_n, fwd_ch, (0, -1))
+            y_ref = O.conv_fwd(xin, w[cos], b[cos], P)
             if relu_after:
-                ref = [max(v, 0.0) for v in ref]
-            report[f"{i}.fwd"] = _close(f"layer {i} conv fwd", [y_gpu[p] for p in pts], ref, np.abs(y_gpu).max())
-            # dedw and dedb
+                y_ref = np.maximum(y_ref, 0)
+            report[f"{i}.fwd"] = _close(f"layer {i} conv fwd (out channels {cos})", y_gpu[:, cos], y_ref)
+            # dedw rows and dedb of a channel subset (all channels where affordable)
+            cos = _pick(r, co_n, dw_ch, (0, -1))
+            dw_ref, db_ref, _ = O.conv_bwd(xin, np.ascontiguousarray(w[cos]), np.ascontiguousarray(dy[:, cos]), P,
+                                           need_dx=False)
             g_w = st.grad[wo:wo + w.size].reshape(w.shape)
             g_b = st.grad[bo:bo + co_n]
-            qs = [(r.integers(co_n), r.integers(Ci), r.integers(c), r.integers(c)) for _ in range(samples)]
-            qs += [(0, 0, 0, 0), (co_n - 1, Ci - 1, c - 1, c - 1)]
-            ref = [O.conv_dw_point(np.ascontiguousarray(xin[:, q[1]:q[1] + 1]),
-                                   np.ascontiguousarray(dy[:, q[0]:q[0] + 1]), c, P, 0, 0, q[2], q[3]) for q in qs]
-            report[f"{i}.dw"] = _close(f"layer {i} conv dw", [g_w[q] for q in qs], ref, np.abs(g_w).max())
-            cos = sorted(set([0, co_n - 1] + list(r.integers(0, co_n, 8))))
-            ref = [O.conv_db_point(np.ascontiguousarray(dy[:, co:co + 1]), 0) for co in cos]
-            report[f"{i}.db"] = _close(f"layer {i} conv db", g_b[cos], ref, np.abs(g_b).max())
-            # dedx_conv + col2im (the gradient entering the previous stage)
+            report[f"{i}.dw"] = _close(f"layer {i} conv dw (rows {len(cos)})", g_w[cos], dw_ref)
+            report[f"{i}.db"] = _close(f"layer {i} conv db", g_b[cos], db_ref)
+            # the fused step's update of those rows
+            report[f"{i}.upd_w"] = st.check_update_rows(f"layer {i} conv W1", wo, cos, dw_ref.reshape(len(cos), -1))
+            report[f"{i}.upd_b"] = st.check_update_rows(f"layer {i} conv b1", bo, cos, db_ref.reshape(len(cos), 1))
+            # dedx_conv (+ col2im) over whole maps of an input-channel subset, ReLU mask of the layer below
             if i > first_w:
                 dx_gpu = st.dout_nchw(src)
-                pts = [(r.integers(N), r.integers(Ci), r.integers(H), r.integers(Wd)) for _ in range(samples)]
-                pts += [(0, 0, 0, 0), (N - 1, Ci - 1, H - 1, Wd - 1)]
-                ref = []
-                for (n, ci, iy, ix) in pts:
-                    v = O.conv_dx_point(np.ascontiguousarray(w[:, ci:ci + 1]), np.ascontiguousarray(dy[n:n + 1]),
-                                        (H, Wd), P, 0, 0, iy, ix)
-                    if src_masks and not x_in[n, ci, iy, ix] > 0:
-                        v = 0.0
-                    ref.append(v)
-                report[f"{i}.dx"] = _close(f"layer {i} conv dx", [dx_gpu[p] for p in pts], ref, np.abs(dx_gpu).max())
+                cis = _pick(r, Ci, dx_ch, (0, -1))
+                _, _, dx_ref = O.conv_bwd(np.ascontiguousarray(xin[:, cis]), np.ascontiguousarray(w[:, cis]), dy, P)
+                if src_masks:
+                    dx_ref = np.where(xin[:, cis] > 0, dx_ref, 0)
+                report[f"{i}.dx"] = _close(f"layer {i} conv dx (in channels {cis})", dx_gpu[:, cis], dx_ref)
         elif kind == "pool":
             p = L[1]
             pooled = st.out_nchw(i)
@@ -179,26 +224,27 @@ def check_step(wl, samples=24, seed=0):
             z_gpu = st.out_nchw(i)
             dz = st.dout_nchw(i)
             N = a.shape[0]
-            rows = sorted(set([0, N - 1] + list(r.integers(0, N, 6))))
-            z_ref = O.fc_fwd(a[rows], w, b)
+            z_ref = O.fc_fwd(a, w, b)
             if relu_after:
                 z_ref = np.maximum(z_ref, 0)
-            report[f"{i}.fwd"] = _close(f"layer {i} fc fwd", z_gpu[rows], z_ref, np.abs(z_gpu).max())
-            cols = sorted(set([0, out_n - 1] + list(r.integers(0, out_n, 6))))
-            dw_ref, db_ref, _ = O.fc_bwd(a, np.ascontiguousarray(w[cols]), np.ascontiguousarray(dz[:, cols]), False)
+            report[f"{i}.fwd"] = _close(f"layer {i} fc fwd", z_gpu, z_ref)
+            dw_ref, db_ref, da = O.fc_bwd(a, w, np.ascontiguousarray(dz), i > first_w)
             g_w = st.grad[wo:wo + w.size].reshape(w.shape)
             g_b = st.grad[bo:bo + out_n]
-            report[f"{i}.dw"] = _close(f"layer {i} fc dw", g_w[cols], dw_ref, np.abs(g_w).max())
-            report[f"{i}.db"] = _close(f"layer {i} fc db", g_b[cols], db_ref, np.abs(g_b).max())
+            report[f"{i}.dw"] = _close(f"layer {i} fc dw", g_w, dw_ref)
+            report[f"{i}.db"] = _close(f"layer {i} fc db", g_b, db_ref)
+            report[f"{i}.upd_w"] = st.check_update_rows(f"layer {i} fc W1", wo, np.arange(out_n), dw_ref)
+            report[f"{i}.upd_b"] = st.check_update_rows(f"layer {i} fc b1", bo, np.arange(out_n),
+                                                        db_ref.reshape(out_n, 1))
             if i > first_w:
-                _, _, da = O.fc_bwd(a[rows], w, np.ascontiguousarray(dz[rows]), True)
                 if src_masks:
-                    da = np.where(a[rows] > 0, da, 0)
+                    da = np.where(a > 0, da, 0)
                 dx_gpu = st.dout_nchw(src).reshape(N, -1)
-                report[f"{i}.dx"] = _close(f"layer {i} fc dx", dx_gpu[rows], da, np.abs(dx_gpu).max())
-    worst = max(report.values())
-    print(f"[fullsize] {wl.name}: loss {st.loss:.6f} (oracle from GPU logits {l_ref:.6f}); worst ratio {worst:.2e}",
-          flush=True)
+                report[f"{i}.dx"] = _close(f"layer {i} fc dx", dx_gpu, da)
+    worst = max(v for k, v in report.items() if not k.endswith(("upd_w", "upd_b")))
+    worst_u = max(v for k, v in report.items() if k.endswith(("upd_w", "upd_b")))
+    print(f"[fullsize] {wl.name}: loss {st.loss:.6f} (oracle from GPU logits {l_ref:.6f}); worst |d|/max|ref| "
+          f"{worst:.2e}; fused-step update worst |d|/bound {worst_u:.3f}", flush=True)
     return report
 
 
@@ -207,12 +253,13 @@ def test_mlp5000_full_batch():
 
 
 def test_vgg_cifar_full_batch():
-    check_step(workloads.WORKLOADS["vgg_cifar"])
+    # every conv layer's whole dW and db
+    check_step(workloads.WORKLOADS["vgg_cifar"], fwd_ch=8, dw_ch="all", dx_ch=4)
 
 
 def test_vgg16_full_batch():
-    check_step(workloads.WORKLOADS["vgg16"], samples=16)
+    check_step(workloads.WORKLOADS["vgg16"], fwd_ch=4, dw_ch=4, dx_ch=2)
 
 
 def test_lenet5_layerwise():
-    check_step(workloads.WORKLOADS["lenet5"])
+    check_step(workloads.WORKLOADS["lenet5"], fwd_ch="all", dw_ch="all", dx_ch="all")

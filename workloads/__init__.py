@@ -82,7 +82,7 @@ WORKLOADS = {
 # The parameter-server apply: a flat W of VGG-16's size, K gradient buffers
 # summed in a fixed order, then per-parameter Adagrad.
 PS_APPLY = dict(name="ps_adagrad", seed=5, n=138_357_544, k=8, grad_std=1e-3,
-                eta=0.01, eps=1e-8, acc0=0.1, steps=100)
+                eta=0.01, eps=1e-8, acc0=0.1, steps=100, pool=16)
 
 
 def rng(seed: int, tensor_id: int) -> np.random.Generator:
@@ -159,3 +159,19 @@ def make_inputs(wl: Workload):
 def ps_gradient(seed, j, n, std):
     """Gradient buffer j of the parameter-server workload: N(0, std^2)."""
     return normal(seed, 100 + j, n, std)
+
+
+def ps_pool(ps=None, count=None, threads=8):
+    """The pool of `count` (default ps["pool"]) gradient buffers of the parameter-server workload,
+    drawn in parallel host threads (each buffer is its own Philox stream, so the bits do not
+    depend on the thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+    ps = PS_APPLY if ps is None else ps
+    count = ps["pool"] if count is None else count
+    with ThreadPoolExecutor(max(1, min(threads, count))) as ex:
+        return list(ex.map(lambda j: ps_gradient(ps["seed"], j, ps["n"], ps["grad_std"]), range(count)))
+
+
+def ps_step_buffers(step, k, pool):
+    """Pool indices of the k fresh gradient buffers of step `step` (0-based), in fold order."""
+    return [(k * step + i) % pool for i in range(k)]
