@@ -315,7 +315,23 @@ __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
 // Specialised epilogues of one wavefront's TM x TN blocks; r0, c0 (its first
 // row and column) are wavefront-uniform.
-template <int TM, int TN, int EM>
+// Byte offset of lane (li, lh)'s first element (row 4*lh of the block, its column) in a dedw result
+// whose wavefront block starts at column c0: the plain column, or the permuted conv weight position;
+// kOffOut for a column past N (or past the permuted store's width).
+__device__ __forceinline__ uint32_t dw_lane_offset(const KArgs& p, int col, int lh, uint32_t ldc) {
+  bool ok = col < p.N;
+  uint32_t cb = (uint32_t)col;
+  if (p.perm_c > 0) {
+    ok = ok && col < p.perm_k;
+    const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
+    cb = (uint32_t)(ci * p.perm_c * p.perm_c + tap);
+  }
+  return ok ? (4u * lh * ldc + cb) * 4u : kOffOut;
+}
+
+// ONES_ONLY (dedw forms): only the ones column's results (the bias), when it falls in the wavefront's
+// blocks; the weight block was stored by store_wave_pre.
+template <int TM, int TN, int EM, bool ONES_ONLY = false>
 __device__ __forceinline__ void store_wave(const f32x16 (&acc)[TM][TN], const KArgs& p, int r0, int c0, int li,
                                            int lh) {
   const int rows = min(p.M - r0, TM * 32);
@@ -400,15 +416,8 @@ __device__ __forceinline__ void store_wave(const f32x16 (&acc)[TM][TN], const KA
     for (int c = 0; c < TN; ++c) {
       const int col = c0 + c * 32 + li;
       // Plain or permuted conv weight columns.
-      bool ok = col < p.N;
-      uint32_t cb = (uint32_t)col;
-      if (p.perm_c > 0) {
-        ok = ok && col < p.perm_k;
-        const int tap = col / p.perm_ci, ci = col - tap * p.perm_ci;
-        cb = (uint32_t)(ci * p.perm_c * p.perm_c + tap);
-      }
-      const uint32_t vo = ok ? (4u * lh * ldc + cb) * 4u : kOffOut;
-      if (c0 + c * 32 < p.N) {
+      const uint32_t vo = dw_lane_offset(p, col, lh, ldc);
+      if (!ONES_ONLY && c0 + c * 32 < p.N) {
 #pragma unroll
         for (int a = 0; a < TM; ++a) block(acc[a][c], a, rd, rs, vo, ldc);
       }
@@ -420,6 +429,67 @@ __device__ __forceinline__ void store_wave(const f32x16 (&acc)[TM][TN], const KA
       }
     }
   }
+}
+
+// Small-tile dedw epilogue with its memory operands loaded ahead (one 32x32 block per wavefront).
+// When a weight-gradient product has only a few k-slices per tile (an fc layer's dedw has k = the
+// batch), the product is short next to the round trips of its epilogue: the parameters and rule
+// state the wavefront updates (or the GradBuf values it adds to) are therefore loaded by
+// prefetch_params before the item's operand loads, so their latency overlaps the main loop, and
+// store_wave_pre finishes the block from those registers.  The ones column (bias) is finished by
+// store_wave<..., ONES_ONLY> with its own loads.
+template <int EM>
+__device__ __forceinline__ void prefetch_params(const KArgs& p, int r0, int c0, int li, int lh, float (&w)[16],
+                                                float (&st)[16]) {
+  const uint32_t ldc = (uint32_t)p.ldc;
+  const int rows = min(p.M - r0, 32);
+  const bool w_on = EM == EM_UPDATE || p.accum;
+  const bool st_on = EM == EM_UPDATE && p.ustate &&
+                     (p.urule == SGD_MOMENTUM || p.urule == SGD_ADAGRAD || p.urule == SGD_NESTEROV);
+  const brsrc rd = brsrc_rows(p.C + (int64_t)r0 * p.ldc, w_on ? rows : 0, ldc);
+  const brsrc rs = brsrc_rows(st_on ? p.ustate + (int64_t)r0 * p.ldc : p.C, st_on ? rows : 0, ldc);
+  const uint32_t vo = c0 < p.N ? dw_lane_offset(p, c0 + li, lh, ldc) : kOffOut;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t o = vo + blk_row(r) * ldc * 4u;
+    w[r] = bload(rd, o);
+    st[r] = bload(rs, o);
+  }
+}
+
+template <int EM>
+__device__ __forceinline__ void store_wave_pre(const f32x16 (&acc)[1][1], const KArgs& p, int r0, int c0, int li,
+                                               int lh, float (&w)[16], float (&st)[16]) {
+  if (c0 < p.N) {
+    const uint32_t ldc = (uint32_t)p.ldc;
+    const int rows = min(p.M - r0, 32);
+    const bool st_on = EM == EM_UPDATE && p.ustate;
+    const brsrc rd = brsrc_rows(p.C + (int64_t)r0 * p.ldc, rows, ldc);
+    const brsrc rs = brsrc_rows(st_on ? p.ustate + (int64_t)r0 * p.ldc : p.C, st_on ? rows : 0, ldc);
+    const uint32_t vo = dw_lane_offset(p, c0 + li, lh, ldc);
+    const f32x16& v = acc[0][0];
+    auto finish16 = [&](auto rule_c) {
+      constexpr int RULE = decltype(rule_c)::value;  // -1: store (with accumulation)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t o = vo + blk_row(r) * ldc * 4u;
+        if (RULE >= 0) {
+          rule1<(RULE >= 0 ? RULE : 0)>(w[r], st[r], v[r], p.eta, p.mu, p.eps, p.decay);
+        } else {
+          const float x = v[r] * p.gscale;
+          w[r] = p.accum ? w[r] + x : x;
+        }
+        bstore(w[r], rd, o);
+        if (RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD || RULE == SGD_NESTEROV) bstore(st[r], rs, o);
+      }
+    };
+    if (EM == EM_DW) finish16(std::integral_constant<int, -1>{});
+    else if (p.urule == SGD_PLAIN) finish16(std::integral_constant<int, SGD_PLAIN>{});
+    else if (p.urule == SGD_MOMENTUM) finish16(std::integral_constant<int, SGD_MOMENTUM>{});
+    else if (p.urule == SGD_NESTEROV) finish16(std::integral_constant<int, SGD_NESTEROV>{});
+    else finish16(std::integral_constant<int, SGD_ADAGRAD>{});
+  }
+  store_wave<1, 1, EM, true>(acc, p, r0, c0, li, lh);
 }
 
 // Generic epilogue: each 32x32 block of a wavefront is parked in the
@@ -549,6 +619,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr unsigned kOffBad = 0x80000000u;  // out-of-range buffer offset: the load returns zeros
 constexpr int kDmaBK = 16;
 constexpr int kDmaStages = 3;
+// Weight gradients with at most this many k-slices per tile (k <= 128: an fc layer's dedw at batch
+// <= 128) take 64x64 tiles and load their epilogue's memory operands ahead of the main loop.
+constexpr int kPrefetchSlices = 8;
 
 // Buffer resource over [base, base + 2 GiB): 64-bit base, stride 0, record
 // count, and the gfx9 data-format word.
@@ -898,6 +971,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
       for (int c = 0; c < TN; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+    // One 32x32 block per wavefront and a short reduction: the epilogue's parameter (and state)
+    // loads are issued now, ahead of the operands (see prefetch_params).
+    constexpr bool kPre = TM == 1 && TN == 1 && (EM == EM_UPDATE || EM == EM_DW);
+    const bool whole = k0 == 0 && k1 == s.ipt;
+    const bool pre = kPre && whole && s.ipt <= kPrefetchSlices && (EM == EM_UPDATE || p.accum);
+    float pre_w[16], pre_s[16];
+    if constexpr (kPre) {
+      if (pre) prefetch_params<EM>(p, m0 + wm * WM, n0 + wn * WN, li, lh, pre_w, pre_s);
+    }
     __syncthreads();  // every wave is done with the ring from the previous item
     // Prologue: slices 0 .. S-2 in flight.  Slices past the end of the item
     // read zeros, which keeps the per-thread load count (and so the vmcnt
@@ -935,10 +1017,17 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     }
     wait_vmcnt<0>();  // the trailing zero-fill loads land before the ring is reused
 
-    if (k0 == 0 && k1 == s.ipt) {
+    if (whole) {
       if (EM == EM_GENERIC) {
         __syncthreads();  // the ring is free for the epilogue's LDS blocks
         store_tile_generic<TM, TN>(acc, p, m0 + wm * WM, n0 + wn * WN, 0, li, lh, lds + wave * 1024);
+      } else if constexpr (kPre) {
+        if (pre) {
+          store_wave_pre<EM>(reinterpret_cast<const f32x16(&)[1][1]>(acc), p, m0 + wm * WM, n0 + wn * WN, li, lh,
+                             pre_w, pre_s);
+        } else {
+          store_wave<TM, TN, EM>(acc, p, m0 + wm * WM, n0 + wn * WN, li, lh);
+        }
       } else {
         store_wave<TM, TN, EM>(acc, p, m0 + wm * WM, n0 + wn * WN, li, lh);
       }
@@ -1332,12 +1421,15 @@ int staged_cfg(int M, int Nt) {
   return 0;
 }
 
-// Tile choice for gemm_dma: 128x128 unless one side of the output is narrow;
-// a weight gradient (form A^T B, not gathered) with both sides <= 64 -- a
-// first conv layer's, 64 x (27 + 1) at VGG -- takes 64x64, which wastes half
-// the matrix-core work 128x64 would.
-int dma_cfg(int M, int Nt, int form, bool gather) {
-  if (form == 1 && !gather && M <= 64 && Nt <= 64) return 3;
+// Tile choice for gemm_dma: 128x128 unless one side of the output is narrow.
+// A weight gradient (form A^T B, not gathered) takes 64x64 when both sides
+// are <= 64 -- a first conv layer's, 64 x (27 + 1) at VGG, where 128x64 would
+// waste half the matrix-core work -- or when its reduction is short (an fc
+// layer's dedw, k = the batch): then the product is bound by the epilogue's
+// parameter traffic, 64x64 tiles keep four times as many of them in flight,
+// and their epilogue operands are loaded ahead (prefetch_params).
+int dma_cfg(int M, int Nt, int K, int form, bool gather) {
+  if (form == 1 && !gather && ((M <= 64 && Nt <= 64) || ceil_div(K, kDmaBK) <= kPrefetchSlices)) return 3;
   if (Nt <= 64) return 1;
   if (M <= 64) return 2;
   return 0;
@@ -1404,7 +1496,7 @@ int gemm_pick_splits(int M, int Nt, int K) {
 int64_t gemm_scratch_floats(int M, int Nt, int K, bool a_t, bool b_t, bool fused, int splits) {
   const int64_t staged = splits > 1 ? (int64_t)splits * M * Nt : 0;
   (void)fused;
-  const int cfg = dma_cfg(M, Nt, form_of(a_t, b_t), false);
+  const int cfg = dma_cfg(M, Nt, K, form_of(a_t, b_t), false);
   const Cfg& c = kDma[cfg];
   const SkPlan p = sk_choose(tiles_of(c, M, Nt), ceil_div(K, kDmaBK), machine_for(cfg), (int64_t)c.bm * c.bn, INT64_MAX);
   const int64_t sk = p.sk_iters > 0 ? 2 * (int64_t)p.grid * c.bm * c.bn : 0;
@@ -1471,7 +1563,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     dma = false;
     cfg = d.cfg - kDmaConfigs;
   } else {
-    cfg = dma_cfg(d.M, a.Nt, form, d.gather != 0);
+    cfg = dma_cfg(d.M, a.Nt, d.K, form, d.gather != 0);
     dma = dma_ok(d);
     if (!dma) cfg = staged_cfg(d.M, a.Nt);
   }
