@@ -172,7 +172,10 @@ def test_compute_gradient_into_matches_compute_plus_accumulate():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(gb.data.cpu().numpy(), (g0 + g).astype(np.float32))
     bad = S.GradBuf(n - 1)
-    with pytest.raises(S.SgdError):
+    with pytest.raises(ValueError):        # the binding's length check
+        net.compute_gradient_into(Wd, Xd, yd, bad, loss, ws)
+    bad = S.GradBuf(n - 1, data=torch.empty(n, device=dev))
+    with pytest.raises(S.SgdError):        # the library's: the buffer's declared length is wrong
         net.compute_gradient_into(Wd, Xd, yd, bad, loss, ws)
 
 
