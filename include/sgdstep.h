@@ -379,6 +379,27 @@ int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, flo
                    float* loss, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sgd_train_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step, bitwise the same W, state and loss, with no workspace
+ * argument.  The workspace lives in a static device array of
+ * SGD_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds
+ * until the process ends; the call makes no hipMalloc / hipFree and creates
+ * no stream or event (every dedw product runs on `stream`, which gives the
+ * same results as the overlapped step).  The array's address on the current
+ * device is looked up once, on the first call on that device.  Every call on
+ * one GPU shares that GPU's array and nothing in it needs to start at zero:
+ * calls that overlap on one GPU (different streams, threads or processes'
+ * shared contexts) race and give undefined results -- serialise them.  Errors:
+ * SGD_EWORKSPACE when sgd_workspace_bytes(net) exceeds the array, SGD_EINVAL
+ * (null net, bad rule, profiling on), SGD_EDEVICE, and those of
+ * sgd_train_step.
+ */
+#define SGD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sgd_train_step_noalloc(sgd_net* net, float* W, const float* X, const int32_t* y, float* state,
+                           const sgd_rule* rule, float* loss, void* stream);
+
+/*
  * SPRINT on one GPU (SPRINT report section 3.4, Algorithms 1 and 2): worker
  * threads, each with its own HIP stream, copy of the weights, gradient
  * array Grad and gradient buffer GradBuf_t with the empty flag, and one

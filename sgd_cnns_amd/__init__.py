@@ -35,7 +35,8 @@ EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_of
            "sgd_accumulate_grads",
            "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_debug", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
            "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_train_step_graph", "sgd_step_graph_launch",
-           "sgd_step_graph_destroy", "sgd_stream_ref", "sgd_last_error"]
+           "sgd_step_graph_destroy", "sgd_stream_ref", "sgd_train_step_noalloc", "sgd_last_error"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SgdLayer(C.Structure):
@@ -128,6 +129,7 @@ def lib():
             "sgd_step_graph_launch": (i, [P, P]),
             "sgd_step_graph_destroy": (None, [P]),
             "sgd_stream_ref": (i, [C.POINTER(P), i, C.POINTER(P), i, i64, i, P]),
+            "sgd_train_step_noalloc": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P]),
             "sgd_last_error": (C.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -338,6 +340,14 @@ class Net:
         self._check_step(W, X, y, loss, ws, state=state, need_state=rule.rule != PLAIN)
         _check(lib().sgd_train_step(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(state), C.byref(rule), _ptr(loss),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+    def train_step_noalloc(self, W, X, y, state, rule, loss, stream=None):
+        """train_step with the library's static scratch as the workspace (sgd_train_step_noalloc)."""
+        _require_cuda(W, X, y, state, loss)
+        self._check_step(W, X, y, loss, None, state=state, need_state=rule.rule != PLAIN)
+        _check(lib().sgd_train_step_noalloc(self._h, _ptr(W), _ptr(X), _ptr(y), _ptr(state), C.byref(rule),
+                                            _ptr(loss), _stream(stream)))
 
 
 class StepGraph:

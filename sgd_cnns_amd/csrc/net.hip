@@ -12,6 +12,7 @@
 // section 3.3 SGEMM table.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -595,18 +596,18 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
 // stream joins the side stream at the end, so the step stays one stream-
 // ordered operation for the caller.
 int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, bool accum, const sgd_rule* rule,
-                 float* state, float gscale, void* ws, hipStream_t st) {
+                 float* state, float gscale, void* ws, hipStream_t st, bool overlap) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_off);
   float* partial_dw = reinterpret_cast<float*>(static_cast<char*>(ws) + net->partial_dw_off);
   float* dcol = reinterpret_cast<float*>(static_cast<char*>(ws) + net->dcol_off);
   auto& stages = net->stages;
   int weighted = 0;
   for (const Stage& s : stages) weighted += (s.kind == SGD_FC || s.kind == SGD_CONV);
-  if (net->overlap && net->side.ready(weighted)) return fail(SGD_EDEVICE, "backward: could not create the side stream");
-  const hipStream_t side = net->overlap ? net->side.s : st;
+  if (overlap && net->side.ready(weighted)) return fail(SGD_EDEVICE, "backward: could not create the side stream");
+  const hipStream_t side = overlap ? net->side.s : st;
   int fork_i = 0;
   auto fork = [&]() -> int {
-    if (!net->overlap) return 0;
+    if (!overlap) return 0;
     hipEvent_t ev = net->side.ev[fork_i++];
     if (hipEventRecord(ev, st) != hipSuccess || hipStreamWaitEvent(side, ev, 0) != hipSuccess)
       return fail(SGD_EDEVICE, "backward: fork to the side stream failed");
@@ -618,7 +619,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
   // stream's last ones.
   auto launch_dw = [&](GemmDesc& g, const Stage& s) -> int {
     if (s.dw_main) {
-      g.partial = net->overlap ? partial : partial_dw;
+      g.partial = overlap ? partial : partial_dw;
       g.partial_floats = s.dw_cap;
       return gemm(g, st);
     }
@@ -765,7 +766,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
   }
   // Join even after an error, so nothing enqueued on the side stream is left
   // unordered with the caller's stream.
-  if (!net->overlap) return e;
+  if (!overlap) return e;
   hipEvent_t join = net->side.ev[weighted];
   if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess)
     return e ? e : fail(SGD_EDEVICE, "backward: join of the side stream failed");
@@ -878,7 +879,7 @@ static int check_labels(const sgd_net* net, const int32_t* y, hipStream_t st, co
 
 static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, float* grad, bool accum,
                 const sgd_rule* rule, float* state, float* loss, void* ws, size_t ws_bytes, void* stream,
-                const char* who, float gscale = 1.f, bool labels_checked = false) {
+                const char* who, float gscale = 1.f, bool labels_checked = false, bool serial = false) {
   if (!net || !W || !X || !y || !grad || !loss || !ws) return fail(SGD_EINVAL, std::string(who) + ": null pointer");
   if ((int64_t)ws_bytes < net->ws_bytes)
     return fail(SGD_EWORKSPACE, std::string(who) + ": workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
@@ -892,7 +893,7 @@ static int step(sgd_net* net, const float* W, const float* X, const int32_t* y, 
   int e = SGD_OK;
   try {
     e = sgd::run_forward(net, W, X, y, loss, ws, st);
-    if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, gscale, ws, st);
+    if (!e) e = sgd::run_backward(net, W, X, grad, accum, rule, state, gscale, ws, st, net->overlap && !serial);
   } catch (...) {
     e = fail(SGD_EINVAL, std::string(who) + ": out of host memory");
   }
@@ -1031,6 +1032,55 @@ int sgd_train_step(sgd_net* net, float* W, const float* X, const int32_t* y, flo
                    float* loss, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_rule(rule, state, "sgd_train_step")) return e;
   return step(net, W, X, y, W, false, rule, state, loss, ws, ws_bytes, stream, "sgd_train_step");
+}
+
+// ---------------------------------------------- allocation-free step ----
+// The device memory sgd_train_step_noalloc uses in place of a caller
+// workspace: one static array per GPU the library runs on, held until the
+// process ends.  Host code never passes `scratch` itself (in host code that
+// name is a host-side stand-in, not a device address): it uses the address
+// hipGetSymbolAddress reports for the current device, looked up once per
+// device and kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[SGD_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[kMaxDevices] = {};
+
+static int scratch_addr(void** out, const char* who) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(SGD_EDEVICE, std::string(who) + ": no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(SGD_EDEVICE, std::string(who) + ": hipGetSymbolAddress of the static scratch failed: " +
+                                   hipGetErrorString(e));
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SGD_OK;
+}
+
+int sgd_train_step_noalloc(sgd_net* net, float* W, const float* X, const int32_t* y, float* state,
+                           const sgd_rule* rule, float* loss, void* stream) {
+  const char* who = "sgd_train_step_noalloc";
+  if (!net) return fail(SGD_EINVAL, std::string(who) + ": null net");
+  if (int e = check_rule(rule, state, who)) return e;
+  if (net->prof.on) return fail(SGD_EINVAL, std::string(who) + ": profiling is on (its events are created on demand)");
+  if (net->ws_bytes > (int64_t)SGD_NOALLOC_SCRATCH_BYTES)
+    return fail(SGD_EWORKSPACE, std::string(who) + ": the net needs " + std::to_string(net->ws_bytes) +
+                                    " bytes of workspace; the static scratch holds " +
+                                    std::to_string((long long)SGD_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (int e = scratch_addr(&ws, who)) return e;
+  // every dedw product on the caller's stream: no side stream or event is created
+  return step(net, W, X, y, W, false, rule, state, loss, ws, SGD_NOALLOC_SCRATCH_BYTES, stream, who, 1.f, false,
+              true);
 }
 
 struct sgd_step_graph {
