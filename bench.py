@@ -184,7 +184,8 @@ def step_bench(wl, steps, warmup, use_graph=True):
     net.profile(True)
     prof_ms, _ = timed(eager, steps)
     net.profile(False)
-    kern = kernel_totals(net.profile_read())
+    prof_recs = net.profile_read()
+    kern = kernel_totals(prof_recs)
     # the same with the dedw products on the caller's stream (no overlap): each kernel has the GPU to
     # itself, so its event time is its own duration; eq. (4) models this serial sum
     reps = max(3, min(steps, 10))
@@ -224,7 +225,7 @@ def step_bench(wl, steps, warmup, use_graph=True):
     del ws, gb
     torch.cuda.empty_cache()
     return dict(ms=ms, eager_ms=eager_ms, graph_ms=graph_ms, graph=use_g, prof_ms=prof_ms, iso_ms=iso_ms,
-                kern=kern, kern_iso=kern_iso, iso_recs=iso_recs, n_params=n, losses=losses,
+                kern=kern, kern_iso=kern_iso, iso_recs=iso_recs, prof_recs=prof_recs, n_params=n, losses=losses,
                 update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * statistics.fmean(upd),
                         "GB/s": upd_b / (statistics.fmean(upd) / 1e3) / 1e9},
                 unfused_ms=unf)
@@ -297,6 +298,33 @@ def roofline_of(kern, name, steps):
                "frac": ach / PEAK_HBM_GBS, "bytes_per_launch": d["bytes"] / d["launches"]}
     out.update({"launches": d["launches"], "launches_per_step": d["launches"] / steps,
                 "avg_launch_us": 1e3 * d["ms"] / d["launches"]})
+    return out
+
+
+def per_product(recs, steps):
+    """The last recorded step's launches grouped by matrix product (main kernel + stream-K fixup +
+    split-K reduce) and other kernels, in launch order: [phase, layer, kernels, m, n, k, us, TFLOP/s or
+    GB/s].  The last step, because the first one after an idle GPU runs slower."""
+    per = max(1, len(recs) // steps)
+    out = []
+    by = {}
+    for (name, layer, phase, ms, flops, nbytes, shape) in recs[len(recs) - per:]:
+        m, n, k, pid = shape
+        if pid < 0:
+            out.append([phase, layer, name, 0, 0, 0, round(1e3 * ms, 1), round(nbytes / (ms / 1e3) / 1e9, 1)])
+            continue
+        if pid not in by:
+            by[pid] = [phase, layer, name, m, n, k, 0.0, 0.0]
+            out.append(by[pid])
+        e = by[pid]
+        if name != e[2] and name not in e[2].split("+"):
+            e[2] += "+" + name
+        e[6] += 1e3 * ms
+        e[7] += flops if is_product(name) else 0.0
+    for e in out:
+        if e[3]:
+            e[7] = round(e[7] / (e[6] / 1e6) / 1e12, 1)
+            e[6] = round(e[6], 1)
     return out
 
 
@@ -448,6 +476,7 @@ def ps_bench(steps=100, reps=20):
                      "GB/s": rb / rms / 1e6, "frac_hbm_peak": rb / rms / 1e6 / PEAK_HBM_GBS}
     ceiling = max(ref["stream_10r2w_g1"]["GB/s"], ref["stream_10r2w_g4"]["GB/s"])
     gbs = nbytes / st["mean"] / 1e6
+    traffic, source = measured_traffic("apply_kernel<2, 8>", "ps_adagrad")
     del bufs, gb
     torch.cuda.empty_cache()
     return {"workload": (f"ps_adagrad: {n} parameters, K={k} fresh seeded gradient buffers N(0, 1e-3^2) per step "
@@ -459,7 +488,8 @@ def ps_bench(steps=100, reps=20):
             "bytes_per_step": nbytes, "GB/s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
             "roofline": {"bound": "hbm", "kernel": "apply_kernel<2, 8> (sgd_apply_fused, Adagrad, K = 8)",
                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                         "bytes_per_launch": nbytes, "avg_launch_us": 1e3 * st["mean"]},
+                         "bytes_per_launch": nbytes, "avg_launch_us": 1e3 * st["mean"], "traffic": traffic,
+                         "traffic_source": source if traffic is not None else f"null: {source}"},
             "frac_of_stream_10r2w_ceiling": gbs / ceiling,
             "stream_ref": ref,
             "unfused": {"chain": "accumulate copy + 7 accumulate adds + apply_update (Adagrad)",
@@ -838,6 +868,157 @@ def sprint_report(out_path, workload="mlp5000"):
 
 
 
+# --------------------------------------------------------------- rocprofv3 summaries ----
+_EM_NAMES = {"0": "generic", "1": "store", "2": "bias", "3": "mask", "4": "dw", "5": "update"}
+
+
+def bench_kernel_name(instance):
+    """The name the library's profiler gives a launch of this kernel instance (as printed by
+    rocprofv3, demangled), or the instance itself for kernels outside the products."""
+    import re
+    m = re.search(r"gemm_(dma|staged)<(\d+), (\d+), (?:(\d+), )?(true|false), (true|false), (\d+)"
+                  r"(?:, (true|false), (true|false))?>", instance)
+    if not m:
+        m2 = re.search(r"(\w+)<", instance) or re.search(r"(\w+)\(", instance)
+        return m2.group(1) if m2 else instance
+    fam, bm, bn, _bk, at, bt, em, ga, gb = m.groups()
+    if ga == "true":
+        return f"gemm_conv_{'fwd' if em == '2' else 'dx'}_{bm}x{bn}"
+    if gb == "true":
+        return f"gemm_conv_dw_{bm}x{bn}"
+    form = {("false", "false"): "nt", ("true", "true"): "tn", ("false", "true"): "nn", ("true", "false"): "tt"}[(at, bt)]
+    return f"gemm_{fam}_{bm}x{bn}_{form}"
+
+
+def short_instance(name):
+    import re
+    m = re.search(r"(\w+<[^()]*>)", name)
+    return m.group(1) if m else name.split("(")[0]
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def summarize_stats(directory, out_md, title, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv)."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    L = [f"# rocprofv3 kernel statistics — {title}", "", "Command (repository root, one MI355X):", "", "```",
+         command, "```", "", "Every dispatch of the run (warm-up, timed steps, graph replays, the event-bracketed "
+         "and no-overlap passes, the unfused reference).  The library's own name for each instance is in "
+         "parentheses.", "", "| kernel | calls | avg µs | total ms | % |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:40]:
+        inst = short_instance(r["Name"])
+        L.append(f"| `{inst}` ({bench_kernel_name(r['Name'])}) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                 f"{float(r['TotalDurationNs']) / 1e6:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f} |")
+    open(out_md, "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
+def _counter_table(directory, counter):
+    """{instance: [per-dispatch values]} of one counter, and the calibration copy's value (the largest
+    copy-kernel dispatch)."""
+    per = {}
+    copy = 0.0
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in name or "copy_kernel" in name:
+            copy = max(copy, v)
+        per.setdefault(name, []).append(v)
+    return per, copy
+
+
+def summarize_traffic(fetch_dir, write_dir, workload, calib_mib, out_md, out_json, command):
+    """HBM bytes per dispatch from a FETCH_SIZE pass and a WRITE_SIZE pass (KiB per dispatch), each
+    scaled so the calibration copy of calib_mib MiB counts its bytes once, per kernel instance; merged
+    into out_json under the workload (with a hash of the kernel sources)."""
+    import hashlib
+    f, fcopy = _counter_table(fetch_dir, "FETCH_SIZE")
+    w, wcopy = _counter_table(write_dir, "WRITE_SIZE")
+    nbytes = calib_mib * 2 ** 20
+    fs = nbytes / (fcopy * 1024) if fcopy else 1.0
+    ws = nbytes / (wcopy * 1024) if wcopy else 1.0
+    src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", x), "rb").read() for x in ("gemm.hip", "update.hip"))
+    kern = {}
+    for inst, vals in f.items():
+        if "copyBuffer" in inst or "copy_kernel" in inst:
+            continue
+        name = bench_kernel_name(inst) if ("gemm_dma<" in inst or "gemm_staged<" in inst) else short_instance(inst)
+        fb = 1024 * fs * statistics.fmean(vals)
+        wb = 1024 * ws * statistics.fmean(w.get(inst, [0.0]))
+        rec = {"instance": short_instance(inst), "dispatches": len(vals), "fetch_bytes": fb, "write_bytes": wb,
+               "traffic_bytes": fb + wb}
+        if name not in kern or kern[name]["dispatches"] < len(vals):
+            kern[name] = rec
+    entry = {"workload": workload, "source_sha256(gemm.hip+update.hip)": hashlib.sha256(src).hexdigest(),
+             "fetch_scale": fs, "write_scale": ws,
+             "calibration": f"one {calib_mib} MiB device copy in the same runs", "command": command, "kernels": kern}
+    old = json.load(open(out_json)) if os.path.exists(out_json) else []
+    old = old if isinstance(old, list) else [old]
+    old = [e for e in old if e.get("workload") != workload] + [entry]
+    json.dump(old, open(out_json, "w"), indent=1)
+    L = [f"# HBM traffic per launch — {workload} (FETCH_SIZE / WRITE_SIZE)", "",
+         "Commands (repository root, one MI355X; two separate counter passes, then this summary):", "", "```",
+         command, "```", "",
+         f"Calibration: the same runs copy {calib_mib} MiB once; FETCH_SIZE is scaled by {fs:.3f} and WRITE_SIZE by "
+         f"{ws:.3f} so that copy counts its bytes once.  FETCH_SIZE counts L2-to-fabric reads, so Infinity Cache "
+         "(MALL) hits are included.  Averages over every dispatch of the instance.", "",
+         "| kernel (instance) | dispatches | fetch MB/launch | write MB/launch | traffic MB/launch |",
+         "|---|---|---|---|---|"]
+    for name, r in sorted(kern.items(), key=lambda kv: -kv[1]["traffic_bytes"] * kv[1]["dispatches"])[:25]:
+        L.append(f"| `{name}` (`{r['instance']}`) | {r['dispatches']} | {r['fetch_bytes'] / 1e6:.1f} | "
+                 f"{r['write_bytes'] / 1e6:.1f} | {r['traffic_bytes'] / 1e6:.1f} |")
+    open(out_md, "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
+def summarize_mfma(directory, out_md, title, command, min_us=50.0):
+    """Matrix-core busy fraction and clock per GEMM instance from GRBM_GUI_ACTIVE and
+    SQ_VALU_MFMA_BUSY_CYCLES (one pass)."""
+    rows = _csv_rows(directory, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        d = by.setdefault(key, {"dur": (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for (name, _), d in by.items():
+        if "GRBM_GUI_ACTIVE" not in d or "SQ_VALU_MFMA_BUSY_CYCLES" not in d or d["dur"] < min_us:
+            continue
+        a = agg.setdefault(name, {"n": 0, "dur": 0.0, "clk": 0.0, "busy": 0.0})
+        a["n"] += 1
+        a["dur"] += d["dur"]
+        gui = d["GRBM_GUI_ACTIVE"] / 8.0          # the counter sums the 8 XCDs
+        a["clk"] += gui / d["dur"]               # cycles per microsecond = MHz
+        a["busy"] += d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024.0)
+    L = [f"# Matrix-core busy fraction and clock — {title}", "", "Command (repository root, one MI355X):", "", "```",
+         command, "```", "",
+         "Per GEMM instance, averaged over its dispatches: duration from the counter run's timestamps; clock = "
+         "GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs) over that duration; matrix cores busy = "
+         "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).  Dispatches under "
+         f"{min_us:.0f} µs are left out (the timestamps do not bracket them closely).", "",
+         "| kernel | dispatches | avg µs | MHz | MFMA busy % |", "|---|---|---|---|---|"]
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["dur"]):
+        if not name.startswith(("void sgd", "sgd")) and "gemm" not in name:
+            continue
+        L.append(f"| `{short_instance(name)}` ({bench_kernel_name(name)}) | {a['n']} | {a['dur'] / a['n']:.1f} | "
+                 f"{a['clk'] / a['n']:.0f} | {100 * a['busy'] / a['n']:.1f} |")
+    open(out_md, "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def step_record(wl, r, steps, fit, cpu):
     """The JSON record of one step workload."""
     ms = r["ms"]
@@ -882,6 +1063,10 @@ def step_record(wl, r, steps, fit, cpu):
                         "note": "standalone apply after gradient-into-GradBuf (the unfused pair); the timed step "
                                 "applies the rule in the dedw epilogues"},
         "eq4": eq4_record(fit, r["iso_recs"], len(r["iso_ms"]), statistics.fmean(r["iso_ms"]), st["mean"]),
+        "products_fields": ["phase (0 fwd, 1 bwd)", "layer", "kernels", "m", "n", "k", "us",
+                            "TFLOP/s (products) or GB/s (others)"],
+        "products": per_product(r["prof_recs"], steps),
+        "products_isolated": per_product(r["iso_recs"], len(r["iso_ms"])),
         "cpu_baseline": cpu,
     }
     return rec
@@ -906,7 +1091,23 @@ def main():
                     help="also save the timing model's raw grid times and step records under this prefix")
     ap.add_argument("--sprint", metavar="OUT_MD", default=None,
                     help="run SPRINT's asynchronous workers and updater (Algorithms 1 and 2) and write the report")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
+                    help="summarize rocprofv3 output instead of running: 'stats DIR OUT.md TITLE', "
+                         "'traffic FETCH_DIR WRITE_DIR WORKLOAD CALIB_MIB OUT.md OUT.json', 'mfma DIR OUT.md TITLE' "
+                         "(with --summary-command giving the command text to record)")
+    ap.add_argument("--summary-command", default="", help="the command(s) that produced the summarized output")
     args = ap.parse_args()
+    if args.summarize:
+        kind, rest = args.summarize[0], args.summarize[1:]
+        if kind == "stats":
+            summarize_stats(rest[0], rest[1], rest[2], args.summary_command)
+        elif kind == "traffic":
+            summarize_traffic(rest[0], rest[1], rest[2], int(rest[3]), rest[4], rest[5], args.summary_command)
+        elif kind == "mfma":
+            summarize_mfma(rest[0], rest[1], rest[2], args.summary_command)
+        else:
+            raise SystemExit(f"unknown summary kind {kind}")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this build runs the step on a "
