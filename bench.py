@@ -879,8 +879,7 @@ def bench_kernel_name(instance):
     m = re.search(r"gemm_(dma|staged)<(\d+), (\d+), (?:(\d+), )?(true|false), (true|false), (\d+)"
                   r"(?:, (true|false), (true|false))?>", instance)
     if not m:
-        m2 = re.search(r"(\w+)<", instance) or re.search(r"(\w+)\(", instance)
-        return m2.group(1) if m2 else instance
+        return short_instance(instance).split("<")[0]
     fam, bm, bn, _bk, at, bt, em, ga, gb = m.groups()
     if ga == "true":
         return f"gemm_conv_{'fwd' if em == '2' else 'dx'}_{bm}x{bn}"
@@ -891,9 +890,14 @@ def bench_kernel_name(instance):
 
 
 def short_instance(name):
-    import re
-    m = re.search(r"(\w+<[^()]*>)", name)
-    return m.group(1) if m else name.split("(")[0]
+    """A demangled kernel name without its return type, namespaces and parameter list."""
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    n = n.split("(")[0]
+    for ns in ("sgd::", "at::native::"):
+        n = n.replace(ns, "")
+    return n.strip()
 
 
 def _csv_rows(directory, suffix):
@@ -953,7 +957,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, calib_mib, out_md, out_jso
     src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", x), "rb").read() for x in ("gemm.hip", "update.hip"))
     kern = {}
     for inst, vals in f.items():
-        if "copyBuffer" in inst or "copy_kernel" in inst:
+        if "sgd::" not in inst:   # the library's kernels only (not the calibration copy or torch's own)
             continue
         name = bench_kernel_name(inst) if ("gemm_dma<" in inst or "gemm_staged<" in inst) else short_instance(inst)
         fb = 1024 * fs * statistics.fmean(vals)
