@@ -201,7 +201,7 @@ def test_compute_gradient_into_vgg_split_k_paths():
 
 
 @pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad", "nesterov_wd"])
-@pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged", "mlp5000"])
+@pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged", "mlp5000", "mlp_k320"])
 def test_train_step_equals_gradient_then_apply(rule, case):
     # the fused step (update applied in the dedw epilogues / split-K reduction)
     # must give bitwise the same W and optimizer state as gradient-into-GradBuf
@@ -213,6 +213,9 @@ def test_train_step_equals_gradient_then_apply(rule, case):
     elif case == "mlp_ragged":
         wl = workloads.Workload("mlp_ragged", 31, 70, (3072, 1, 1),
                                 [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)])
+    elif case == "mlp_k320":   # fc weight gradients with k = 320: whole tiles and a stream-K remainder
+        wl = workloads.Workload("mlp_k320", 33, 320, (3072, 1, 1),
+                                [("fc", 4096), ("relu",), ("fc", 4096), ("relu",), ("fc", 10), ("softmax_ce",)])
     else:
         wl = workloads.WORKLOADS["mlp5000"]
     print(f"[train_step] {case} {rule}", flush=True)
@@ -392,3 +395,39 @@ def test_implicit_and_explicit_conv_agree():
     np.testing.assert_array_equal(ga[w0:b0 + nb], gb[w0:b0 + nb])
     per_tensor_grad_check(ga, gb.astype(np.float32), wo, bo, W.size)
     assert neta.workspace_bytes() < netb.workspace_bytes()
+
+
+@pytest.mark.parametrize("rule", ["momentum", "adagrad"])
+def test_train_step_explicit_conv_matches_unfused(rule):
+    """With implicit convolution off, a conv layer's weight gradient is an ungathered product with the
+    permuted [co][ci][ky][kx] store, with the update in its epilogue (VGG-CIFAR, batch 2).  Bitwise
+    equal to gradient + apply, and the gradient itself against the oracle."""
+    wl = workloads.WORKLOADS["vgg_cifar"].with_batch(2)
+    print(f"[explicit-conv train_step] {rule}", flush=True)
+    X, y, W = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    net.set_implicit_conv(False)
+    n = net.param_count()
+    dev = torch.device("cuda")
+    Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+    st0 = workloads.normal(9, 3, n, 1e-3)
+    if rule == "adagrad":
+        st0 = np.abs(st0) + np.float32(0.1)
+    R = S.Rule(rule, 0.01, 0.9, 1e-8)
+    ws = net.workspace()
+    la, lb = torch.empty(1, device=dev), torch.empty(1, device=dev)
+    Wa, sa = torch.from_numpy(W).to(dev), torch.from_numpy(st0).to(dev)
+    gb = S.GradBuf(n)
+    net.compute_gradient_into(Wa, Xd, yd, gb, la, ws)
+    g = gb.data.clone()
+    S.apply_update(Wa, gb, sa, R)
+    Wb, sb = torch.from_numpy(W).to(dev), torch.from_numpy(st0).to(dev)
+    net.train_step(Wb, Xd, yd, sb, R, lb, ws)
+    torch.cuda.synchronize()
+    assert la.item() == lb.item()
+    assert torch.equal(Wa, Wb) and torch.equal(sa, sb)
+    onet = O.OracleNet(wl.chw, wl.layers)
+    _, g_ref = onet.gradient(W, X, y)
+    wo = [onet.params[i][0] for i in sorted(onet.params)]
+    bo = [onet.params[i][2] for i in sorted(onet.params)]
+    per_tensor_grad_check(g.cpu().numpy(), g_ref, wo, bo, n)

@@ -244,6 +244,52 @@ def test_mlp5000_config_full_batch_matches_oracle():
         W_prev, V_prev = W_gpu, V_gpu
 
 
+# An fc net whose weight gradients have k = 320 (20 slices of 16): 4096 x 4097 and 4096 x 3073
+# products with the update in their epilogue, more tiles than resident blocks, so whole tiles and a
+# stream-K remainder (partial sums reduced by the fix-up kernel, which applies the rule) both occur.
+MLP_K320 = workloads.Workload("mlp_k320", 33, 320, (3072, 1, 1),
+                            [("fc", 4096), ("relu",), ("fc", 4096), ("relu",), ("fc", 10), ("softmax_ce",)])
+
+
+@pytest.mark.parametrize("rname", ["momentum", "adagrad", "nesterov_wd"])
+def test_fc_update_k320_matches_oracle(rname):
+    """Two training steps of MLP_K320 against the oracle's backward chain on the GPU's activations (the
+    batch is large enough for ReLU-kink flips, see _mlp_chain) followed by the oracle's rule."""
+    wl = MLP_K320
+    spec = RULES[rname]
+    print(f"[mlp_k320] {rname}", flush=True)
+    X, y, W0 = workloads.make_inputs(wl)
+    net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    onet = O.OracleNet(wl.chw, wl.layers)
+    n = net.param_count()
+    w_offs, b_offs = net.param_offsets()
+    st0 = initial_state(spec[0], n, 77)
+    dev = torch.device("cuda")
+    Wd = torch.from_numpy(W0).to(dev)
+    sd = None if st0 is None else torch.from_numpy(st0).to(dev)
+    Xd, yd = torch.from_numpy(X).to(dev), torch.from_numpy(y).to(dev)
+    loss = torch.empty(1, device=dev)
+    ws = net.workspace()
+    rule = S.Rule(*spec)
+    W_prev, st_prev = W0, st0
+    for step in range(2):
+        net.train_step(Wd, Xd, yd, sd, rule, loss, ws)
+        torch.cuda.synchronize()
+        W_gpu, st_gpu, l_gpu = Wd.cpu().numpy(), sd.cpu().numpy(), float(loss.item())
+        l_pure, g_ref, flips = _mlp_chain(onet, net, ws, W_prev, X, y, wl.layers)
+        assert abs(l_gpu - l_pure) <= LOSS_RTOL * abs(l_pure), (l_gpu, l_pure)
+        W_ref, st_ref = W_prev.copy(), st_prev.copy()
+        O.apply_rule(spec[0], W_ref, st_ref, g_ref, *spec[1:])
+        worst = 0.0
+        for name, a, b in tensor_bounds(w_offs, b_offs, n):
+            sl = slice(a, b)
+            worst = max(worst, check_update(f"mlp_k320 {rname} step {step + 1} {name}", spec[0], g_ref[sl],
+                                            W_prev[sl], st_prev[sl], W_ref[sl], st_ref[sl], W_gpu[sl], st_gpu[sl],
+                                            spec[1], spec[2], spec[4]))
+        print(f"[mlp_k320] step {step + 1}: worst |d|/bound {worst:.3f}; mask flips {flips}", flush=True)
+        W_prev, st_prev = W_gpu, st_gpu
+
+
 def test_debug_mode_rejects_bad_labels_before_launch():
     """A host-built out-of-range label: in debug mode the call returns SGD_EINVAL and launches nothing
     (W untouched); in normal mode the softmax kernel never indexes with it and the loss is NaN."""
