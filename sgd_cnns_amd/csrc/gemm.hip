@@ -949,6 +949,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     const int nsl = k1 - k0;
     const int arows = p.M - m0, brows = p.N - n0;
     const int ones_col = (p.Nt > p.N && p.N >= n0 && p.N < n0 + BN) ? p.N - n0 : -1;
+    // The wavefront's 32 x 32 blocks that lie wholly outside the output (in the ragged last tile row
+    // or column) skip their matrix-core work: nothing stores them, and the matrix cores they would
+    // occupy are shared with the other resident blocks.  (128 x 128 tiles only: in the narrower
+    // instances the second loop copy costs the registers of a fourth wavefront per SIMD.)
+    constexpr bool kSkip = TM == 2 && TN == 2;
+    const int na = kSkip ? __builtin_amdgcn_readfirstlane(min(TM, max(0, (arows - wm * WM + 31) >> 5))) : TM;
+    const int nc = kSkip ? __builtin_amdgcn_readfirstlane(min(TN, max(0, (p.Nt - n0 - wn * WN + 31) >> 5))) : TN;
     const i32x4 ra = buffer_rsrc(GA ? p.A : AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
     const i32x4 rb = buffer_rsrc(GB ? p.B : BT ? p.B + (int64_t)kbeg * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + kbeg);
     const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
@@ -989,30 +996,69 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
       load_a(As[st], st * kDmaBK);
       load_b(Bs[st], st * kDmaBK);
     }
-    for (int i = 0; i < nsl; ++i) {
-      const int cur = i % kDmaStages;
-      wait_vmcnt<kLoads * (kDmaStages - 2)>();  // this thread's loads of slice i are in LDS
-      if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval);
-      lds_barrier();  // everyone's loads of slice i landed; everyone finished slice i-1
-      const int nx = i + kDmaStages - 1;  // refill the buffer slice i-1 used
-      load_a(As[nx % kDmaStages], nx * kDmaBK);
-      load_b(Bs[nx % kDmaStages], nx * kDmaBK);
+    // The slice loop, once with every block's matrix-core work and once (edge tiles) without the
+    // blocks outside the output; two copies so the interior tiles' loop has no branches.  The
+    // narrower instances keep the plain loop written out below (through the lambda they compile
+    // to more registers).
+    auto slices = [&](auto skip_tag) {
+      constexpr bool SKIP = decltype(skip_tag)::value;
+      for (int i = 0; i < nsl; ++i) {
+        const int cur = i % kDmaStages;
+        wait_vmcnt<kLoads * (kDmaStages - 2)>();  // this thread's loads of slice i are in LDS
+        if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval);
+        lds_barrier();  // everyone's loads of slice i landed; everyone finished slice i-1
+        const int nx = i + kDmaStages - 1;  // refill the buffer slice i-1 used
+        load_a(As[nx % kDmaStages], nx * kDmaBK);
+        load_b(Bs[nx % kDmaStages], nx * kDmaBK);
 #pragma unroll
-      for (int g = 0; g < kDmaBK / 8; ++g) {
-        float4 av[TM], bv[TN];
+        for (int g = 0; g < kDmaBK / 8; ++g) {
+          float4 av[TM], bv[TN];
 #pragma unroll
-        for (int a = 0; a < TM; ++a) av[a] = SA::operand(As[cur], wm * WM + a * 32 + li, g, lh);
+          for (int a = 0; a < TM; ++a) av[a] = SA::operand(As[cur], wm * WM + a * 32 + li, g, lh);
 #pragma unroll
-        for (int c = 0; c < TN; ++c) bv[c] = SB::operand(Bs[cur], wn * WN + c * 32 + li, g, lh);
+          for (int c = 0; c < TN; ++c) bv[c] = SB::operand(Bs[cur], wn * WN + c * 32 + li, g, lh);
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
+          for (int a = 0; a < TM; ++a)
 #pragma unroll
-          for (int c = 0; c < TN; ++c) {
-            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].x, bv[c].x, acc[a][c], 0, 0, 0);
-            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].y, bv[c].y, acc[a][c], 0, 0, 0);
-            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].z, bv[c].z, acc[a][c], 0, 0, 0);
-            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].w, bv[c].w, acc[a][c], 0, 0, 0);
-          }
+            for (int c = 0; c < TN; ++c) {
+              if (SKIP && (a >= na || c >= nc)) continue;
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].x, bv[c].x, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].y, bv[c].y, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].z, bv[c].z, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].w, bv[c].w, acc[a][c], 0, 0, 0);
+            }
+        }
+      }
+    };
+    if constexpr (kSkip) {
+      if (na < TM || nc < TN) slices(std::true_type{});
+      else slices(std::false_type{});
+    } else {
+      for (int i = 0; i < nsl; ++i) {  // the same loop as `slices`, without the skip
+        const int cur = i % kDmaStages;
+        wait_vmcnt<kLoads * (kDmaStages - 2)>();
+        if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval);
+        lds_barrier();
+        const int nx = i + kDmaStages - 1;
+        load_a(As[nx % kDmaStages], nx * kDmaBK);
+        load_b(Bs[nx % kDmaStages], nx * kDmaBK);
+#pragma unroll
+        for (int g = 0; g < kDmaBK / 8; ++g) {
+          float4 av[TM], bv[TN];
+#pragma unroll
+          for (int a = 0; a < TM; ++a) av[a] = SA::operand(As[cur], wm * WM + a * 32 + li, g, lh);
+#pragma unroll
+          for (int c = 0; c < TN; ++c) bv[c] = SB::operand(Bs[cur], wn * WN + c * 32 + li, g, lh);
+#pragma unroll
+          for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int c = 0; c < TN; ++c) {
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].x, bv[c].x, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].y, bv[c].y, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].z, bv[c].z, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a].w, bv[c].w, acc[a][c], 0, 0, 0);
+            }
+        }
       }
     }
     wait_vmcnt<0>();  // the trailing zero-fill loads land before the ring is reused
