@@ -876,6 +876,9 @@ def bench_kernel_name(instance):
     """The name the library's profiler gives a launch of this kernel instance (as printed by
     rocprofv3, demangled), or the instance itself for kernels outside the products."""
     import re
+    ms = re.search(r"dw_short<(\d+), \d+, -?\d+>", instance)
+    if ms:
+        return f"gemm_dw_short_k{2 * int(ms.group(1))}"
     m = re.search(r"gemm_(dma|staged)<(\d+), (\d+), (?:(\d+), )?(true|false), (true|false), (\d+)"
                   r"(?:, (true|false), (true|false))?>", instance)
     if not m:

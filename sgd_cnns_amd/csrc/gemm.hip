@@ -1177,6 +1177,127 @@ __global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int
   }
 }
 
+// ---- Short-reduction weight gradients: dW = dY^T X with k <= 32 (an fc layer at a small batch).
+//
+// With so few k the product is a stream over W and the rule's state: the operands dY and X are a
+// few MB that stay in the caches, and the matrix-core work is a small part of the time.  So there
+// is no LDS ring.  A wavefront keeps its 32 rows of dY for the whole reduction in registers and
+// walks a run of 32-column blocks of W; for NBLK blocks at a time it issues every load first
+// (X's columns, and the W / state / GradBuf values it updates), then the products, the rule and
+// the stores.  With no LDS and few registers many wavefronts are resident, and their loads keep
+// HBM busy.  In the MFMA's result layout a lane holds one column of the block, so every load and
+// store instruction covers two whole 128-byte runs of W rows.
+constexpr int kShortK = 32;  // the largest reduction dw_short takes
+struct ShortArgs {
+  int MB, NB;  // 32-row blocks of W; 32-column blocks (the ones column included)
+  int MG;      // groups of 4 row blocks: one workgroup of 4 wavefronts each
+  int per;     // column blocks per workgroup
+};
+
+// KP: k pairs (k <= 2 KP); RULE: -1 stores (or accumulates) the gradient, else the update rule
+// applied in place of the store.
+template <int KP, int NBLK, int RULE>
+__global__ __launch_bounds__(kThreads, KP * NBLK > 16 ? 3 : 4) void dw_short(KArgs p, ShortArgs s) {
+  constexpr bool kState = RULE == SGD_MOMENTUM || RULE == SGD_ADAGRAD || RULE == SGD_NESTEROV;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int li = lane & 31, lh = lane >> 5;
+  const int mb = (int)(blockIdx.x % (unsigned)s.MG) * 4 + wave;
+  const int nb0 = (int)(blockIdx.x / (unsigned)s.MG) * s.per, nb1 = min(s.NB, nb0 + s.per);
+  if (mb >= s.MB || nb0 >= nb1) return;
+  const int m0 = mb * 32;
+  const int rows = min(p.M - m0, 32);
+  const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb, ldc = (uint32_t)p.ldc;
+  const bool ones = p.ones_out != nullptr;
+  const bool need_w = RULE >= 0 || p.accum;
+  // Operands: dY [K][lda] and X [K][ldb]; k >= K lies past the records (reads 0).
+  const brsrc ra = brsrc_rows(p.A, p.K, lda);
+  const brsrc rb = brsrc_rows(p.B, p.K, ldb);
+  // W (or the GradBuf) and the state from the wavefront's first row, and the ones column's bias
+  // (and its state): rows past M lie past the records (read 0, stores dropped).
+  const brsrc rw = brsrc_rows(p.C + (int64_t)m0 * p.ldc, rows, ldc);
+  const brsrc rs = brsrc_rows(kState ? p.ustate + (int64_t)m0 * p.ldc : p.C, kState ? rows : 0, ldc);
+  const brsrc rbw = brsrc_rows(ones ? p.ones_out + m0 : p.C, ones ? rows : 0, 1);
+  const brsrc rbs = brsrc_rows(kState && p.ustate_b ? p.ustate_b + m0 : p.C, kState && p.ustate_b ? rows : 0, 1);
+  float dy[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j)
+    dy[j] = bload(ra, m0 + li < p.M ? ((uint32_t)(2 * j + lh) * lda + (uint32_t)(m0 + li)) * 4u : kOffOut);
+
+  for (int nb = nb0; nb < nb1; nb += NBLK) {
+    float xb[NBLK][KP], wv[NBLK][16], sv[NBLK][16];
+    // Every load of the NBLK blocks first (a block past the run reads nothing).
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const int n = nb + b < nb1 ? (nb + b) * 32 + li : INT_MAX;
+#pragma unroll
+      for (int j = 0; j < KP; ++j)
+        xb[b][j] = bload(rb, n < p.N ? ((uint32_t)(2 * j + lh) * ldb + (uint32_t)n) * 4u : kOffOut);
+      const uint32_t vo = n < p.N ? ((uint32_t)(4 * lh) * ldc + (uint32_t)n) * 4u : kOffOut;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t o = vo == kOffOut ? kOffOut : vo + (uint32_t)blk_row(r) * ldc * 4u;
+        wv[b][r] = need_w ? bload(rw, o) : 0.f;
+        sv[b][r] = kState ? bload(rs, o) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const int n0 = nb + b < nb1 ? (nb + b) * 32 : INT_MAX / 2;
+      const int n = n0 + li;
+      // The ones column (bias): X reads 1 for every k < K.
+      const bool ones_blk = ones && p.N >= n0 && p.N < n0 + 32;
+      if (ones_blk && n == p.N) {
+#pragma unroll
+        for (int j = 0; j < KP; ++j) xb[b][j] = 2 * j + lh < p.K ? 1.f : 0.f;
+      }
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KP; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(dy[j], xb[b][j], acc, 0, 0, 0);
+      // Lane (li, lh) holds column n of rows m0 + 4 lh + blk_row(r).
+      const uint32_t vo = n < p.N ? ((uint32_t)(4 * lh) * ldc + (uint32_t)n) * 4u : kOffOut;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t o = vo == kOffOut ? kOffOut : vo + (uint32_t)blk_row(r) * ldc * 4u;
+        float w = wv[b][r], st = sv[b][r];
+        if constexpr (RULE >= 0) {
+          rule1<(RULE >= 0 ? RULE : 0)>(w, st, acc[r], p.eta, p.mu, p.eps, p.decay);
+        } else {
+          const float x = acc[r] * p.gscale;
+          w = p.accum ? w + x : x;
+        }
+        bstore(w, rw, o);
+        if (kState) bstore(st, rs, o);
+      }
+      // The bias: the ones column's results, in the lane that holds column N.
+      if (ones_blk) {
+        const uint32_t ob = n == p.N ? (uint32_t)(4 * lh) * 4u : kOffOut;
+        float bw[16], bs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t o = ob == kOffOut ? kOffOut : ob + (uint32_t)blk_row(r) * 4u;
+          bw[r] = (RULE >= 0 || p.accum) ? bload(rbw, o) : 0.f;
+          bs[r] = kState ? bload(rbs, o) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t o = ob == kOffOut ? kOffOut : ob + (uint32_t)blk_row(r) * 4u;
+          if constexpr (RULE >= 0) {
+            rule1<(RULE >= 0 ? RULE : 0)>(bw[r], bs[r], acc[r], p.eta, p.mu, p.eps, p.decay);
+          } else {
+            const float x = acc[r] * p.gscale;
+            bw[r] = p.accum ? bw[r] + x : x;
+          }
+          bstore(bw[r], rbw, o);
+          if (kState) bstore(bs[r], rbs, o);
+        }
+      }
+    }
+  }
+}
+
 // Sum split-K partial tiles in slice order, then store: the ones column to
 // ones_out, the conv weight gradient permuted, anything else through the
 // epilogue.
@@ -1559,6 +1680,60 @@ int gemm(const GemmDesc& d, hipStream_t s) {
   return e;
 }
 
+// dw_short takes a weight gradient (A^T B, not gathered, plain store, accumulation or update rule)
+// whose reduction is at most kShortK, with 16-byte-aligned rows of W (and of the state) and
+// operand records within the 2 GiB a buffer resource addresses.
+bool short_dw_ok(const GemmDesc& d, int form) {
+  if (form != 1 || d.gather || d.perm_c > 0 || d.epi != EPI_STORE) return false;
+  if (d.K < 1 || d.K > kShortK || d.M < 1 || d.N < 1) return false;
+  if (d.lda < d.M || d.ldb < d.N || d.ldc < d.N) return false;
+  if (d.N % 4 || d.ldc % 4 || !aligned16(d.C)) return false;
+  const bool st = d.urule == SGD_MOMENTUM || d.urule == SGD_ADAGRAD || d.urule == SGD_NESTEROV;
+  if (st && (!d.ustate || !aligned16(d.ustate))) return false;
+  const int64_t lim = 0x7ffffff0;
+  return 4 * (int64_t)d.K * d.lda <= lim && 4 * (int64_t)d.K * d.ldb <= lim && 4 * 32 * d.ldc <= lim;
+}
+
+typedef void (*ShortKernel)(KArgs, ShortArgs);
+// Blocks per batch of loads: one for the rules with a state array (their W and state loads fill
+// the 128 registers of 4 wavefronts per SIMD), two for the others when a wavefront walks at
+// least 4 blocks (at k = 32 that takes 3 wavefronts per SIMD; VGG-16's 4096 x 25088 fc weight
+// gradient: 148 us against 157 with one), else one.
+template <int KP>
+ShortKernel short_fn(int urule, bool two) {
+  switch (urule) {
+    case SGD_PLAIN: return two ? dw_short<KP, 2, SGD_PLAIN> : dw_short<KP, 1, SGD_PLAIN>;
+    case SGD_MOMENTUM: return dw_short<KP, 1, SGD_MOMENTUM>;
+    case SGD_NESTEROV: return dw_short<KP, 1, SGD_NESTEROV>;
+    case SGD_ADAGRAD: return dw_short<KP, 1, SGD_ADAGRAD>;
+    default: return two ? dw_short<KP, 2, -1> : dw_short<KP, 1, -1>;
+  }
+}
+
+// One workgroup covers 4 row blocks and a run of `per` column blocks; the runs are sized so the
+// grid is about one round of the resident workgroups (one per wavefront slot of a SIMD).
+int dw_short_launch(const GemmDesc& d, KArgs a, double flops, double bytes, hipStream_t s) {
+  a.C = d.C;
+  a.ldc = d.ldc;
+  ShortArgs sa{};
+  sa.MB = (int)ceil_div(d.M, 32);
+  sa.NB = (int)ceil_div(a.Nt, 32);
+  sa.MG = (int)ceil_div(sa.MB, 4);
+  const int cus = machine_for(0).cus;
+  const bool st = d.urule == SGD_MOMENTUM || d.urule == SGD_ADAGRAD || d.urule == SGD_NESTEROV;
+  const int64_t blocks = (int64_t)sa.MG * sa.NB;  // per wavefront slot of a workgroup
+  const bool two = !st && blocks >= 4 * 4 * (int64_t)cus;
+  const int occ = two && d.K > 16 ? 3 : 4;  // wavefronts per SIMD the instance's registers allow
+  sa.per = (int)std::max<int64_t>(1, ceil_div(blocks, (int64_t)cus * occ));
+  const int64_t grid = (int64_t)sa.MG * ceil_div(sa.NB, sa.per);
+  const bool k16 = d.K <= 16;
+  const ShortKernel fn = k16 ? short_fn<8>(d.urule, two) : short_fn<16>(d.urule, two);
+  prof_begin(k16 ? "gemm_dw_short_k16" : "gemm_dw_short_k32", flops, bytes, s);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, s, a, sa);
+  prof_end(s);
+  return check_launch("gemm_dw_short");
+}
+
 int gemm_launch(const GemmDesc& d, hipStream_t s) {
   const bool ones = d.ones_out != nullptr;
   KArgs a{};
@@ -1629,6 +1804,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
   const double out_words = (double)d.M * a.Nt;
   const double out_passes = d.urule >= 0 ? (d.urule == SGD_PLAIN ? 2.0 : 4.0) : d.accum ? 2.0 : 1.0;
   const double bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + out_passes * out_words);
+  if (d.cfg < 0 && short_dw_ok(d, form)) return dw_short_launch(d, a, flops, bytes, s);
 
   // gemm_dma schedule.  The plan depends only on the shape and the machine
   // (the instance without an update rule sets the occupancy), so a product

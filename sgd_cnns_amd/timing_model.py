@@ -123,7 +123,9 @@ def family_for(form, m, n, k):
 
 def family_of_kernel(name):
     """"staged" for the staged kernels, "dma" for the direct-load ones (the
-    gathered convolution kernels share their main loop)."""
+    gathered convolution kernels share their main loop, and the streaming
+    weight-gradient kernel of short reductions is what the library picks for
+    the same aligned operands)."""
     return "staged" if name.startswith("gemm_staged_") else "dma"
 
 
@@ -131,6 +133,8 @@ def form_of_kernel(name):
     """The product form of a GEMM kernel name, e.g. gemm_dma_128x128_tn -> "tn"."""
     if name.startswith("gemm_conv_"):
         return _CONV_FORMS[name.split("_")[2]]
+    if name.startswith("gemm_dw_short_"):
+        return "tn"
     suffix = name.rsplit("_", 1)[-1]
     if name.startswith(("gemm_dma_", "gemm_staged_")) and suffix in FORMS:
         return suffix

@@ -76,6 +76,37 @@ def test_gemm_matches_oracle(form, m, n, k, pad):
     assert np.all(err <= bound), f"max err / bound = {worst:.3f}"
 
 
+# Short reductions (k <= 32) in the tn form, with n and C's row stride multiples of 4 and 16-byte aligned
+# rows, take the streaming weight-gradient kernel: ragged m, odd k, k at the 16 / 32 boundaries, a single
+# k, VGG-16's fc weight-gradient shapes at batch 32.  C's 4 padding columns (a 16-byte run) must stay
+# untouched.
+SHORT = [(1000, 36, 4, 0), (77, 132, 31, 4), (120, 400, 16, 0), (33, 8, 1, 0), (10, 4, 17, 4), (300, 516, 3, 0),
+         (4096, 4096, 32, 0), (1000, 4096, 32, 0), (65, 25088, 32, 0)]
+
+
+@pytest.mark.parametrize("m,n,k,pad", SHORT)
+def test_gemm_short_reduction_matches_oracle(m, n, k, pad):
+    print(f"[gemm short] m={m} n={n} k={k} pad={pad}", flush=True)
+    seed = 60 + m % 5
+    A = stored(seed, 0, k, m, pad)
+    B = stored(seed, 1, k, n, pad)
+    opA = A[:, :m].T.astype(np.float64)
+    opBt = B[:, :n].T.astype(np.float64)
+    ref = O.fc_fwd(opA, opBt, np.zeros(n), dtype=np.float64)
+    bound = k * U / (1 - k * U) * O.fc_fwd(np.abs(opA), np.abs(opBt), np.zeros(n), dtype=np.float64)
+    Cfull = torch.full((m, n + 4), float("nan"), device="cuda")
+    nbytes = S.gemm_workspace_bytes(m, n, k, True, True)
+    ws = torch.empty(max(nbytes, 4) // 4, device="cuda")
+    S.gemm(on_device(A, m), on_device(B, n), Cfull[:, :n], True, True, ws)
+    torch.cuda.synchronize()
+    got = Cfull.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(got[:, n:])), "padding columns of C were written"
+    err = np.abs(got[:, :n] - ref)
+    assert np.all(np.isfinite(got[:, :n]))
+    worst = float((err / np.maximum(bound, 1e-300)).max())
+    assert np.all(err <= bound), f"max err / bound = {worst:.3f}"
+
+
 def test_gemm_rejects_bad_arguments():
     """Argument errors are caught on the host, before any launch."""
     m, n, k = 128, 128, 30000
@@ -123,6 +154,8 @@ def test_profile_records_carry_product_shapes():
                    ("tn", 10, 33, batch), ("nn", batch, 32, 10),      # layer 2 dedw(+dedb), dedx
                    ("tn", 32, inp + 1, batch)])                      # layer 1 dedw(+dedb)
     assert got == want
+    # batch 8: both weight gradients are short reductions, on the streaming kernel
+    assert all(kn.startswith("gemm_dw_short_") for p in prods if p["form"] == "tn" for kn in p["kernels"]), prods
     assert others, "the softmax and loss kernels are recorded outside the products"
     for (name, _l, _p, ms, _f, _b, shape) in recs:
         assert ms >= 0
