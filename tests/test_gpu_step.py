@@ -201,7 +201,7 @@ def test_compute_gradient_into_vgg_split_k_paths():
 
 
 @pytest.mark.parametrize("rule", ["plain", "momentum", "adagrad", "nesterov_wd"])
-@pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged", "mlp5000", "mlp_k320"])
+@pytest.mark.parametrize("case", ["lenet5", "vgg_cifar_b2", "mlp_ragged", "mlp5000", "mlp_k320", "mlp_b32"])
 def test_train_step_equals_gradient_then_apply(rule, case):
     # the fused step (update applied in the dedw epilogues / split-K reduction)
     # must give bitwise the same W and optimizer state as gradient-into-GradBuf
@@ -213,6 +213,9 @@ def test_train_step_equals_gradient_then_apply(rule, case):
     elif case == "mlp_ragged":
         wl = workloads.Workload("mlp_ragged", 31, 70, (3072, 1, 1),
                                 [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)])
+    elif case == "mlp_b32":    # k = 32: the short-reduction weight-gradient kernel, one and two blocks per batch
+        wl = workloads.Workload("mlp_b32", 35, 32, (3072, 1, 1),
+                                [("fc", 4096), ("relu",), ("fc", 4096), ("relu",), ("fc", 10), ("softmax_ce",)])
     elif case == "mlp_k320":   # fc weight gradients with k = 320: whole tiles and a stream-K remainder
         wl = workloads.Workload("mlp_k320", 33, 320, (3072, 1, 1),
                                 [("fc", 4096), ("relu",), ("fc", 4096), ("relu",), ("fc", 10), ("softmax_ce",)])

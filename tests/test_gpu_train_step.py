@@ -41,6 +41,10 @@ NETS = {
                                      [("fc", 300), ("relu",), ("fc", 129), ("relu",), ("fc", 10), ("softmax_ce",)]),
     "vgg_cifar_b2": workloads.WORKLOADS["vgg_cifar"].with_batch(2),
     "implicit_conv": workloads.Workload("implicit_conv", 41, 3, (3, 10, 10), IMPLICIT_NET),
+    # k = 32: every fc weight gradient on the short-reduction kernel, 4096 x 4096 with two column blocks per
+    # batch of loads (plain SGD), the others one
+    "mlp_b32": workloads.Workload("mlp_b32", 35, 32, (3072, 1, 1),
+                                  [("fc", 4096), ("relu",), ("fc", 4096), ("relu",), ("fc", 10), ("softmax_ce",)]),
 }
 
 # (rule, eta, mu, eps, decay)
