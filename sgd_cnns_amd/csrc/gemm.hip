@@ -1690,8 +1690,10 @@ bool short_dw_ok(const GemmDesc& d, int form) {
   if (d.N % 4 || d.ldc % 4 || !aligned16(d.C)) return false;
   const bool st = d.urule == SGD_MOMENTUM || d.urule == SGD_ADAGRAD || d.urule == SGD_NESTEROV;
   if (st && (!d.ustate || !aligned16(d.ustate))) return false;
+  // Operand offsets are formed for every k < kShortK (those at k >= K fall past the records and
+  // read 0), so kShortK rows of each operand must stay within 32-bit offsets below 2 GiB.
   const int64_t lim = 0x7ffffff0;
-  return 4 * (int64_t)d.K * d.lda <= lim && 4 * (int64_t)d.K * d.ldb <= lim && 4 * 32 * d.ldc <= lim;
+  return 4 * (int64_t)kShortK * d.lda <= lim && 4 * (int64_t)kShortK * d.ldb <= lim && 4 * 32 * d.ldc <= lim;
 }
 
 typedef void (*ShortKernel)(KArgs, ShortArgs);
