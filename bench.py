@@ -113,6 +113,7 @@ def step_bench(wl, steps, warmup, use_graph=True):
     dev = torch.device("cuda")
     X, y, W = workloads.make_inputs(wl)
     net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+    overlap = net.overlap  # the library's default for this net (dedw products on a second stream or not)
     n = net.param_count()
     W0 = torch.from_numpy(W).to(dev)
     Wd = W0.clone()
@@ -196,7 +197,7 @@ def step_bench(wl, steps, warmup, use_graph=True):
     iso_ms, _ = timed(eager, reps)
     net.profile(False)
     iso_recs = net.profile_read()
-    net.set_overlap(True)
+    net.set_overlap(None)
     kern_iso = kernel_totals(iso_recs)
     # the unfused pair for reference: gradient into the GradBuf, then the standalone apply kernel
     gb = S.GradBuf(n, device=dev)
@@ -224,7 +225,7 @@ def step_bench(wl, steps, warmup, use_graph=True):
         raise RuntimeError(f"{wl.name}: non-finite loss in a profiled step")
     del ws, gb
     torch.cuda.empty_cache()
-    return dict(ms=ms, eager_ms=eager_ms, graph_ms=graph_ms, graph=use_g, prof_ms=prof_ms, iso_ms=iso_ms,
+    return dict(ms=ms, eager_ms=eager_ms, graph_ms=graph_ms, graph=use_g, overlap=overlap, prof_ms=prof_ms, iso_ms=iso_ms,
                 kern=kern, kern_iso=kern_iso, iso_recs=iso_recs, prof_recs=prof_recs, n_params=n, losses=losses,
                 update={"kernel": f"apply_{wl.rule}", "avg_us": 1e3 * statistics.fmean(upd),
                         "GB/s": upd_b / (statistics.fmean(upd) / 1e3) / 1e9},
@@ -251,7 +252,7 @@ def kernel_totals(recs):
 
 
 def is_product(name):
-    return name.startswith(("gemm_dma_", "gemm_staged_", "gemm_conv_"))
+    return name.startswith(("gemm_dma_", "gemm_staged_", "gemm_conv_", "gemm_dw_short_"))
 
 
 def kernel_table(kern, total_ms, top=10):
@@ -1051,6 +1052,7 @@ def step_record(wl, r, steps, fit, cpu):
         "images_per_s": wl.batch / (st["mean"] / 1e3), "ms_per_step": st["mean"],
         "median_ms_per_step": st["median"], "min_ms_per_step": st["min"], "max_ms_per_step": st["max"],
         "steps": steps, "timed_as": "HIP graph replay of sgd_train_step" if r["graph"] else "sgd_train_step per call",
+        "dedw_side_stream": r["overlap"],
         "eager_ms_per_step": statistics.fmean(r["eager_ms"]),
         "eager_median_ms_per_step": statistics.median(r["eager_ms"]),
         "graph_ms_per_step": None if r["graph_ms"] is None else statistics.fmean(r["graph_ms"]),

@@ -322,16 +322,26 @@ int sgd_set_implicit_conv(sgd_net* net, int enable);
 int sgd_set_debug(sgd_net* net, int enable);
 
 /*
- * Backward-pass concurrency.  With overlap on (the default) each layer's
- * dedw product runs on a second stream the library owns, forked from the
- * caller's stream once the product's inputs are final and joined back into
- * it before the call's work ends, so a dedw product overlaps the next
- * layer's dedx product (SPRINT section 3.3's products are independent once
- * the layer's output gradient exists).  Results are bitwise identical with
- * overlap off; the caller still sees one stream-ordered operation.  Errors:
- * SGD_EINVAL (null net).
+ * Backward-pass concurrency.  With overlap on each layer's dedw product runs
+ * on a second stream the library owns, forked from the caller's stream once
+ * the product's inputs are final and joined back into it before the call's
+ * work ends, so a dedw product overlaps the next layer's dedx product
+ * (SPRINT section 3.3's products are independent once the layer's output
+ * gradient exists).  Results are bitwise identical with overlap off; the
+ * caller still sees one stream-ordered operation.
+ *
+ * enable: 1 on, 0 off, negative: the default, which is on when the net's
+ * weight-gradient products total at least 2^30 flops per step (2 m n k
+ * summed over the dedw products, dedb's column included) and off below,
+ * where the fork and join cost more than the overlap gains.  A graph
+ * recorded by sgd_train_step_graph keeps the setting in effect when it was
+ * recorded.  Errors: SGD_EINVAL (null net).
  */
 int sgd_set_overlap(sgd_net* net, int enable);
+
+/* The overlap setting in effect (after the default is resolved): *on = 1 or
+ * 0.  Errors: SGD_EINVAL (null net or output). */
+int sgd_get_overlap(const sgd_net* net, int* on);
 
 /*
  * Per-launch kernel timing, for measurement.  While enabled, every kernel

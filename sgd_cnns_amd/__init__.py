@@ -33,7 +33,7 @@ LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
-           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_debug", "sgd_set_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
+           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_debug", "sgd_set_overlap", "sgd_get_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
            "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_train_step_graph", "sgd_step_graph_launch",
            "sgd_step_graph_destroy", "sgd_stream_ref", "sgd_train_step_noalloc", "sgd_last_error"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -117,6 +117,7 @@ def lib():
             "sgd_train_step": (i, [P, P, P, P, P, C.POINTER(SgdRule), P, P, sz, P]),
             "sgd_profile": (i, [P, i]),
             "sgd_set_overlap": (i, [P, i]),
+            "sgd_get_overlap": (i, [P, C.POINTER(C.c_int)]),
             "sgd_set_debug": (i, [P, i]),
             "sgd_set_implicit_conv": (i, [P, i]),
             "sgd_gemm_workspace_bytes": (sz, [C.POINTER(SgdGemmArgs)]),
@@ -291,8 +292,16 @@ class Net:
         _check(lib().sgd_set_debug(self._h, 1 if enable else 0))
 
     def set_overlap(self, enable):
-        """Run the dedw products on a second stream, overlapping the next layer (default on)."""
-        _check(lib().sgd_set_overlap(self._h, 1 if enable else 0))
+        """Run the dedw products on a second stream, overlapping the next layer: True, False, or None for the
+        library's default (on when the weight-gradient products total at least 2^30 flops per step)."""
+        _check(lib().sgd_set_overlap(self._h, -1 if enable is None else 1 if enable else 0))
+
+    @property
+    def overlap(self):
+        """The overlap setting in effect (the default resolved)."""
+        v = C.c_int()
+        _check(lib().sgd_get_overlap(self._h, C.byref(v)))
+        return bool(v.value)
 
     def profile(self, enable):
         """Start (clearing old records) or stop per-launch kernel timing."""

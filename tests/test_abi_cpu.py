@@ -124,6 +124,25 @@ def test_set_debug_flag():
     net.set_debug(False)
 
 
+@pytest.mark.parametrize("name,default", [("lenet5", False), ("mlp5000", True), ("vgg_cifar", True), ("vgg16", True)])
+def test_overlap_default_and_setting(name, default):
+    """The dedw side stream is on by default only for nets whose weight-gradient products total at least
+    2^30 flops per step (LeNet-5 at batch 16: about 10^7); an explicit setting wins and -1 restores the
+    default, also after a re-plan."""
+    L = S.lib()
+    assert L.sgd_set_overlap(None, 1) == S.EINVAL
+    assert L.sgd_get_overlap(None, C.byref(C.c_int())) == S.EINVAL
+    wl = workloads.WORKLOADS[name]
+    net = S.Net((wl.batch,) + wl.chw, wl.layers)
+    assert net.overlap is default
+    net.set_overlap(not default)
+    assert net.overlap is (not default)
+    net.set_implicit_conv(False)
+    assert net.overlap is (not default)
+    net.set_overlap(None)
+    assert net.overlap is default
+
+
 def test_binding_rejects_wrong_dtypes_and_lengths():
     # argument marshalling checks, on host tensors (no compute call is made)
     torch = pytest.importorskip("torch")
