@@ -998,8 +998,9 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     }
     // The slice loop, once with every block's matrix-core work and once (edge tiles) without the
     // blocks outside the output; two copies so the interior tiles' loop has no branches.  The
-    // narrower instances keep the plain loop written out below (through the lambda they compile
-    // to more registers).
+    // narrower instances keep the plain loop written out below: compiled through the lambda they
+    // take more registers and ran 3% slower (VGG-16's 128 x 64 and 64 x 128 products, same-box
+    // comparison).
     auto slices = [&](auto skip_tag) {
       constexpr bool SKIP = decltype(skip_tag)::value;
       for (int i = 0; i < nsl; ++i) {
