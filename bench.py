@@ -61,22 +61,60 @@ def cpu_model():
     return None
 
 
+def kernel_code_sha256(files=("gemm.hip", "update.hip")):
+    """SHA-256 of the kernel sources' code: C/C++ comments, trailing blanks and empty lines removed, so an
+    edit of a comment does not mark counters taken on the same code as stale."""
+    import hashlib
+    out = []
+    for f in files:
+        text = open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", f), encoding="utf-8").read()
+        code, i, n, quote = [], 0, len(text), None
+        while i < n:
+            c = text[i]
+            if quote:
+                code.append(c)
+                if c == "\\" and i + 1 < n:
+                    code.append(text[i + 1])
+                    i += 2
+                    continue
+                if c == quote:
+                    quote = None
+                i += 1
+            elif c in "\"'":
+                quote = c
+                code.append(c)
+                i += 1
+            elif text.startswith("//", i):
+                j = text.find("\n", i)
+                i = n if j < 0 else j
+            elif text.startswith("/*", i):
+                j = text.find("*/", i + 2)
+                i = n if j < 0 else j + 2
+            else:
+                code.append(c)
+                i += 1
+        lines = [ln.rstrip() for ln in "".join(code).split("\n")]
+        out.append("\n".join(ln for ln in lines if ln))
+    return hashlib.sha256("\n".join(out).encode()).hexdigest()
+
+
+TRAFFIC_KEY = "code_sha256(gemm.hip+update.hip, comments stripped)"
+
+
 def measured_traffic(kernel, workload):
     """(HBM bytes per launch, source) of `kernel` from the committed FETCH_SIZE/WRITE_SIZE counter
     runs, or (None, reason) when there is no record for it or the kernel sources changed since the
     counters were taken (the record stores a SHA-256 of the sources)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None, "no counter record"
     rec = json.load(open(path))
     recs = rec if isinstance(rec, list) else [rec]
-    src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", f), "rb").read() for f in ("gemm.hip", "update.hip"))
-    digest = hashlib.sha256(src).hexdigest()
+    digest = kernel_code_sha256()
     for r in recs:
         if r.get("workload") != workload:
             continue
-        if r.get("source_sha256(gemm.hip+update.hip)") != digest:
+        if r.get(TRAFFIC_KEY) != digest:
             return None, f"profiles/traffic.json ({workload}) predates the current kernel sources"
         k = r.get("kernels", {}).get(kernel)
         if k is None:
@@ -958,7 +996,6 @@ def summarize_traffic(fetch_dir, write_dir, workload, calib_mib, out_md, out_jso
     nbytes = calib_mib * 2 ** 20
     fs = nbytes / (fcopy * 1024) if fcopy else 1.0
     ws = nbytes / (wcopy * 1024) if wcopy else 1.0
-    src = b"".join(open(os.path.join(ROOT, "sgd_cnns_amd", "csrc", x), "rb").read() for x in ("gemm.hip", "update.hip"))
     kern = {}
     for inst, vals in f.items():
         if "sgd::" not in inst:   # the library's kernels only (not the calibration copy or torch's own)
@@ -970,7 +1007,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, calib_mib, out_md, out_jso
                "traffic_bytes": fb + wb}
         if name not in kern or kern[name]["dispatches"] < len(vals):
             kern[name] = rec
-    entry = {"workload": workload, "source_sha256(gemm.hip+update.hip)": hashlib.sha256(src).hexdigest(),
+    entry = {"workload": workload, TRAFFIC_KEY: kernel_code_sha256(),
              "fetch_scale": fs, "write_scale": ws,
              "calibration": f"one {calib_mib} MiB device copy in the same runs", "command": command, "kernels": kern}
     old = json.load(open(out_json)) if os.path.exists(out_json) else []
