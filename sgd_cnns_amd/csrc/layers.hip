@@ -493,11 +493,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__global__ void softmax_ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ y,
-                                  float* __restrict__ dz, float* __restrict__ row_loss, int N, int C, float scale) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (row >= N) return;
+// One row of softmax-CE on one wavefront: writes the row's logit gradient
+// and returns its loss (every lane gets it).
+__device__ __forceinline__ float softmax_ce_row(const float* __restrict__ z, const int32_t* __restrict__ y,
+                                                float* __restrict__ dz, int row, int C, float scale, int lane) {
   const float* zr = z + (int64_t)row * C;
   float m = -INFINITY;
   bool nan = false;
@@ -517,7 +516,44 @@ __global__ void softmax_ce_kernel(const float* __restrict__ z, const int32_t* __
   const bool ok = (unsigned)lbl < (unsigned)C;
   const float lse = (nan || !ok) ? __builtin_nanf("") : m + logf(se);
   for (int j = lane; j < C; j += 64) dz[(int64_t)row * C + j] = scale * (expf(zr[j] - lse) - (j == lbl ? 1.f : 0.f));
-  if (lane == 0) row_loss[row] = lse - zr[ok ? lbl : 0];
+  return lse - zr[ok ? lbl : 0];
+}
+
+__global__ void softmax_ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ y,
+                                  float* __restrict__ dz, float* __restrict__ row_loss, int N, int C, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float l = softmax_ce_row(z, y, dz, row, C, scale, lane);
+  if (lane == 0) row_loss[row] = l;
+}
+
+// Small batches (N <= kFusedRows): every row and the loss in one block of
+// 1024 threads -- each wavefront takes rows w, w + 16, ..., then threads
+// 0..kBlock-1 sum the row losses with loss_sum_kernel's reduction tree (one
+// term per thread), so the loss is bitwise the same as the two-kernel path.
+constexpr int kFusedRows = 64;
+__global__ __launch_bounds__(1024) void softmax_ce_loss_kernel(const float* __restrict__ z,
+                                                               const int32_t* __restrict__ y, float* __restrict__ dz,
+                                                               float* __restrict__ row_loss, float* __restrict__ loss,
+                                                               int N, int C, float scale, float lscale) {
+  __shared__ float sh[kBlock];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x < kBlock) sh[threadIdx.x] = 0.f;
+  __syncthreads();
+  for (int row = wave; row < N; row += 16) {
+    const float l = softmax_ce_row(z, y, dz, row, C, scale, lane);
+    if (lane == 0) {
+      row_loss[row] = l;
+      sh[row] = l;
+    }
+  }
+  __syncthreads();
+  for (int o = kBlock / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = lscale * sh[0];
 }
 
 // loss = scale * sum of row losses, one block, fixed reduction tree.
@@ -685,6 +721,14 @@ int maxpool_bwd(const float* dy, const uint8_t* argmax, const float* pooled, flo
 
 int softmax_ce(const float* z, const int32_t* y, float* dz, float* row_loss, float* loss, int N, int C,
                float scale, hipStream_t s) {
+  static_assert(kFusedRows <= kBlock, "the fused kernel's sum keeps one row loss per thread of the tree");
+  if (N <= kFusedRows) {
+    prof_begin("softmax_ce", 7.0 * N * C, 4.0 * (2.0 * N * C + 2.0 * N + 1), s);
+    hipLaunchKernelGGL(softmax_ce_loss_kernel, dim3(1), dim3(1024), 0, s, z, y, dz, row_loss, loss, N, C, scale,
+                       scale);
+    prof_end(s);
+    return check_launch("softmax_ce");
+  }
   const int rows_per_block = kBlock / 64;
   prof_begin("softmax_ce", 6.0 * N * C, 4.0 * (2.0 * N * C + 2.0 * N), s);
   hipLaunchKernelGGL(softmax_ce_kernel, dim3((int)ceil_div(N, rows_per_block)), dim3(kBlock), 0, s, z, y, dz,
