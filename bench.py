@@ -290,7 +290,8 @@ def kernel_totals(recs):
 
 
 def is_product(name):
-    return name.startswith(("gemm_dma_", "gemm_staged_", "gemm_conv_", "gemm_dw_short_"))
+    return name.startswith(("gemm_dma_", "gemm_staged_", "gemm_conv_", "gemm_dw_short_", "gemm_skinny_",
+                            "gemm_smallk_"))
 
 
 def kernel_table(kern, total_ms, top=10):
@@ -918,6 +919,10 @@ def bench_kernel_name(instance):
     ms = re.search(r"dw_short<(\d+), \d+, -?\d+>", instance)
     if ms:
         return f"gemm_dw_short_k{2 * int(ms.group(1))}"
+    if "skinny_nt_kernel" in instance:
+        return "gemm_skinny_nt"
+    if "smallk_nn_kernel" in instance:
+        return "gemm_smallk_nn"
     m = re.search(r"gemm_(dma|staged)<(\d+), (\d+), (?:(\d+), )?(true|false), (true|false), (\d+)"
                   r"(?:, (true|false), (true|false))?>", instance)
     if not m:

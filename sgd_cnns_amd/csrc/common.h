@@ -115,6 +115,11 @@ struct GemmDesc {
   // gemm_dma schedule override: sk_grid > 0 forces that many blocks with
   // the first sk_dp tiles done whole and the rest by stream-K.
   int sk_grid = -1, sk_dp = 0;
+  // The product may take the skinny kernels (a logits layer's forward and
+  // input-gradient products): set for fc layers and standalone products,
+  // not for convolutions, whose explicit and implicit paths keep one sum
+  // order.
+  bool skinny = false;
   // Implicit GEMM: 1 = A (K-contiguous, not transposed) is gathered by cv
   // (A and lda are ignored); 2 = B (row-contiguous, transposed) is (B and
   // ldb are ignored).  Needs cv.SC % 16 == 0 for A, % 4 == 0 for B.

@@ -1299,6 +1299,92 @@ __global__ __launch_bounds__(kThreads, KP * NBLK > 16 ? 3 : 4) void dw_short(KAr
   }
 }
 
+// ---- Skinny products: the logits layer's forward product (at most 16 outputs per row) and its
+// input-gradient product (a reduction of at most 16).  Both are a pass over one large operand -- the
+// layer's input, or its output gradient and ReLU mask -- next to which the tile kernels' prologue,
+// stream-K split and fixup launch cost more than the arithmetic.
+constexpr int kSkinny = 16;
+
+// C[m][0..N) = epilogue(A[m][:] . B[n][:]) for N <= kSkinny, one block per row: thread t sums the
+// float4 groups t, t + 256, ... of k for every output, then each output's 256 partial sums are added
+// by a fixed tree in LDS.
+__global__ __launch_bounds__(kThreads) void skinny_nt_kernel(KArgs p) {
+  __shared__ float red[kSkinny][kThreads];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int N = p.N, K4 = p.K / 4;
+  const float4* a = reinterpret_cast<const float4*>(p.A + (int64_t)row * p.lda);
+  float acc[kSkinny];
+#pragma unroll
+  for (int n = 0; n < kSkinny; ++n) acc[n] = 0.f;
+  for (int k4 = t; k4 < K4; k4 += kThreads) {
+    // every load first (rows past N re-read row N - 1 and are not used), then the products
+    const float4 av = a[k4];
+    float4 bv[kSkinny];
+#pragma unroll
+    for (int n = 0; n < kSkinny; ++n)
+      bv[n] = reinterpret_cast<const float4*>(p.B + (int64_t)min(n, N - 1) * p.ldb)[k4];
+#pragma unroll
+    for (int n = 0; n < kSkinny; ++n) {
+      if (n < N) {
+        acc[n] += av.x * bv[n].x;
+        acc[n] += av.y * bv[n].y;
+        acc[n] += av.z * bv[n].z;
+        acc[n] += av.w * bv[n].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < kSkinny; ++n) red[n][t] = acc[n];
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (t < o) {
+#pragma unroll
+      for (int n = 0; n < kSkinny; ++n) red[n][t] += red[n][t + o];
+    }
+    __syncthreads();
+  }
+  if (t < N) p.C[(int64_t)row * p.ldc + t] = epilogue(red[t][0], p.epi, row, t, p, 0.f);
+}
+
+// C[m][n..n+3] = epilogue(sum over k < K <= kSkinny of A[m][k] B[k][n..n+3]), one float4 of C per
+// thread (N a multiple of 4), k in order.
+__global__ __launch_bounds__(kThreads) void smallk_nn_kernel(KArgs p) {
+  const int N4 = p.N / 4;
+  const int64_t total = (int64_t)p.M * N4;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int m = (int)(i / N4), n = (int)(i - (int64_t)m * N4) * 4;
+    const float* ar = p.A + (int64_t)m * p.lda;
+    // every load first (k past K re-reads row K - 1 and is not used), then the products in k order
+    float4 mk = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (p.epi == EPI_MASK) mk = *reinterpret_cast<const float4*>(p.mask + (int64_t)m * p.ldm + n);
+    float av[kSkinny];
+    float4 bv[kSkinny];
+#pragma unroll
+    for (int k = 0; k < kSkinny; ++k) {
+      const int kc = min(k, p.K - 1);
+      av[k] = ar[kc];
+      bv[k] = *reinterpret_cast<const float4*>(p.B + (int64_t)kc * p.ldb + n);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kSkinny; ++k) {
+      if (k < p.K) {
+        acc.x += av[k] * bv[k].x;
+        acc.y += av[k] * bv[k].y;
+        acc.z += av[k] * bv[k].z;
+        acc.w += av[k] * bv[k].w;
+      }
+    }
+    if (p.epi == EPI_MASK) {
+      acc.x = mk.x > 0.f ? acc.x : 0.f;
+      acc.y = mk.y > 0.f ? acc.y : 0.f;
+      acc.z = mk.z > 0.f ? acc.z : 0.f;
+      acc.w = mk.w > 0.f ? acc.w : 0.f;
+    }
+    *reinterpret_cast<float4*>(p.C + (int64_t)m * p.ldc + n) = acc;
+  }
+}
+
 // Sum split-K partial tiles in slice order, then store: the ones column to
 // ones_out, the conv weight gradient permuted, anything else through the
 // epilogue.
@@ -1737,6 +1823,26 @@ int dw_short_launch(const GemmDesc& d, KArgs a, double flops, double bytes, hipS
   return check_launch("gemm_dw_short");
 }
 
+// The skinny kernels take plain products (no gather, ones column, accumulation or update rule) whose
+// vector operands are 16-byte aligned with row strides a multiple of 4 floats.
+bool plain_product(const GemmDesc& d) {
+  return d.skinny && !d.gather && !d.ones_out && !d.accum && d.urule < 0 && d.perm_c == 0 && d.M >= 1 && d.N >= 1 &&
+         d.K >= 1;
+}
+bool skinny_nt_ok(const GemmDesc& d, int form) {
+  return form == 0 && plain_product(d) && d.N <= kSkinny && d.K % 4 == 0 && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
+         aligned16(d.A) && aligned16(d.B) && (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RELU);
+}
+// The small-k kernel reloads B's 16 rows for every output row, so it is used for outputs up to 2^20
+// elements (LeNet-5's and VGG-CIFAR's logits dedx: 7.0 -> 6.0 and 10.9 -> 6.6 us); the MLP's 512 x 5000
+// output stays on the tiled kernel, which shares B through LDS (11 us against 13).
+bool smallk_nn_ok(const GemmDesc& d, int form) {
+  return form == 2 && plain_product(d) && d.K <= kSkinny && (int64_t)d.M * d.N <= ((int64_t)1 << 20) &&
+         d.N % 4 == 0 && d.ldb % 4 == 0 && d.ldc % 4 == 0 &&
+         aligned16(d.B) && aligned16(d.C) &&
+         (d.epi == EPI_STORE || (d.epi == EPI_MASK && d.ldm % 4 == 0 && aligned16(d.mask)));
+}
+
 int gemm_launch(const GemmDesc& d, hipStream_t s) {
   const bool ones = d.ones_out != nullptr;
   KArgs a{};
@@ -1808,6 +1914,21 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
   const double out_passes = d.urule >= 0 ? (d.urule == SGD_PLAIN ? 2.0 : 4.0) : d.accum ? 2.0 : 1.0;
   const double bytes = 4.0 * ((double)d.M * d.K + (double)d.K * d.N + out_passes * out_words);
   if (d.cfg < 0 && short_dw_ok(d, form)) return dw_short_launch(d, a, flops, bytes, s);
+  if (d.cfg < 0 && (skinny_nt_ok(d, form) || smallk_nn_ok(d, form))) {
+    a.C = d.C;
+    a.ldc = d.ldc;
+    if (form == 0) {
+      prof_begin("gemm_skinny_nt", flops, bytes, s);
+      hipLaunchKernelGGL(skinny_nt_kernel, dim3((unsigned)d.M), dim3(kThreads), 0, s, a);
+    } else {
+      const int64_t quads = (int64_t)d.M * (d.N / 4);
+      prof_begin("gemm_smallk_nn", flops, bytes + (d.epi == EPI_MASK ? 4.0 * d.M * d.N : 0.0), s);
+      hipLaunchKernelGGL(smallk_nn_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(quads, kThreads), 4096)),
+                         dim3(kThreads), 0, s, a);
+    }
+    prof_end(s);
+    return check_launch("gemm_skinny");
+  }
 
   // gemm_dma schedule.  The plan depends only on the shape and the machine
   // (the instance without an update rule sets the occupancy), so a product

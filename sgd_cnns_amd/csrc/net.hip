@@ -584,6 +584,7 @@ int run_forward(sgd_net* net, const float* Wt, const float* X, const int32_t* y,
       g.K = s.Ci;
       g.epi = s.relu ? EPI_BIAS_RELU : EPI_BIAS;
       g.bias = Wt + s.b_off;
+      g.skinny = true;
       g.splits = s.split_fwd;
       g.partial = partial;
       g.partial_floats = net->partial_floats;
@@ -671,6 +672,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.epi = mask ? EPI_MASK : EPI_STORE;
         d.mask = mask ? at<float>(ws, src.out) : nullptr;
         d.ldm = s.Ci;
+        d.skinny = true;
         d.splits = s.split_dx;
         d.partial = partial;
         d.partial_floats = net->partial_floats;
@@ -987,6 +989,7 @@ int sgd_gemm(const sgd_gemm_args* g, void* ws, size_t ws_bytes, void* stream) {
   d.N = g->n;
   d.K = g->k;
   d.epi = sgd::EPI_STORE;
+  d.skinny = true;
   d.splits = sgd::gemm_pick_splits(g->m, g->n, g->k);
   d.partial = static_cast<float*>(ws);
   d.partial_floats = (int64_t)(ws_bytes / 4);

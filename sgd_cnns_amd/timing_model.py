@@ -125,7 +125,8 @@ def family_of_kernel(name):
     """"staged" for the staged kernels, "dma" for the direct-load ones (the
     gathered convolution kernels share their main loop, and the streaming
     weight-gradient kernel of short reductions is what the library picks for
-    the same aligned operands)."""
+    the same aligned operands, as are the skinny kernels of a logits layer's
+    products)."""
     return "staged" if name.startswith("gemm_staged_") else "dma"
 
 
@@ -135,6 +136,8 @@ def form_of_kernel(name):
         return _CONV_FORMS[name.split("_")[2]]
     if name.startswith("gemm_dw_short_"):
         return "tn"
+    if name.startswith(("gemm_skinny_", "gemm_smallk_")):
+        return name.rsplit("_", 1)[-1]
     suffix = name.rsplit("_", 1)[-1]
     if name.startswith(("gemm_dma_", "gemm_staged_")) and suffix in FORMS:
         return suffix

@@ -107,6 +107,37 @@ def test_gemm_short_reduction_matches_oracle(m, n, k, pad):
     assert np.all(err <= bound), f"max err / bound = {worst:.3f}"
 
 
+# A logits layer's products on the skinny kernels: the forward form (nt) with at most 16 outputs per row
+# and a k that is a multiple of 4, and the input-gradient form (nn) with a reduction of at most 16, n a
+# multiple of 4 and at most 2^20 outputs (the largest case here is exactly that); C's 4 padding columns must
+# stay untouched.
+SKINNY = [("nt", 512, 10, 5000), ("nt", 16, 10, 84), ("nt", 3, 16, 4), ("nt", 130, 1, 512),
+          ("nn", 128, 512, 10), ("nn", 16, 84, 10), ("nn", 7, 4, 1), ("nn", 130, 512, 16), ("nn", 1024, 1024, 3)]
+
+
+@pytest.mark.parametrize("form,m,n,k", SKINNY)
+def test_gemm_skinny_products_match_oracle(form, m, n, k):
+    a_t, b_t = TM.FORMS[form]
+    print(f"[gemm skinny] form={form} m={m} n={n} k={k}", flush=True)
+    seed = 70 + m % 3
+    A = stored(seed, 0, m, k, 0)
+    B = stored(seed, 1, k, n, 0) if b_t else stored(seed, 1, n, k, 0)
+    opA = A.astype(np.float64)
+    opBt = (B.T if b_t else B).astype(np.float64)
+    ref = O.fc_fwd(opA, opBt, np.zeros(n), dtype=np.float64)
+    bound = k * U / (1 - k * U) * O.fc_fwd(np.abs(opA), np.abs(opBt), np.zeros(n), dtype=np.float64)
+    Cfull = torch.full((m, n + 4), float("nan"), device="cuda")
+    nbytes = S.gemm_workspace_bytes(m, n, k, a_t, b_t)
+    ws = torch.empty(max(nbytes, 4) // 4, device="cuda")
+    S.gemm(on_device(A, k), on_device(B, n if b_t else k), Cfull[:, :n], a_t, b_t, ws)
+    torch.cuda.synchronize()
+    got = Cfull.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(got[:, n:])), "padding columns of C were written"
+    err = np.abs(got[:, :n] - ref)
+    assert np.all(np.isfinite(got[:, :n]))
+    assert np.all(err <= bound), f"max err / bound = {float((err / np.maximum(bound, 1e-300)).max()):.3f}"
+
+
 def test_gemm_rejects_bad_arguments():
     """Argument errors are caught on the host, before any launch."""
     m, n, k = 128, 128, 30000
@@ -154,8 +185,11 @@ def test_profile_records_carry_product_shapes():
                    ("tn", 10, 33, batch), ("nn", batch, 32, 10),      # layer 2 dedw(+dedb), dedx
                    ("tn", 32, inp + 1, batch)])                      # layer 1 dedw(+dedb)
     assert got == want
-    # batch 8: both weight gradients are short reductions, on the streaming kernel
+    # batch 8: both weight gradients are short reductions, on the streaming kernel; the logits layer's
+    # forward and input-gradient products are on the skinny kernels
     assert all(kn.startswith("gemm_dw_short_") for p in prods if p["form"] == "tn" for kn in p["kernels"]), prods
+    skinny = {(p["form"], p["n"]) for p in prods if p["kernels"][0].startswith(("gemm_skinny_", "gemm_smallk_"))}
+    assert skinny == {("nt", 10), ("nn", 32)}, prods
     assert others, "the softmax and loss kernels are recorded outside the products"
     for (name, _l, _p, ms, _f, _b, shape) in recs:
         assert ms >= 0
