@@ -840,12 +840,25 @@ struct DmaTg : DmaT<R> {
 // each as a partial product to that block's slot (2b for the tile its range
 // starts in, 2b + 1 for the tile it ends in) and gemm_sk_fixup adds the slots
 // in k order before the epilogue, so results do not depend on timing.
+//
+// Grouped form (rg * cg > 1; no whole tiles first): a product only a few tiles
+// tall (rg = its tile rows) is cut along k the same way, but the flattened
+// space is (group of cg tile columns, k-slice), and gridDim.x / (rg * cg)
+// ranges are each run by rg * cg blocks at once, one per tile of the group.
+// The group's blocks are consecutive after the XCD renumbering, so they run
+// on one XCD at the same time over the same k-slices: each A slice is read by
+// cg blocks and each B slice by rg blocks, and all but the first read of a
+// slice hit that XCD's L2 (the ungrouped order reads an operand panel once per
+// tile, at a different time for each).  Slots and the fixup's k order follow
+// the group's range, with the block's own index for the slot.
 struct SkArgs {
   int ipt;           // k-slices per tile: ceil(K / 16)
-  int dp_tiles;      // tiles done whole before the stream-K part
-  int sk_iters;      // (tiles - dp_tiles) * ipt; 0 or >= gridDim.x, and
-                     // sk_iters * gridDim.x < 2^31 (32-bit range arithmetic)
+  int dp_tiles;      // tiles done whole before the stream-K part (0 if grouped)
+  int sk_iters;      // ungrouped: (tiles - dp_tiles) * ipt; grouped: tiles_n / cg * ipt.
+                     // 0 or >= the number of ranges, and sk_iters * gridDim.x < 2^31
+                     // (32-bit range arithmetic)
   float* part;       // 2 * gridDim.x slots of BM * BN floats
+  int rg = 1, cg = 1;  // block group: rg tile rows (all of them) by cg tile columns
 };
 
 __host__ __device__ inline int sk_start(int b, int S, int G) { return (int)((uint32_t)b * (uint32_t)S / (uint32_t)G); }
@@ -919,14 +932,18 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
   // stream-K range, tile by tile.  One store site keeps the epilogue's code
   // (and registers) out of the pipelined loop.
   const int S = s.sk_iters;
-  int it = S > 0 ? sk_start(b, S, G) : 0;
-  const int end = S > 0 ? sk_start(b + 1, S, G) : 0;
+  const int gsz = s.rg * s.cg;  // 1 when ungrouped
+  const int grp = b / gsz, g_r = (b - grp * gsz) / s.cg, g_c = b - grp * gsz - g_r * s.cg;
+  const int Q = G / gsz;
+  int it = S > 0 ? sk_start(grp, S, Q) : 0;
+  const int end = S > 0 ? sk_start(grp + 1, S, Q) : 0;
   int t_next = b;
   bool first_sk = true;
   for (;;) {
-    int t, k0, k1, slot = -1;
+    int k0, k1, slot = -1;
+    int tm_i, tn_i;
     if (t_next < s.dp_tiles) {
-      t = t_next;
+      tile_coords(t_next, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
       k0 = 0;
       k1 = s.ipt;
       t_next += G;
@@ -934,15 +951,18 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
       const int tt = (int)((uint32_t)it / (uint32_t)s.ipt);
       k0 = it - tt * s.ipt;
       k1 = min(s.ipt, k0 + (end - it));
-      t = s.dp_tiles + tt;
+      if (gsz == 1) {
+        tile_coords(s.dp_tiles + tt, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
+      } else {
+        tm_i = g_r;
+        tn_i = tt * s.cg + g_c;
+      }
       it += k1 - k0;
       slot = first_sk ? 2 * b : 2 * b + 1;
       first_sk = false;
     } else {
       break;
     }
-    int tm_i, tn_i;
-    tile_coords(t, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
     const int m0 = tm_i * BM, n0 = tn_i * BN;
     const int kbeg = k0 * kDmaBK;
     const int kval = min(p.K, k1 * kDmaBK) - kbeg;
@@ -1108,19 +1128,30 @@ __global__ __launch_bounds__(kThreads) void gemm_sk_fixup(KArgs p, SkArgs s, int
   __shared__ float4 part_sum[kThreads];
   const int j = blockIdx.x;
   const int S = s.sk_iters;
-  const int x0 = j * s.ipt;
-  const int blo = sk_block_of(x0, S, G), bhi = sk_block_of(x0 + s.ipt - 1, S, G);
+  const int tiles_m = p.tiles / p.tiles_n;
+  // Stream-K tile j; grouped, it is tile (j % rg, j / rg) and its ranges are those of its column
+  // group, run by the group member (j % rg) * cg + (column % cg) of each.
+  const int gsz = s.rg * s.cg, Q = G / gsz;
+  int tm_i, tn_i, u, member;
+  if (gsz == 1) {
+    tile_coords(s.dp_tiles + j, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
+    u = j;
+    member = 0;
+  } else {
+    tm_i = j % s.rg;
+    tn_i = j / s.rg;
+    u = tn_i / s.cg;
+    member = tm_i * s.cg + (tn_i - u * s.cg);
+  }
+  const int x0 = u * s.ipt;
+  const int blo = sk_block_of(x0, S, Q), bhi = sk_block_of(x0 + s.ipt - 1, S, Q);
   if (blo == bhi) return;  // inside one range: stored by gemm_dma
   const int n = bhi - blo + 1;  // <= G <= 1024 (checked on the host)
   for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int bb = blo + i;
-    slots[i] = sk_start(bb, S, G) / s.ipt == j ? 2 * bb : 2 * bb + 1;
+    const int qq = blo + i, bb = qq * gsz + member;
+    slots[i] = sk_start(qq, S, Q) / s.ipt == u ? 2 * bb : 2 * bb + 1;
   }
   __syncthreads();
-  const int t = s.dp_tiles + j;
-  const int tiles_m = p.tiles / p.tiles_n;
-  int tm_i, tn_i;
-  tile_coords(t, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
   const int m0 = tm_i * BM, n0 = tn_i * BN;
   const int grp = threadIdx.x % TS, v4 = threadIdx.x / TS;
   const int idx = (blockIdx.y * (kThreads / TS) + v4) * 4;  // the float4's first element in the slot
@@ -1617,6 +1648,7 @@ struct SkPlan {
   int grid;
   int dp;
   int64_t sk_iters;
+  int rg = 1, cg = 1;  // block group of the grouped form (see SkArgs)
 };
 constexpr double kItemCost = 6.0;
 SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, int64_t cap_floats) {
@@ -1666,6 +1698,33 @@ SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, in
     }
   }
   return best;
+}
+
+// The grouped form for a pure stream-K plan of a product at most kGroupRows
+// tile rows tall: rg = all of its tile rows, cg the widest divisor of its tile
+// columns (up to kGroupCols) for which a group divides an XCD's run of G / 8
+// blocks, so that the group's blocks share an XCD.  The per-block work, the
+// number of ranges a tile is cut into and the slot count are those of the
+// ungrouped plan.
+constexpr int kGroupRows = 8, kGroupCols = 8;
+constexpr bool group_sk = true;
+void sk_group(SkPlan& p, int64_t tiles_m, int64_t tiles_n, int64_t ipt) {
+  p.rg = p.cg = 1;
+  if (p.dp != 0 || p.sk_iters <= 0 || p.grid % 8 || tiles_m > kGroupRows) return;
+  const int run = p.grid / 8;
+  if (run % tiles_m) return;
+  int cg = 1;
+  for (int c = kGroupCols; c > 1; --c)
+    if (tiles_n % c == 0 && run % (tiles_m * c) == 0) {
+      cg = c;
+      break;
+    }
+  if (tiles_m * cg < 2) return;
+  const int64_t S = tiles_n / cg * ipt, Q = p.grid / (tiles_m * cg);
+  if (S < Q || S * p.grid >= ((int64_t)1 << 31)) return;
+  p.rg = (int)tiles_m;
+  p.cg = cg;
+  p.sk_iters = S;
 }
 
 // Tile choice for gemm_staged, from measurements on the step's shapes.
@@ -1951,6 +2010,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
       }
     } else {
       plan = sk_choose(T, ipt, machine_for(cfg), tile, cap);
+      if (group_sk) sk_group(plan, ceil_div(d.M, c.bm), ceil_div(a.Nt, c.bn), ipt);
     }
     if (plan.sk_iters > 0 && plan.sk_iters * plan.grid >= ((int64_t)1 << 31)) {
       set_error("gemm: stream-K schedule too long for 32-bit range arithmetic");
@@ -1960,7 +2020,8 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
       set_error("gemm: partial-tile buffer too small for the stream-K schedule");
       return SGD_EINVAL;
     }
-    const int64_t item = plan.dp > 0 ? ipt : std::min<int64_t>(ipt, ceil_div(plan.sk_iters, plan.grid));
+    const int64_t item =
+        plan.dp > 0 ? ipt : std::min<int64_t>(ipt, ceil_div(plan.sk_iters, plan.grid / (plan.rg * plan.cg)));
     if (!dma_span_ok(d, c, item)) {
       if (d.cfg >= 0 || d.gather) {
         set_error("gemm: a work item spans more than 2 GiB of an operand");
@@ -1985,7 +2046,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
       return SGD_EINVAL;
     }
     const int64_t T = a.tiles, ipt = ceil_div(d.K, kDmaBK), tile = (int64_t)c.bm * c.bn;
-    const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial};
+    const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial, plan.rg, plan.cg};
     prof_begin(d.gather ? kConvNames[cfg][d.gather == 2 ? 2 : (d.cv.flip ? 1 : 0)] : kDmaNames[cfg][form], flops, bytes, s);
     hipLaunchKernelGGL(f.main, dim3(plan.grid), dim3(kThreads), 0, s, a, sk);
     prof_end(s);
@@ -1993,13 +2054,15 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     if (plan.sk_iters > 0) {
       // Partial tiles written and read back by the fixup (for the profile),
       // and the most slots a tile has.
+      // (Grouped: the ranges of column group u cut each of its rg * cg tiles alike.)
+      const int gsz = plan.rg * plan.cg, Q = plan.grid / gsz;
       int64_t shared = 0, slots = 0, most = 1;
-      for (int64_t j = 0; j < T - plan.dp; ++j) {
-        const int blo = sk_block_of((int)(j * ipt), sk.sk_iters, plan.grid);
-        const int bhi = sk_block_of((int)(j * ipt + ipt - 1), sk.sk_iters, plan.grid);
+      for (int64_t u = 0; u < sk.sk_iters / ipt; ++u) {
+        const int blo = sk_block_of((int)(u * ipt), sk.sk_iters, Q);
+        const int bhi = sk_block_of((int)(u * ipt + ipt - 1), sk.sk_iters, Q);
         if (blo != bhi) {
-          ++shared;
-          slots += bhi - blo + 1;
+          shared += gsz;
+          slots += (int64_t)gsz * (bhi - blo + 1);
           most = std::max<int64_t>(most, bhi - blo + 1);
         }
       }

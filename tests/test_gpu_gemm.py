@@ -28,10 +28,13 @@ U = 2.0 ** -24
 # (200, 1100) and (256, 2100) are more than 8 tiles wide, so their tiles run in bands of 8 tile columns (a
 # ragged last band of 1 column in the first; stream-K tiles shared between blocks, completed by the fixup, in
 # the second).  In the tn form, (64, 28) and (48, 60) take the 64x64 tile (a first conv layer's dedw shape;
-# the first split over many stream-K blocks, the second with a ragged tile).
+# the first split over many stream-K blocks, the second with a ragged tile).  A few tile rows and many
+# k-slices give the grouped stream-K form (block groups of all tile rows by up to 8 tile columns running
+# the same k-ranges): 2 x 2 groups in (256, 192), 2 x 1 in (256, 2100), 4 x 8 with ragged edges in
+# (500, 1000), and 8 x 1 in (1000, 600).
 SHAPES = [(77, 130, 1000, 0), (256, 192, 4096, 0), (128, 128, 30000, 0), (1000, 36, 4, 0), (5, 3, 7, 0),
           (300, 516, 260, 12), (513, 257, 1031, 3), (4096, 64, 576, 0), (200, 1100, 300, 0), (256, 2100, 4096, 0),
-          (64, 28, 100000, 0), (48, 60, 5000, 0)]
+          (64, 28, 100000, 0), (48, 60, 5000, 0), (500, 1000, 3000, 0), (1000, 600, 4000, 0)]
 
 
 def stored(seed, tid, rows, cols, pad):
