@@ -859,6 +859,7 @@ struct SkArgs {
                      // (32-bit range arithmetic)
   float* part;       // 2 * gridDim.x slots of BM * BN floats
   int rg = 1, cg = 1;  // block group: rg tile rows (all of them) by cg tile columns
+  int edge_last = 0;   // one block per tile: the ragged last tile row (bit 0) and column (bit 1) go last
 };
 
 __host__ __device__ inline int sk_start(int b, int S, int G) { return (int)((uint32_t)b * (uint32_t)S / (uint32_t)G); }
@@ -898,6 +899,36 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, boo
   const int cols = min(kBandN, tiles_n - band * kBandN);
   tm_i = in_band / cols;
   tn_i = band * kBandN + (in_band - tm_i * cols);
+}
+
+// Tile of block b in a launch of one block per tile with more tiles than
+// resident blocks and a ragged last tile row and/or column (bits 0 and 1 of
+// ragged).  The edge tiles carry a fraction of the matrix-core work (their
+// blocks outside the output skip it), so each XCD's run of blocks takes its
+// share of the interior tiles first, in tile_coords order over the interior,
+// and its share of the edge tiles (last column, then last row) at the end:
+// the launch's last, partly filled round of resident blocks then holds light
+// tiles rather than full ones.
+__device__ __forceinline__ void edge_last_coords(int b, int G, int tiles_m, int tiles_n, bool banded, int ragged,
+                                                 int& tm_i, int& tn_i) {
+  const int runs = (G & 7) == 0 ? 8 : 1, R = G / runs;  // the XCD runs of the renumbering below
+  const int x = b / R, j = b - x * R;
+  const int rowr = ragged & 1, colr = ragged >> 1;
+  const int im = tiles_m - rowr, in_ = tiles_n - colr;
+  const int ne = G - im * in_;
+  const int e0 = x * ne / runs, ix = R - ((x + 1) * ne / runs - e0);
+  if (j < ix) {
+    tile_coords(x * R - e0 + j, im, in_, banded, tm_i, tn_i);
+    return;
+  }
+  const int e = e0 + j - ix;
+  if (e < colr * im) {
+    tm_i = e;
+    tn_i = tiles_n - 1;
+  } else {
+    tm_i = tiles_m - 1;
+    tn_i = e - colr * im;
+  }
 }
 
 // GA: the A operand is a K-contiguous convolution gather (DmaKg); GB: the B
@@ -943,7 +974,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     int k0, k1, slot = -1;
     int tm_i, tn_i;
     if (t_next < s.dp_tiles) {
-      tile_coords(t_next, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
+      if (s.edge_last) edge_last_coords(t_next, G, tiles_m, p.tiles_n, p.perm_c == 0, s.edge_last, tm_i, tn_i);
+      else tile_coords(t_next, tiles_m, p.tiles_n, p.perm_c == 0, tm_i, tn_i);
       k0 = 0;
       k1 = s.ipt;
       t_next += G;
@@ -1649,6 +1681,7 @@ struct SkPlan {
   int dp;
   int64_t sk_iters;
   int rg = 1, cg = 1;  // block group of the grouped form (see SkArgs)
+  int edge_last = 0;   // see edge_last_coords
 };
 constexpr double kItemCost = 6.0;
 SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, int64_t cap_floats) {
@@ -1708,6 +1741,7 @@ SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, in
 // ungrouped plan.
 constexpr int kGroupRows = 8, kGroupCols = 8;
 constexpr bool group_sk = true;
+constexpr bool edge_last = true;
 void sk_group(SkPlan& p, int64_t tiles_m, int64_t tiles_n, int64_t ipt) {
   p.rg = p.cg = 1;
   if (p.dp != 0 || p.sk_iters <= 0 || p.grid % 8 || tiles_m > kGroupRows) return;
@@ -2011,6 +2045,10 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     } else {
       plan = sk_choose(T, ipt, machine_for(cfg), tile, cap);
       if (group_sk) sk_group(plan, ceil_div(d.M, c.bm), ceil_div(a.Nt, c.bn), ipt);
+      // One block per tile over more than one round of resident blocks: ragged edge tiles last.
+      const Machine mc = machine_for(cfg);
+      if (edge_last && plan.sk_iters == 0 && plan.dp == T && T == plan.grid && T > (int64_t)mc.cus * mc.occ)
+        plan.edge_last = (d.M % c.bm ? 1 : 0) | (a.Nt % c.bn ? 2 : 0);
     }
     if (plan.sk_iters > 0 && plan.sk_iters * plan.grid >= ((int64_t)1 << 31)) {
       set_error("gemm: stream-K schedule too long for 32-bit range arithmetic");
@@ -2046,7 +2084,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
       return SGD_EINVAL;
     }
     const int64_t T = a.tiles, ipt = ceil_div(d.K, kDmaBK), tile = (int64_t)c.bm * c.bn;
-    const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial, plan.rg, plan.cg};
+    const SkArgs sk{(int)ipt, plan.dp, (int)plan.sk_iters, d.partial, plan.rg, plan.cg, plan.edge_last};
     prof_begin(d.gather ? kConvNames[cfg][d.gather == 2 ? 2 : (d.cv.flip ? 1 : 0)] : kDmaNames[cfg][form], flops, bytes, s);
     hipLaunchKernelGGL(f.main, dim3(plan.grid), dim3(kThreads), 0, s, a, sk);
     prof_end(s);

@@ -31,10 +31,13 @@ U = 2.0 ** -24
 # the first split over many stream-K blocks, the second with a ragged tile).  A few tile rows and many
 # k-slices give the grouped stream-K form (block groups of all tile rows by up to 8 tile columns running
 # the same k-ranges): 2 x 2 groups in (256, 192), 2 x 1 in (256, 2100), 4 x 8 with ragged edges in
-# (500, 1000), and 8 x 1 in (1000, 600).
+# (500, 1000), and 8 x 1 in (1000, 600).  One block per tile over more tiles than resident blocks, with a
+# ragged last tile row and column, puts the edge tiles last: (3900, 3950) has 961 tiles (no XCD runs),
+# (4000, 4000) 1024 (or 3969 64 x 64 tiles in the tn form).
 SHAPES = [(77, 130, 1000, 0), (256, 192, 4096, 0), (128, 128, 30000, 0), (1000, 36, 4, 0), (5, 3, 7, 0),
           (300, 516, 260, 12), (513, 257, 1031, 3), (4096, 64, 576, 0), (200, 1100, 300, 0), (256, 2100, 4096, 0),
-          (64, 28, 100000, 0), (48, 60, 5000, 0), (500, 1000, 3000, 0), (1000, 600, 4000, 0)]
+          (64, 28, 100000, 0), (48, 60, 5000, 0), (500, 1000, 3000, 0), (1000, 600, 4000, 0), (3900, 3950, 200, 0),
+          (4000, 4000, 64, 0)]
 
 
 def stored(seed, tid, rows, cols, pad):
