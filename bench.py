@@ -788,6 +788,102 @@ def timing_model_report(out_path, raw_prefix=None, reps=3):
     print(text)
 
 
+def vendor_compare(out_path, reps=15):
+    """Context for the rooflines: every distinct matrix product of each workload's step (its form and
+    m, n, k, as the step profiler records them, with its count per step), timed as one plain sgd_gemm
+    launch (the same main loop and schedule as the step's product, with a plain store in place of the
+    fused epilogue and the explicit operand in place of a convolution gather) and as torch.mm, the
+    vendor's fp32 GEMM (TF32 off), on the same operands.  Median of `reps` event-bracketed launches
+    each; both results are compared (max |difference| / max |result|)."""
+    import numpy as np
+    import torch
+
+    import sgd_cnns_amd as S
+    import workloads
+    from sgd_cnns_amd import timing_model as TM
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+
+    def median_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda._sleep(100_000 * reps)  # queue the launches ahead of the GPU
+        for r in range(reps):
+            ev[r].record(stream)
+            fn()
+        ev[reps].record(stream)
+        ev[reps].synchronize()
+        return 1e3 * sorted(ev[r].elapsed_time(ev[r + 1]) for r in range(reps))[reps // 2]
+
+    lines = ["# Step products: sgd_gemm against the vendor fp32 GEMM (torch.mm)", "",
+             "Command (repository root, one MI355X): `python bench.py --vendor-compare OUT.md`", "",
+             "Every distinct product of each workload's step (form, m, n, k as the step profiler records "
+             "them, with a weight gradient's n taken without the bias's implicit ones column; count = "
+             "launches per step), timed as one plain sgd_gemm launch (the step product's "
+             "main loop and schedule, with a plain store in place of the fused epilogue and the explicit "
+             "operand in place of a convolution gather) and as torch.mm on the same operands (fp32, TF32 "
+             f"off).  Median of {reps} event-bracketed launches.  `diff` = max |ours - torch| / max |torch|.", ""]
+    summary = {}
+    for name in STEP_WORKLOADS:
+        wl = workloads.WORKLOADS[name]
+        say(f"vendor compare: {name}")
+        X, y, W = workloads.make_inputs(wl)
+        net = S.Net((wl.batch,) + tuple(wl.chw), wl.layers)
+        net.set_overlap(False)
+        Wd, Xd, yd = (torch.from_numpy(a).to(dev) for a in (W, X, y))
+        grad = torch.empty(net.param_count(), device=dev)
+        loss = torch.empty(1, device=dev)
+        ws = net.workspace(dev)
+        net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+        net.profile(True)
+        net.compute_gradient(Wd, Xd, yd, grad, loss, ws, stream)
+        net.profile(False)
+        torch.cuda.synchronize()
+        prods, _ = TM.products_of(net.profile_read())
+        del ws, grad, Wd, Xd
+        count = {}
+        for pr in prods:
+            if pr["form"] in TM.FORMS:
+                # A weight gradient's recorded n counts the bias's implicit ones column, which the
+                # stored operand does not hold: both sides take the stored width.
+                n = pr["n"] - 1 if pr["form"] == "tn" and pr["n"] % 4 == 1 else pr["n"]
+                key = (pr["form"], pr["m"], n, pr["k"])
+                count[key] = count.get(key, 0) + 1
+        lines += [f"## {name}", "", "| form | m | n | k | per step | ours µs | torch.mm µs | ours / torch | ours TFLOP/s | "
+                  "torch TFLOP/s | diff |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        tot_o = tot_t = 0.0
+        for (form, m, n, k), c in sorted(count.items(), key=lambda kv: -2.0 * kv[0][1] * kv[0][2] * kv[0][3] * kv[1]):
+            a_t, b_t = TM.FORMS[form]
+            A = torch.randn((k, m) if a_t else (m, k), device=dev)
+            B = torch.randn((k, n) if b_t else (n, k), device=dev)
+            Co = torch.empty(m, n, device=dev)
+            Ct = torch.empty(m, n, device=dev)
+            opA = A.t() if a_t else A
+            opB = B if b_t else B.t()
+            wsz = S.gemm_workspace_bytes(m, n, k, a_t, b_t)
+            gws = torch.empty(max(wsz, 256) // 4 + 64, device=dev)
+            t_o = median_us(lambda: S.gemm(A, B, Co, a_t, b_t, gws, stream))
+            t_t = median_us(lambda: torch.mm(opA, opB, out=Ct))
+            torch.cuda.synchronize()
+            diff = float((Co - Ct).abs().max() / Ct.abs().max().clamp_min(1e-30))
+            fl = 2.0 * m * n * k
+            tot_o += c * t_o
+            tot_t += c * t_t
+            lines.append(f"| {form} | {m} | {n} | {k} | {c} | {t_o:.1f} | {t_t:.1f} | {t_o / t_t:.2f} | "
+                         f"{fl / t_o / 1e6:.1f} | {fl / t_t / 1e6:.1f} | {diff:.1e} |")
+            del A, B, Co, Ct, gws
+        torch.cuda.empty_cache()
+        lines += ["", f"Sum over one step's products: ours {tot_o / 1e3:.3f} ms, torch.mm {tot_t / 1e3:.3f} ms "
+                  f"(ratio {tot_o / tot_t:.2f}).", ""]
+        summary[name] = {"ours_ms": tot_o / 1e3, "torch_ms": tot_t / 1e3}
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"vendor_compare": summary}))
+
+
 def sprint_report(out_path, workload="mlp5000"):
     """SPRINT's asynchronous workers and updater on one GPU (section 3.4, Algorithms 1 and 2): for
     several worker counts and sub-batch sizes, the throughput, T_GPU, T_Update, the measured average
@@ -1147,6 +1243,9 @@ def main():
                          "'traffic FETCH_DIR WRITE_DIR WORKLOAD CALIB_MIB OUT.md OUT.json', 'mfma DIR OUT.md TITLE' "
                          "(with --summary-command giving the command text to record)")
     ap.add_argument("--summary-command", default="", help="the command(s) that produced the summarized output")
+    ap.add_argument("--vendor-compare", metavar="OUT_MD", default=None,
+                    help="time every distinct product of each workload's step on sgd_gemm and on torch.mm (the "
+                         "vendor fp32 GEMM) and write the comparison instead of the step bench")
     args = ap.parse_args()
     if args.summarize:
         kind, rest = args.summarize[0], args.summarize[1:]
@@ -1172,6 +1271,9 @@ def main():
         return
     if args.timing_model:
         timing_model_report(args.timing_model, args.timing_model_raw)
+        return
+    if args.vendor_compare:
+        vendor_compare(args.vendor_compare)
         return
     import workloads
     if args.copy_calibration_mib:
