@@ -1086,6 +1086,20 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     if constexpr (kSkip) {
       if (na < TM || nc < TN) slices(std::true_type{});
       else slices(std::false_type{});
+    } else if (__builtin_amdgcn_readfirstlane(arows <= wm * WM || p.Nt - n0 <= wn * WN)) {
+      // The narrow tiles' wavefront whose whole 32-row (32-column) part lies outside the output -- columns
+      // 32..63 of a 64-wide tile over a first conv layer's 29-column weight gradient, rows 32..63 of a
+      // 64-row tile over a batch-32 fc layer -- only does its share of the loads: nothing stores its
+      // accumulators (zeros) except as a zero partial tile.
+      for (int i = 0; i < nsl; ++i) {
+        const int cur = i % kDmaStages;
+        wait_vmcnt<kLoads * (kDmaStages - 2)>();
+        if (ones_col >= 0) SB::ones_fixup(Bs[cur], ones_col, i * kDmaBK, kval);
+        lds_barrier();
+        const int nx = i + kDmaStages - 1;
+        load_a(As[nx % kDmaStages], nx * kDmaBK);
+        load_b(Bs[nx % kDmaStages], nx * kDmaBK);
+      }
     } else {
       for (int i = 0; i < nsl; ++i) {  // the same loop as `slices`, without the skip
         const int cur = i % kDmaStages;

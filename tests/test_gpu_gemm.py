@@ -33,11 +33,13 @@ U = 2.0 ** -24
 # the same k-ranges): 2 x 2 groups in (256, 192), 2 x 1 in (256, 2100), 4 x 8 with ragged edges in
 # (500, 1000), and 8 x 1 in (1000, 600).  One block per tile over more tiles than resident blocks, with a
 # ragged last tile row and column, puts the edge tiles last: (3900, 3950) has 961 tiles (no XCD runs),
-# (4000, 4000) 1024 (or 3969 64 x 64 tiles in the tn form).
+# (4000, 4000) 1024 (or 3969 64 x 64 tiles in the tn form).  With at most 32 valid rows (columns) in a
+# 64-row (64-column) tile the outer wavefronts only load: (32, 2048) on 64 x 128 tiles, (300, 20) on 128 x 64,
+# and (64, 28) on 64 x 64 in the tn form.
 SHAPES = [(77, 130, 1000, 0), (256, 192, 4096, 0), (128, 128, 30000, 0), (1000, 36, 4, 0), (5, 3, 7, 0),
           (300, 516, 260, 12), (513, 257, 1031, 3), (4096, 64, 576, 0), (200, 1100, 300, 0), (256, 2100, 4096, 0),
           (64, 28, 100000, 0), (48, 60, 5000, 0), (500, 1000, 3000, 0), (1000, 600, 4000, 0), (3900, 3950, 200, 0),
-          (4000, 4000, 64, 0)]
+          (4000, 4000, 64, 0), (32, 2048, 3000, 0), (300, 20, 4000, 0)]
 
 
 def stored(seed, tid, rows, cols, pad):
