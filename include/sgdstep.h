@@ -295,6 +295,27 @@ size_t sgd_gemm_workspace_bytes(const sgd_gemm_args* g);
 int sgd_gemm(const sgd_gemm_args* g, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Schedule query for the tile kernels behind sgd_gemm and the step's
+ * products (host only: no device work, no device needed; the compute-unit
+ * count is the current device's, 256 without one).  For an m x n x k
+ * product of the given forms (as sgd_gemm's a_t / b_t; n counts a weight
+ * gradient's bias column) it writes the schedule the library picks when the
+ * product takes the direct-load tile kernels, not gathered, to
+ * out[0..11]: tile rows, tile columns, grid (blocks), tiles done whole
+ * first, stream-K k-slices (0: none), block-group tile rows and columns (1
+ * and 1: ungrouped), edge-last bits (1: ragged last tile row last, 2: ragged
+ * last tile column last), tile rows count, tile columns count, 16-deep
+ * k-slices per tile, compute units.  A product can still take another
+ * kernel (short reductions, a logits layer's skinny products, unaligned
+ * operands); the query describes the tile schedule alone.  It serves tests
+ * and tools that check the schedule's invariants (every (tile, k-slice)
+ * covered once, stream-K slots in k order) on the CPU; it is not a step of
+ * the method.  nout >= 12.  Errors: SGD_EINVAL (sizes < 1, null out,
+ * nout < 12, 2^22 or more 64 x 64 output tiles).
+ */
+int sgd_gemm_plan(int m, int n, int k, int a_t, int b_t, int64_t* out, int nout);
+
+/*
  * Implicit-GEMM convolution (on by default).  A conv layer whose input is
  * an activation of this network with Ci % 16 == 0 gathers the im2col
  * operand of its forward and dedw products straight from that activation

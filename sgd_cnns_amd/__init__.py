@@ -33,7 +33,7 @@ LAYOUT_NHWC, LAYOUT_NCHW, LAYOUT_ROWS = 1, 2, 3
 EXPORTS = ["sgd_create_net", "sgd_destroy_net", "sgd_param_count", "sgd_param_offsets", "sgd_workspace_bytes",
            "sgd_tensor_info", "sgd_compute_gradient", "sgd_compute_gradient_into", "sgd_compute_gradient_into_scaled", "sgd_accumulate_grad",
            "sgd_accumulate_grads",
-           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_debug", "sgd_set_overlap", "sgd_get_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_profile", "sgd_profile_read",
+           "sgd_apply_update", "sgd_apply_fused", "sgd_train_step", "sgd_set_debug", "sgd_set_overlap", "sgd_get_overlap", "sgd_set_implicit_conv", "sgd_gemm", "sgd_gemm_workspace_bytes", "sgd_gemm_plan", "sgd_profile", "sgd_profile_read",
            "sgd_sprint_workspace_bytes", "sgd_sprint_run", "sgd_train_step_graph", "sgd_step_graph_launch",
            "sgd_step_graph_destroy", "sgd_stream_ref", "sgd_train_step_noalloc", "sgd_last_error"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -122,6 +122,7 @@ def lib():
             "sgd_set_implicit_conv": (i, [P, i]),
             "sgd_gemm_workspace_bytes": (sz, [C.POINTER(SgdGemmArgs)]),
             "sgd_gemm": (i, [C.POINTER(SgdGemmArgs), P, sz, P]),
+            "sgd_gemm_plan": (i, [i, i, i, i, i, C.POINTER(i64), i]),
             "sgd_profile_read": (i, [P, C.POINTER(SgdKernelTime), i]),
             "sgd_sprint_workspace_bytes": (sz, [P, C.POINTER(SgdSprintConfig)]),
             "sgd_sprint_run": (i, [P, C.POINTER(SgdSprintConfig), P, P, C.POINTER(SgdRule), P, P, i64, P, sz, P,
@@ -409,6 +410,16 @@ def _gemm_args(A, B, C_, a_t, b_t):
                          f"and C {tuple(C_.shape)} do not form a product")
     return SgdGemmArgs(m, n, k, int(a_t), int(b_t), A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0),
                        C_.data_ptr(), C_.stride(0))
+
+
+PLAN_FIELDS = ("bm", "bn", "grid", "dp", "sk_iters", "rg", "cg", "edge_last", "tiles_m", "tiles_n", "ipt", "cus")
+
+
+def gemm_plan(m, n, k, a_t=False, b_t=False):
+    """The tile kernels' schedule for an m x n x k product (host only; see sgd_gemm_plan), as a dict."""
+    out = (C.c_int64 * len(PLAN_FIELDS))()
+    _check(lib().sgd_gemm_plan(int(m), int(n), int(k), int(a_t), int(b_t), out, len(PLAN_FIELDS)))
+    return dict(zip(PLAN_FIELDS, (int(v) for v in out)))
 
 
 def gemm_workspace_bytes(m, n, k, a_t=False, b_t=False):

@@ -138,4 +138,10 @@ int gemm_pick_splits(int M, int Nt, int K);
 // `fused`: the dedw form with an update rule in the epilogue.
 int64_t gemm_scratch_floats(int M, int Nt, int K, bool a_t, bool b_t, bool fused, int splits);
 
+// The automatic direct-load (gemm_dma) schedule of an M x Nt x K product of the given form (0 nt, 1 tn,
+// 2 nn, 3 tt), not gathered, with unlimited scratch: out[0..11] = tile rows, tile columns, grid, whole tiles
+// first, stream-K k-slices, group rows, group columns, edge-last bits, tile rows count, tile columns count,
+// k-slices per tile, compute units.  Host only.
+int gemm_plan_query(int M, int Nt, int K, int form, int64_t* out);
+
 }  // namespace sgd

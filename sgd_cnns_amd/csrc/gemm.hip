@@ -1950,6 +1950,20 @@ bool smallk_nn_ok(const GemmDesc& d, int form) {
          (d.epi == EPI_STORE || (d.epi == EPI_MASK && d.ldm % 4 == 0 && aligned16(d.mask)));
 }
 
+// The automatic gemm_dma schedule of an M x Nt x K product on configuration cfg with cap floats of
+// partial-tile scratch: the stream-K plan, its grouped form, and the edge-last tile order.
+SkPlan auto_plan(int cfg, int M, int Nt, int K, int64_t cap) {
+  const Cfg& c = kDma[cfg];
+  const int64_t T = tiles_of(c, M, Nt), ipt = ceil_div(K, kDmaBK), tile = (int64_t)c.bm * c.bn;
+  const Machine mc = machine_for(cfg);
+  SkPlan plan = sk_choose(T, ipt, mc, tile, cap);
+  if (group_sk) sk_group(plan, ceil_div(M, c.bm), ceil_div(Nt, c.bn), ipt);
+  // One block per tile over more than one round of resident blocks: ragged edge tiles last.
+  if (edge_last && plan.sk_iters == 0 && plan.dp == T && T == plan.grid && T > (int64_t)mc.cus * mc.occ)
+    plan.edge_last = (M % c.bm ? 1 : 0) | (Nt % c.bn ? 2 : 0);
+  return plan;
+}
+
 int gemm_launch(const GemmDesc& d, hipStream_t s) {
   const bool ones = d.ones_out != nullptr;
   KArgs a{};
@@ -2057,12 +2071,7 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
         return SGD_EINVAL;
       }
     } else {
-      plan = sk_choose(T, ipt, machine_for(cfg), tile, cap);
-      if (group_sk) sk_group(plan, ceil_div(d.M, c.bm), ceil_div(a.Nt, c.bn), ipt);
-      // One block per tile over more than one round of resident blocks: ragged edge tiles last.
-      const Machine mc = machine_for(cfg);
-      if (edge_last && plan.sk_iters == 0 && plan.dp == T && T == plan.grid && T > (int64_t)mc.cus * mc.occ)
-        plan.edge_last = (d.M % c.bm ? 1 : 0) | (a.Nt % c.bn ? 2 : 0);
+      plan = auto_plan(cfg, d.M, a.Nt, d.K, cap);
     }
     if (plan.sk_iters > 0 && plan.sk_iters * plan.grid >= ((int64_t)1 << 31)) {
       set_error("gemm: stream-K schedule too long for 32-bit range arithmetic");
@@ -2158,6 +2167,16 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     prof_end(s);
     if (int e = check_launch("splitk_reduce")) return e;
   }
+  return 0;
+}
+
+int gemm_plan_query(int M, int Nt, int K, int form, int64_t* out) {
+  const int cfg = dma_cfg(M, Nt, K, form, false);
+  const Cfg& c = kDma[cfg];
+  const SkPlan p = auto_plan(cfg, M, Nt, K, INT64_MAX);
+  const int64_t v[12] = {c.bm, c.bn, p.grid, p.dp, p.sk_iters, p.rg, p.cg, p.edge_last,
+                         ceil_div(M, c.bm), ceil_div(Nt, c.bn), ceil_div(K, kDmaBK), machine_for(cfg).cus};
+  for (int i = 0; i < 12; ++i) out[i] = v[i];
   return 0;
 }
 

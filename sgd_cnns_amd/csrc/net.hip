@@ -964,6 +964,14 @@ static int gemm_args_ok(const sgd_gemm_args* g) {
   return SGD_OK;
 }
 
+int sgd_gemm_plan(int m, int n, int k, int a_t, int b_t, int64_t* out, int nout) {
+  if (m < 1 || n < 1 || k < 1 || !out || nout < 12) return fail(SGD_EINVAL, "sgd_gemm_plan: bad arguments");
+  if (((int64_t)m + 63) / 64 * (((int64_t)n + 63) / 64) >= ((int64_t)1 << 22))
+    return fail(SGD_EINVAL, "sgd_gemm_plan: more than 2^22 output tiles");
+  const int form = a_t ? (b_t ? 1 : 3) : (b_t ? 2 : 0);
+  return sgd::gemm_plan_query(m, n, k, form, out);
+}
+
 size_t sgd_gemm_workspace_bytes(const sgd_gemm_args* g) {
   if (gemm_args_ok(g)) return 0;
   const int splits = sgd::gemm_pick_splits(g->m, g->n, g->k);
