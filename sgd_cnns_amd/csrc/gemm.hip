@@ -619,6 +619,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr unsigned kOffBad = 0x80000000u;  // out-of-range buffer offset: the load returns zeros
 constexpr int kDmaBK = 16;
 constexpr int kDmaStages = 3;
+constexpr bool pipe_slices = true;  // the pipelined slice loop (see gemm_dma)
 // Weight gradients with at most this many k-slices per tile (k <= 128: an fc layer's dedw at batch
 // <= 128) take 64x64 tiles and load their epilogue's memory operands ahead of the main loop.
 constexpr int kPrefetchSlices = 8;
@@ -933,7 +934,7 @@ __device__ __forceinline__ void edge_last_coords(int b, int G, int tiles_m, int 
 
 // GA: the A operand is a K-contiguous convolution gather (DmaKg); GB: the B
 // operand is a row-contiguous one (DmaTg).
-template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
+template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false, bool PIPE = false>
 __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -1006,6 +1007,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     // occupy are shared with the other resident blocks.  (128 x 128 tiles only: in the narrower
     // instances the second loop copy costs the registers of a fourth wavefront per SIMD.)
     constexpr bool kSkip = TM == 2 && TN == 2;
+    constexpr bool kPipe = PIPE && kSkip && EM != EM_UPDATE && EM != EM_GENERIC;
     const int na = kSkip ? __builtin_amdgcn_readfirstlane(min(TM, max(0, (arows - wm * WM + 31) >> 5))) : TM;
     const int nc = kSkip ? __builtin_amdgcn_readfirstlane(min(TN, max(0, (p.Nt - n0 - wn * WN + 31) >> 5))) : TN;
     const i32x4 ra = buffer_rsrc(GA ? p.A : AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
@@ -1053,6 +1055,60 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     // narrower instances keep the plain loop written out below: compiled through the lambda they
     // take more registers and ran 3% slower (VGG-16's 128 x 64 and 64 x 128 products, same-box
     // comparison).
+    // Pipelined form (kPipe): a slice's operands are all read from LDS before its first product, and
+    // the wait and barrier that publish the next slice (and free this slice's buffer for the load two
+    // slices ahead) sit between the slice's two operand groups, so the barrier and the next slice's
+    // first LDS reads overlap products still in the matrix pipe rather than leaving it idle; with one
+    // or two wavefronts per SIMD the other wavefronts cannot cover that gap.  Same products in the
+    // same order; 16 more VGPRs (not for the update instances, which then lose their third block).
+    auto slices_pipe = [&](auto skip_tag) {
+      constexpr bool SKIP = decltype(skip_tag)::value;
+      constexpr int NG = kDmaBK / 8;
+      static_assert(NG == 2, "two operand groups per slice");
+      wait_vmcnt<kLoads * (kDmaStages - 2)>();  // slice 0 is in LDS
+      if (ones_col >= 0) SB::ones_fixup(Bs[0], ones_col, 0, kval);
+      lds_barrier();
+      load_a(As[(kDmaStages - 1) % kDmaStages], (kDmaStages - 1) * kDmaBK);
+      load_b(Bs[(kDmaStages - 1) % kDmaStages], (kDmaStages - 1) * kDmaBK);
+      for (int i = 0; i < nsl; ++i) {
+        const int cur = i % kDmaStages;
+        float4 av[NG][TM], bv[NG][TN];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+#pragma unroll
+          for (int a = 0; a < TM; ++a) av[g][a] = SA::operand(As[cur], wm * WM + a * 32 + li, g, lh);
+#pragma unroll
+          for (int c = 0; c < TN; ++c) bv[g][c] = SB::operand(Bs[cur], wn * WN + c * 32 + li, g, lh);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of the products
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (g == 1) {
+            // Publish slice i + 1 and refill this slice's buffer (all of its reads are done: the
+            // barrier waits for them) with slice i + S.
+            __builtin_amdgcn_sched_barrier(0);
+            const int nxt = (i + 1) % kDmaStages;
+            wait_vmcnt<kLoads * (kDmaStages - 2)>();
+            if (ones_col >= 0) SB::ones_fixup(Bs[nxt], ones_col, (i + 1) * kDmaBK, kval);
+            lds_barrier();
+            const int nx = i + kDmaStages;
+            load_a(As[cur], nx * kDmaBK);
+            load_b(Bs[cur], nx * kDmaBK);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int c = 0; c < TN; ++c) {
+              if (SKIP && (a >= na || c >= nc)) continue;
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[g][a].x, bv[g][c].x, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[g][a].y, bv[g][c].y, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[g][a].z, bv[g][c].z, acc[a][c], 0, 0, 0);
+              acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[g][a].w, bv[g][c].w, acc[a][c], 0, 0, 0);
+            }
+        }
+      }
+    };
     auto slices = [&](auto skip_tag) {
       constexpr bool SKIP = decltype(skip_tag)::value;
       for (int i = 0; i < nsl; ++i) {
@@ -1083,7 +1139,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
         }
       }
     };
-    if constexpr (kSkip) {
+    if constexpr (kSkip && kPipe) {
+      if (na < TM || nc < TN) slices_pipe(std::true_type{});
+      else slices_pipe(std::false_type{});
+    } else if constexpr (kSkip) {
       if (na < TM || nc < TN) slices(std::true_type{});
       else slices(std::false_type{});
     } else if (__builtin_amdgcn_readfirstlane(arows <= wm * WM || p.Nt - n0 <= wn * WN)) {
@@ -1569,53 +1628,56 @@ struct DmaFns {
   FixKernel fix;
   int bm, bn;
 };
-template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
+template <int BM, int BN, bool PIPE, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
 DmaFns dma_inst() {
-  return {gemm_dma<BM, BN, AT, BT, EM, GA, GB>, gemm_sk_fixup<BM, BN>, BM, BN};
+  constexpr bool kPipe = PIPE && EM != EM_UPDATE && EM != EM_GENERIC;  // else the plain instance
+  return {gemm_dma<BM, BN, AT, BT, EM, GA, GB, kPipe>, gemm_sk_fixup<BM, BN>, BM, BN};
 }
-template <int BM, int BN>
+template <int BM, int BN, bool PIPE = false>
 DmaFns dma_fns_of(int form, int em, int gather) {
   if (gather == 1) {  // conv forward (bias) and dedx (mask or plain store)
-    if (em == EM_BIAS) return dma_inst<BM, BN, false, false, EM_BIAS, true>();
-    if (em == EM_MASK) return dma_inst<BM, BN, false, false, EM_MASK, true>();
-    if (em == EM_STORE) return dma_inst<BM, BN, false, false, EM_STORE, true>();
-    return dma_inst<BM, BN, false, false, EM_GENERIC, true>();
+    if (em == EM_BIAS) return dma_inst<BM, BN, PIPE, false, false, EM_BIAS, true>();
+    if (em == EM_MASK) return dma_inst<BM, BN, PIPE, false, false, EM_MASK, true>();
+    if (em == EM_STORE) return dma_inst<BM, BN, PIPE, false, false, EM_STORE, true>();
+    return dma_inst<BM, BN, PIPE, false, false, EM_GENERIC, true>();
   }
   if (gather == 2) {  // conv dedw
-    if (em == EM_DW) return dma_inst<BM, BN, true, true, EM_DW, false, true>();
-    if (em == EM_UPDATE) return dma_inst<BM, BN, true, true, EM_UPDATE, false, true>();
-    return dma_inst<BM, BN, true, true, EM_GENERIC, false, true>();
+    if (em == EM_DW) return dma_inst<BM, BN, PIPE, true, true, EM_DW, false, true>();
+    if (em == EM_UPDATE) return dma_inst<BM, BN, PIPE, true, true, EM_UPDATE, false, true>();
+    return dma_inst<BM, BN, PIPE, true, true, EM_GENERIC, false, true>();
   }
   switch (form) {
     case 0:
-      if (em == EM_BIAS) return dma_inst<BM, BN, false, false, EM_BIAS>();
-      if (em == EM_STORE) return dma_inst<BM, BN, false, false, EM_STORE>();
-      return dma_inst<BM, BN, false, false, EM_GENERIC>();
+      if (em == EM_BIAS) return dma_inst<BM, BN, PIPE, false, false, EM_BIAS>();
+      if (em == EM_STORE) return dma_inst<BM, BN, PIPE, false, false, EM_STORE>();
+      return dma_inst<BM, BN, PIPE, false, false, EM_GENERIC>();
     case 1:
-      if (em == EM_DW) return dma_inst<BM, BN, true, true, EM_DW>();
-      if (em == EM_UPDATE) return dma_inst<BM, BN, true, true, EM_UPDATE>();
-      if (em == EM_STORE) return dma_inst<BM, BN, true, true, EM_STORE>();
-      return dma_inst<BM, BN, true, true, EM_GENERIC>();
+      if (em == EM_DW) return dma_inst<BM, BN, PIPE, true, true, EM_DW>();
+      if (em == EM_UPDATE) return dma_inst<BM, BN, PIPE, true, true, EM_UPDATE>();
+      if (em == EM_STORE) return dma_inst<BM, BN, PIPE, true, true, EM_STORE>();
+      return dma_inst<BM, BN, PIPE, true, true, EM_GENERIC>();
     case 2:
-      if (em == EM_MASK) return dma_inst<BM, BN, false, true, EM_MASK>();
-      if (em == EM_STORE) return dma_inst<BM, BN, false, true, EM_STORE>();
-      return dma_inst<BM, BN, false, true, EM_GENERIC>();
+      if (em == EM_MASK) return dma_inst<BM, BN, PIPE, false, true, EM_MASK>();
+      if (em == EM_STORE) return dma_inst<BM, BN, PIPE, false, true, EM_STORE>();
+      return dma_inst<BM, BN, PIPE, false, true, EM_GENERIC>();
     default:
-      return dma_inst<BM, BN, true, false, EM_GENERIC>();
+      return dma_inst<BM, BN, PIPE, true, false, EM_GENERIC>();
   }
 }
 // 64x64 is instantiated for the one product dma_cfg gives it: dedw (A^T B,
 // not gathered); anything else gets no kernel.
 DmaFns dma_fns_64x64(int form, int em, int gather) {
   if (gather || form != 1) return {nullptr, nullptr, 0, 0};
-  if (em == EM_DW) return dma_inst<64, 64, true, true, EM_DW>();
-  if (em == EM_UPDATE) return dma_inst<64, 64, true, true, EM_UPDATE>();
-  if (em == EM_STORE) return dma_inst<64, 64, true, true, EM_STORE>();
-  return dma_inst<64, 64, true, true, EM_GENERIC>();
+  if (em == EM_DW) return dma_inst<64, 64, false, true, true, EM_DW>();
+  if (em == EM_UPDATE) return dma_inst<64, 64, false, true, true, EM_UPDATE>();
+  if (em == EM_STORE) return dma_inst<64, 64, false, true, true, EM_STORE>();
+  return dma_inst<64, 64, false, true, true, EM_GENERIC>();
 }
-DmaFns dma_fns(int cfg, int form, int em, int gather) {
+// pipe: the 128x128 instances with the pipelined slice loop (more VGPRs than three blocks per CU allow),
+// for schedules of at most two blocks per CU.
+DmaFns dma_fns(int cfg, int form, int em, int gather, bool pipe) {
   switch (cfg) {
-    case 0: return dma_fns_of<128, 128>(form, em, gather);
+    case 0: return pipe ? dma_fns_of<128, 128, true>(form, em, gather) : dma_fns_of<128, 128>(form, em, gather);
     case 1: return dma_fns_of<128, 64>(form, em, gather);
     case 2: return dma_fns_of<64, 128>(form, em, gather);
     default: return dma_fns_64x64(form, em, gather);
@@ -2101,7 +2163,8 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     a.ldc = d.ldc;
     a.split = 0;
     a.k_per_split = (int)round_up(d.K, kDmaBK);
-    const DmaFns f = dma_fns(cfg, form, epi_mode(d, form), d.gather);
+    const DmaFns f = dma_fns(cfg, form, epi_mode(d, form), d.gather,
+                             pipe_slices && cfg == 0 && plan.grid <= 2 * machine_for(cfg).cus);
     if (!f.main) {
       set_error("gemm: no 64x64 kernel for this product form");
       return SGD_EINVAL;

@@ -40,4 +40,11 @@ def test_bench_kernel_names():
     assert bench.bench_kernel_name(
         "void sgd::(anonymous namespace)::gemm_dma<128, 128, false, true, 3, false, false>(KArgs, SkArgs)") == \
         "gemm_dma_128x128_nn"
+    # the pipelined-loop instances carry one more template flag
+    assert bench.bench_kernel_name(
+        "void sgd::(anonymous namespace)::gemm_dma<128, 128, false, false, 2, true, false, true>(KArgs, SkArgs)") == \
+        "gemm_conv_fwd_128x128"
+    assert bench.bench_kernel_name(
+        "void sgd::(anonymous namespace)::gemm_dma<128, 128, false, false, 2, false, false, false>(KArgs, SkArgs)") == \
+        "gemm_dma_128x128_nt"
     assert bench.is_product("gemm_dw_short_k32") and not bench.is_product("softmax_ce")
