@@ -1007,7 +1007,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     // occupy are shared with the other resident blocks.  (128 x 128 tiles only: in the narrower
     // instances the second loop copy costs the registers of a fourth wavefront per SIMD.)
     constexpr bool kSkip = TM == 2 && TN == 2;
-    constexpr bool kPipe = PIPE && kSkip && EM != EM_UPDATE && EM != EM_GENERIC;
+    constexpr bool kPipe = PIPE && kSkip && !AT && EM != EM_UPDATE && EM != EM_GENERIC;
     const int na = kSkip ? __builtin_amdgcn_readfirstlane(min(TM, max(0, (arows - wm * WM + 31) >> 5))) : TM;
     const int nc = kSkip ? __builtin_amdgcn_readfirstlane(min(TN, max(0, (p.Nt - n0 - wn * WN + 31) >> 5))) : TN;
     const i32x4 ra = buffer_rsrc(GA ? p.A : AT ? p.A + (int64_t)kbeg * p.lda + m0 : p.A + (int64_t)m0 * p.lda + kbeg);
@@ -1630,7 +1630,9 @@ struct DmaFns {
 };
 template <int BM, int BN, bool PIPE, bool AT, bool BT, int EM, bool GA = false, bool GB = false>
 DmaFns dma_inst() {
-  constexpr bool kPipe = PIPE && EM != EM_UPDATE && EM != EM_GENERIC;  // else the plain instance
+  // else the plain instance; the weight-gradient form (A^T B, both operands read from LDS as single
+  // floats) ran 3-8% slower pipelined alone (more LDS reads in flight than the counter holds).
+  constexpr bool kPipe = PIPE && !AT && EM != EM_UPDATE && EM != EM_GENERIC;
   return {gemm_dma<BM, BN, AT, BT, EM, GA, GB, kPipe>, gemm_sk_fixup<BM, BN>, BM, BN};
 }
 template <int BM, int BN, bool PIPE = false>
