@@ -120,6 +120,10 @@ struct GemmDesc {
   // not for convolutions, whose explicit and implicit paths keep one sum
   // order.
   bool skinny = false;
+  // The product runs beside the side stream's weight-gradient products (an input-gradient product of the
+  // overlapped backward pass): it keeps the instances that fit three blocks per CU, so those products
+  // keep their share of each CU.
+  bool beside_side = false;
   // Implicit GEMM: 1 = A (K-contiguous, not transposed) is gathered by cv
   // (A and lda are ignored); 2 = B (row-contiguous, transposed) is (B and
   // ldb are ignored).  Needs cv.SC % 16 == 0 for A, % 4 == 0 for B.

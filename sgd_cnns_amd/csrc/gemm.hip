@@ -2165,8 +2165,11 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     a.ldc = d.ldc;
     a.split = 0;
     a.k_per_split = (int)round_up(d.K, kDmaBK);
+    // The pipelined instances (two blocks per CU) for schedules of at most two blocks per CU, except
+    // beside the side stream's products: there they made VGG-16's step 0.4% slower (same-box A/B), the
+    // MLP's and VGG-CIFAR's no faster.
     const DmaFns f = dma_fns(cfg, form, epi_mode(d, form), d.gather,
-                             pipe_slices && cfg == 0 && plan.grid <= 2 * machine_for(cfg).cus);
+                             pipe_slices && !d.beside_side && cfg == 0 && plan.grid <= 2 * machine_for(cfg).cus);
     if (!f.main) {
       set_error("gemm: no 64x64 kernel for this product form");
       return SGD_EINVAL;

@@ -673,6 +673,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.mask = mask ? at<float>(ws, src.out) : nullptr;
         d.ldm = s.Ci;
         d.skinny = true;
+        d.beside_side = overlap;
         d.splits = s.split_dx;
         d.partial = partial;
         d.partial_floats = net->partial_floats;
@@ -756,6 +757,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.mask = mask ? at<float>(ws, src.out) : nullptr;
         d.ldm = s.Ci;
         d.splits = 1;
+        d.beside_side = overlap;
         d.partial = partial;
         d.partial_floats = net->partial_floats;
         if ((e = gemm(d, st))) continue;
@@ -774,6 +776,7 @@ int run_backward(sgd_net* net, const float* Wt, const float* X, float* grad, boo
         d.flops = 2.0 * (double)P * s.K * (double)s.Co;
         d.epi = EPI_STORE;
         d.splits = s.split_dx;
+        d.beside_side = overlap;
         d.partial = partial;
         d.partial_floats = net->partial_floats;
         if ((e = gemm(d, st))) continue;
