@@ -619,7 +619,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr unsigned kOffBad = 0x80000000u;  // out-of-range buffer offset: the load returns zeros
 constexpr int kDmaBK = 16;
 constexpr int kDmaStages = 3;
-constexpr bool pipe_slices = true;  // the pipelined slice loop (see gemm_dma)
+// Schedule choices that can be switched off as a whole (each is measured against its absence in the
+// design notes): the pipelined slice loop (gemm_dma), the grouped stream-K form (sk_group) and the
+// edge-tiles-last order (edge_last_coords).  Results do not depend on the last, and the first keeps the
+// products' order; grouping changes where k is cut.
+constexpr bool pipe_slices = true;
 // Weight gradients with at most this many k-slices per tile (k <= 128: an fc layer's dedw at batch
 // <= 128) take 64x64 tiles and load their epilogue's memory operands ahead of the main loop.
 constexpr int kPrefetchSlices = 8;
@@ -1818,8 +1822,8 @@ SkPlan sk_choose(int64_t T, int64_t I, const Machine& m, int64_t tile_floats, in
 // number of ranges a tile is cut into and the slot count are those of the
 // ungrouped plan.
 constexpr int kGroupRows = 8, kGroupCols = 8;
-constexpr bool group_sk = true;
-constexpr bool edge_last = true;
+constexpr bool group_sk = true;   // see pipe_slices
+constexpr bool edge_last = true;  // see pipe_slices
 void sk_group(SkPlan& p, int64_t tiles_m, int64_t tiles_n, int64_t ipt) {
   p.rg = p.cg = 1;
   if (p.dp != 0 || p.sk_iters <= 0 || p.grid % 8 || tiles_m > kGroupRows) return;
