@@ -251,6 +251,48 @@ __global__ __launch_bounds__(kBlock) void repack_conv_weights_kernel(RepackJobs 
   }
 }
 
+// Small layers of other filter sizes (LeNet-5's 5x5 convolutions: a few thousand floats in all):
+// one thread per destination float of W' and W'', no staging.  There the staged kernel runs as one or
+// two blocks whose serial loops bound the copy; here every thread does one load and one store.
+// Threads are numbered job by job: W' (Co x ldk, the zero columns included), then W'' if wanted.
+constexpr int64_t kRepackDirectMax = 1 << 16;  // destination floats of all such layers
+struct RepackDirectJob {
+  const float* w;
+  float* wrep;
+  float* wdx;  // nullptr: no W''
+  int Co, Ci, c, ldk;
+  int start;  // first thread of the job
+};
+struct RepackDirectJobs {
+  RepackDirectJob j[kMaxRepackJobs];
+  int n, total;
+};
+
+__global__ __launch_bounds__(kBlock) void repack_conv_direct_kernel(RepackDirectJobs J) {
+  const int t = (int)(blockIdx.x * kBlock + threadIdx.x);
+  if (t >= J.total) return;
+  int l = 0;
+  while (l + 1 < J.n && J.j[l + 1].start <= t) ++l;
+  const RepackDirectJob b = J.j[l];
+  const int cc = b.c * b.c;
+  int i = t - b.start;
+  const int nrep = b.Co * b.ldk;
+  if (i < nrep) {  // W'[co][tap*Ci + ci]
+    const int co = i / b.ldk, k = i - co * b.ldk;
+    float v = 0.f;
+    if (k < cc * b.Ci) {
+      const int tap = k / b.Ci, ci = k - tap * b.Ci;
+      v = b.w[(co * b.Ci + ci) * cc + tap];
+    }
+    b.wrep[i] = v;
+    return;
+  }
+  i -= nrep;  // W''[ci][tap*Co + co]
+  const int r = i / b.Co, co = i - r * b.Co;
+  const int ci = r / cc, tap = r - ci * cc;
+  b.wdx[i] = b.w[(co * b.Ci + ci) * cc + tap];
+}
+
 // The same for 3x3 filters (every conv of the VGG networks) with the tile
 // fixed at 32 output x 16 input channels: the index arithmetic is shifts and
 // multiplications by constants, and the 18.5 KiB tile lets more blocks share
@@ -639,6 +681,32 @@ int repack_conv_weights(const RepackLayer* layers, int n, hipStream_t s) {
       bytes = 0.0;
       return check_launch("repack_conv_weights");
     };
+    if (!three) {
+      // All of the other layers in one direct launch when they are small.
+      RepackDirectJobs D{};
+      int64_t total = 0;
+      double dbytes = 0.0;
+      for (int i = 0; i < n; ++i) {
+        const RepackLayer& L = layers[i];
+        if (L.c == 3) continue;
+        const int64_t cc = (int64_t)L.c * L.c, wfl = (int64_t)L.Co * L.Ci * cc;
+        if (D.n == kMaxRepackJobs) {
+          total = kRepackDirectMax + 1;
+          break;
+        }
+        D.j[D.n++] = {L.w, L.wrep, L.wdx, L.Co, L.Ci, L.c, L.ldk, (int)std::min<int64_t>(total, INT32_MAX)};
+        total += (int64_t)L.Co * L.ldk + (L.wdx ? wfl : 0);
+        dbytes += 4.0 * ((L.wdx ? 2.0 : 1.0) * wfl + (double)L.Co * L.ldk + (L.wdx ? wfl : 0.0));
+      }
+      if (D.n > 0 && total <= kRepackDirectMax) {
+        D.total = (int)total;
+        prof_begin("repack_weights", 0, dbytes, s);
+        hipLaunchKernelGGL(repack_conv_direct_kernel, dim3((unsigned)ceil_div(total, kBlock)), dim3(kBlock), 0, s, D);
+        prof_end(s);
+        if (int e = check_launch("repack_conv_weights")) return e;
+        continue;
+      }
+    }
     for (int i = 0; i < n; ++i) {
       const RepackLayer& L = layers[i];
       if ((L.c == 3) != three) continue;
