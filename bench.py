@@ -1015,6 +1015,8 @@ def bench_kernel_name(instance):
     ms = re.search(r"dw_short<(\d+), \d+, -?\d+>", instance)
     if ms:
         return f"gemm_dw_short_k{2 * int(ms.group(1))}"
+    if "dw_long_kernel" in instance:
+        return "gemm_staged_long_tn"
     if "skinny_nt_kernel" in instance:
         return "gemm_skinny_nt"
     if "smallk_nn_kernel" in instance:

@@ -1525,6 +1525,42 @@ __global__ __launch_bounds__(kThreads) void smallk_nn_kernel(KArgs p) {
   }
 }
 
+// Split-K partials of a weight gradient A^T B (A stored [K][M], B [K][N]) with a small output and a
+// long reduction whose rows miss the direct-load alignment (LeNet-5's first conv layer: 6 x 29
+// outputs over 12544 pixels, rows of 6 floats).  Block z stages k-rows [z * kc, (z + 1) * kc) of both
+// operands in LDS (dynamic, kc * (M + N) floats) and each thread sums its outputs over them in k
+// order, the implicit ones column included; splitk_reduce_kernel adds the slices and runs the
+// epilogue, as for gemm_staged's partials.  Each block reads its rows once, where the tiled kernel's
+// k-loop makes a round trip per 32 rows.
+constexpr int kLongMaxLds = 16384;  // floats
+__global__ __launch_bounds__(256) void dw_long_kernel(KArgs p, float* __restrict__ part, int kc) {
+  extern __shared__ float lds_long[];
+  const int M = p.M, N = p.N, Nt = p.Nt;
+  float* As = lds_long;           // [kc][M]
+  float* Bs = lds_long + kc * M;  // [kc][N]
+  const int k0 = (int)blockIdx.x * kc, nk = max(0, min(p.K, k0 + kc) - k0);
+  for (int i = threadIdx.x; i < nk * M; i += 256) {
+    const int kk = i / M, m = i - kk * M;
+    As[i] = p.A[(int64_t)(k0 + kk) * p.lda + m];
+  }
+  for (int i = threadIdx.x; i < nk * N; i += 256) {
+    const int kk = i / N, n = i - kk * N;
+    Bs[i] = p.B[(int64_t)(k0 + kk) * p.ldb + n];
+  }
+  __syncthreads();
+  const int64_t MN = (int64_t)M * Nt;
+  for (int o = threadIdx.x; o < MN; o += 256) {
+    const int m = o / Nt, n = o - m * Nt;
+    float acc = 0.f;
+    if (n < N) {
+      for (int kk = 0; kk < nk; ++kk) acc += As[kk * M + m] * Bs[kk * N + n];
+    } else {
+      for (int kk = 0; kk < nk; ++kk) acc += As[kk * M + m];
+    }
+    part[(int64_t)blockIdx.x * MN + o] = acc;
+  }
+}
+
 // Sum split-K partial tiles in slice order, then store: the ones column to
 // ones_out, the conv weight gradient permuted, anything else through the
 // epilogue.
@@ -2221,9 +2257,17 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
   a.C = via_partial ? d.partial : d.C;
   a.ldc = via_partial ? a.Nt : d.ldc;
   a.split = via_partial ? 1 : 0;
-  prof_begin(kNames[cfg][form], flops, bytes, s);
-  hipLaunchKernelGGL(staged_fn(cfg, form, via_partial ? EM_GENERIC : epi_mode(d, form)), dim3(a.tiles * splits),
-                     dim3(kThreads), 0, s, a);
+  const int long_kc = (int)ceil_div(d.K, splits);
+  if (via_partial && form == 1 && !d.gather && d.cfg < 0 && d.M <= 64 && d.N <= 64 &&
+      (int64_t)long_kc * (d.M + d.N) <= kLongMaxLds) {
+    prof_begin("gemm_staged_long_tn", flops, bytes, s);
+    hipLaunchKernelGGL(dw_long_kernel, dim3((unsigned)splits), dim3(256),
+                       (size_t)long_kc * (d.M + d.N) * sizeof(float), s, a, d.partial, long_kc);
+  } else {
+    prof_begin(kNames[cfg][form], flops, bytes, s);
+    hipLaunchKernelGGL(staged_fn(cfg, form, via_partial ? EM_GENERIC : epi_mode(d, form)), dim3(a.tiles * splits),
+                       dim3(kThreads), 0, s, a);
+  }
   prof_end(s);
   if (int e = check_launch("gemm")) return e;
   if (via_partial) {

@@ -32,6 +32,8 @@ def test_kernel_code_hash_ignores_comments_not_code(tmp_path, monkeypatch):
 def test_bench_kernel_names():
     assert bench.bench_kernel_name("void sgd::(anonymous namespace)::dw_short<16, 2, 0>(KArgs, ShortArgs)") == \
         "gemm_dw_short_k32"
+    assert bench.bench_kernel_name("sgd::(anonymous namespace)::dw_long_kernel(sgd::(anonymous namespace)::KArgs, "
+                                   "float*, int)") == "gemm_staged_long_tn"
     assert bench.bench_kernel_name("void sgd::(anonymous namespace)::dw_short<8, 1, -1>(KArgs, ShortArgs)") == \
         "gemm_dw_short_k16"
     assert bench.bench_kernel_name(

@@ -36,12 +36,16 @@ U = 2.0 ** -24
 # (4000, 4000) 1024 (or 3969 64 x 64 tiles in the tn form).  With at most 32 valid rows (columns) in a
 # 64-row (64-column) tile the outer wavefronts only load: (32, 2048) on 64 x 128 tiles, (300, 20) on 128 x 64,
 # and (64, 28) on 64 x 64 in the tn form.  Small-batch fc shapes: a batch-16 fc layer's (16, 400, 120) and
-# (16, 120, 84), one row, 32 rows over a ragged 65 columns, odd sizes with padded rows.
+# (16, 120, 84), one row, 32 rows over a ragged 65 columns, odd sizes with padded rows.  Small outputs
+# over long reductions whose rows miss the direct-load alignment take, in the tn form, the staged-in-LDS
+# split-K kernel: LeNet-5's first conv layer's (6, 28, 12544), and (10, 50, 6000) and (21, 40, 8000) with
+# padded rows.
 SHAPES = [(77, 130, 1000, 0), (256, 192, 4096, 0), (128, 128, 30000, 0), (1000, 36, 4, 0), (5, 3, 7, 0),
           (300, 516, 260, 12), (513, 257, 1031, 3), (4096, 64, 576, 0), (200, 1100, 300, 0), (256, 2100, 4096, 0),
           (64, 28, 100000, 0), (48, 60, 5000, 0), (500, 1000, 3000, 0), (1000, 600, 4000, 0), (3900, 3950, 200, 0),
           (4000, 4000, 64, 0), (32, 2048, 3000, 0), (300, 20, 4000, 0), (16, 400, 120, 0), (16, 120, 84, 0),
-          (1, 1000, 128, 0), (32, 65, 128, 0), (7, 129, 33, 5)]
+          (1, 1000, 128, 0), (32, 65, 128, 0), (7, 129, 33, 5), (6, 28, 12544, 0), (10, 50, 6000, 3),
+          (21, 40, 8000, 1)]
 
 
 def stored(seed, tid, rows, cols, pad):
