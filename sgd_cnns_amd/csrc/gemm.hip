@@ -2040,9 +2040,13 @@ bool plain_product(const GemmDesc& d) {
   return d.skinny && !d.gather && !d.ones_out && !d.accum && d.urule < 0 && d.perm_c == 0 && d.M >= 1 && d.N >= 1 &&
          d.K >= 1;
 }
+// A block per row pays a 256-wide reduction tree whatever k is, so many rows over a short k (a 5x5
+// conv layer's 12544 x 6 x 28 forward product as a plain product: 44 us against 8 on the tiles) stay
+// on the tile kernels; a few rows (a logits layer at batch 16: k = 84) still take the row kernel.
 bool skinny_nt_ok(const GemmDesc& d, int form) {
   return form == 0 && plain_product(d) && d.N <= kSkinny && d.K % 4 == 0 && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
-         aligned16(d.A) && aligned16(d.B) && (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RELU);
+         (d.K >= 128 || d.M <= 1024) && aligned16(d.A) && aligned16(d.B) &&
+         (d.epi == EPI_STORE || d.epi == EPI_BIAS || d.epi == EPI_BIAS_RELU);
 }
 // The small-k kernel reloads B's 16 rows for every output row, so it is used for outputs up to 2^20
 // elements (LeNet-5's and VGG-CIFAR's logits dedx: 7.0 -> 6.0 and 10.9 -> 6.6 us); the MLP's 512 x 5000

@@ -124,8 +124,8 @@ def test_gemm_short_reduction_matches_oracle(m, n, k, pad):
 # A logits layer's products on the skinny kernels: the forward form (nt) with at most 16 outputs per row
 # and a k that is a multiple of 4, and the input-gradient form (nn) with a reduction of at most 16, n a
 # multiple of 4 and at most 2^20 outputs (the largest case here is exactly that); C's 4 padding columns must
-# stay untouched.
-SKINNY = [("nt", 512, 10, 5000), ("nt", 16, 10, 84), ("nt", 3, 16, 4), ("nt", 130, 1, 512),
+# stay untouched.  Many rows over a short k, (12544, 6, 28), stay on the tile kernels.
+SKINNY = [("nt", 512, 10, 5000), ("nt", 16, 10, 84), ("nt", 3, 16, 4), ("nt", 130, 1, 512), ("nt", 12544, 6, 28),
           ("nn", 128, 512, 10), ("nn", 16, 84, 10), ("nn", 7, 4, 1), ("nn", 130, 512, 16), ("nn", 1024, 1024, 3)]
 
 
