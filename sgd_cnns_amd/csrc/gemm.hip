@@ -938,9 +938,12 @@ __device__ __forceinline__ void edge_last_coords(int b, int G, int tiles_m, int 
 
 // GA: the A operand is a K-contiguous convolution gather (DmaKg); GB: the B
 // operand is a row-contiguous one (DmaTg).
-template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false, bool PIPE = false>
+// WR: rows of wavefronts (2: a 2 x 2 layout; 1: 1 x 4, each wavefront over all BM rows and a quarter of
+// the columns, for products of at most 32 rows, whose second row of wavefronts would have no rows).
+template <int BM, int BN, bool AT, bool BT, int EM, bool GA = false, bool GB = false, bool PIPE = false, int WR = 2>
 __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WC = 4 / WR;
+  constexpr int WM = BM / WR, WN = BN / WC;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(!(GA && AT) && !(GB && !BT), "gathers: K-contiguous A, row-contiguous B");
   using SA = typename std::conditional<GA, DmaKg<BM>, typename std::conditional<AT, DmaT<BM>, DmaK<BM>>::type>::type;
@@ -960,7 +963,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
   const int tiles_m = p.tiles / p.tiles_n;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // uniform in the wavefront
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WC, wn = wave % WC;
   const int li = lane & 31, lh = lane >> 5;
   f32x16 acc[TM][TN];
 
@@ -1008,9 +1011,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
     const int ones_col = (p.Nt > p.N && p.N >= n0 && p.N < n0 + BN) ? p.N - n0 : -1;
     // The wavefront's 32 x 32 blocks that lie wholly outside the output (in the ragged last tile row
     // or column) skip their matrix-core work: nothing stores them, and the matrix cores they would
-    // occupy are shared with the other resident blocks.  (128 x 128 tiles only: in the narrower
-    // instances the second loop copy costs the registers of a fourth wavefront per SIMD.)
-    constexpr bool kSkip = TM == 2 && TN == 2;
+    // occupy are shared with the other resident blocks.  (128 x 128 tiles, and the 1 x 4 layout, whose
+    // wavefronts all span the tile's rows: a product of at most 32 rows skips their second block.  In
+    // the other narrow instances the second loop copy costs the registers of a fourth wavefront per SIMD.)
+    constexpr bool kSkip = (TM == 2 && TN == 2) || (WR == 1 && TM == 2);
     constexpr bool kPipe = PIPE && kSkip && !AT && EM != EM_UPDATE && EM != EM_GENERIC;
     const int na = kSkip ? __builtin_amdgcn_readfirstlane(min(TM, max(0, (arows - wm * WM + 31) >> 5))) : TM;
     const int nc = kSkip ? __builtin_amdgcn_readfirstlane(min(TN, max(0, (p.Nt - n0 - wn * WN + 31) >> 5))) : TN;
@@ -1215,7 +1219,12 @@ __global__ __launch_bounds__(kThreads) void gemm_dma(KArgs p, SkArgs s) {
         for (int c = 0; c < TN; ++c)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4*>(dst + slot_index<TM, TN>(wave, a, c, q, lane)) =
+            *reinterpret_cast<float4*>(
+                dst + (WR == 2 ? slot_index<TM, TN>(wave, a, c, q, lane)
+                               // the 2 x 2 layout's slot of the same 32 x 32 block (the fixup's)
+                               : slot_index<BM / 64, BN / 64>(((wm * TM + a) / (BM / 64)) * 2 + (wn * TN + c) / (BN / 64),
+                                                              (wm * TM + a) % (BM / 64), (wn * TN + c) % (BN / 64), q,
+                                                              lane))) =
                 make_float4(acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]);
     }
   }
@@ -1705,6 +1714,17 @@ DmaFns dma_fns_of(int form, int em, int gather) {
     default:
       return dma_inst<BM, BN, PIPE, true, false, EM_GENERIC>();
   }
+}
+// 1 x 4 wavefront instances of the 64x128 tile for products of at most 32 rows (fc layers at a small
+// batch): forward (bias) and input-gradient (mask) forms, and plain stores; nullptr otherwise.
+DmaFns dma_fns_rows1(int form, int em, int gather) {
+  constexpr DmaFns none{nullptr, nullptr, 0, 0};
+  if (gather) return none;
+  if (form == 0 && em == EM_BIAS) return {gemm_dma<64, 128, false, false, EM_BIAS, false, false, false, 1>, gemm_sk_fixup<64, 128>, 64, 128};
+  if (form == 0 && em == EM_STORE) return {gemm_dma<64, 128, false, false, EM_STORE, false, false, false, 1>, gemm_sk_fixup<64, 128>, 64, 128};
+  if (form == 2 && em == EM_MASK) return {gemm_dma<64, 128, false, true, EM_MASK, false, false, false, 1>, gemm_sk_fixup<64, 128>, 64, 128};
+  if (form == 2 && em == EM_STORE) return {gemm_dma<64, 128, false, true, EM_STORE, false, false, false, 1>, gemm_sk_fixup<64, 128>, 64, 128};
+  return none;
 }
 // 64x64 is instantiated for the one product dma_cfg gives it: dedw (A^T B,
 // not gathered); anything else gets no kernel.
@@ -2212,8 +2232,11 @@ int gemm_launch(const GemmDesc& d, hipStream_t s) {
     // The pipelined instances (two blocks per CU) for schedules of at most two blocks per CU, except
     // beside the side stream's products: there they made VGG-16's step 0.4% slower (same-box A/B), the
     // MLP's and VGG-CIFAR's no faster.
-    const DmaFns f = dma_fns(cfg, form, epi_mode(d, form), d.gather,
-                             pipe_slices && !d.beside_side && cfg == 0 && plan.grid <= 2 * machine_for(cfg).cus);
+    DmaFns f{nullptr, nullptr, 0, 0};
+    if (cfg == 2 && d.M <= 32) f = dma_fns_rows1(form, epi_mode(d, form), d.gather);
+    if (!f.main)
+      f = dma_fns(cfg, form, epi_mode(d, form), d.gather,
+                  pipe_slices && !d.beside_side && cfg == 0 && plan.grid <= 2 * machine_for(cfg).cus);
     if (!f.main) {
       set_error("gemm: no 64x64 kernel for this product form");
       return SGD_EINVAL;

@@ -34,9 +34,11 @@ U = 2.0 ** -24
 # (500, 1000), and 8 x 1 in (1000, 600).  One block per tile over more tiles than resident blocks, with a
 # ragged last tile row and column, puts the edge tiles last: (3900, 3950) has 961 tiles (no XCD runs),
 # (4000, 4000) 1024 (or 3969 64 x 64 tiles in the tn form).  With at most 32 valid rows (columns) in a
-# 64-row (64-column) tile the outer wavefronts only load: (32, 2048) on 64 x 128 tiles, (300, 20) on 128 x 64,
-# and (64, 28) on 64 x 64 in the tn form.  Small-batch fc shapes: a batch-16 fc layer's (16, 400, 120) and
-# (16, 120, 84), one row, 32 rows over a ragged 65 columns, odd sizes with padded rows.  Small outputs
+# 64-row (64-column) tile the outer wavefronts only load: (300, 20) on 128 x 64, and (64, 28) on 64 x 64 in the
+# tn form; in the nt and nn forms, products of at most 32 rows on 64 x 128 tiles take the 1 x 4 wavefront
+# layout (every wavefront over the tile's rows, the empty second row block skipped): (32, 2048), a batch-16
+# fc layer's (16, 400, 120) and (16, 120, 84), one row, 32 rows over a ragged 65 columns (the tt and tn forms
+# keep the 2 x 2 layout with idle outer wavefronts), odd sizes with padded rows.  Small outputs
 # over long reductions whose rows miss the direct-load alignment take, in the tn form, the staged-in-LDS
 # split-K kernel: LeNet-5's first conv layer's (6, 28, 12544), and (10, 50, 6000) and (21, 40, 8000) with
 # padded rows.
