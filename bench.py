@@ -1022,7 +1022,7 @@ def bench_kernel_name(instance):
     if "smallk_nn_kernel" in instance:
         return "gemm_smallk_nn"
     m = re.search(r"gemm_(dma|staged)<(\d+), (\d+), (?:(\d+), )?(true|false), (true|false), (\d+)"
-                  r"(?:, (true|false), (true|false))?(?:, (?:true|false))?>", instance)
+                  r"(?:, (true|false), (true|false))?(?:, (?:true|false))?(?:, \d+)?>", instance)
     if not m:
         return short_instance(instance).split("<")[0]
     fam, bm, bn, _bk, at, bt, em, ga, gb = m.groups()

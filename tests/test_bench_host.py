@@ -30,6 +30,16 @@ def test_kernel_code_hash_ignores_comments_not_code(tmp_path, monkeypatch):
 
 
 def test_bench_kernel_names():
+    # the trailing template arguments of the kernel (pipelined loop, wavefront rows) do not change the name
+    assert bench.bench_kernel_name(
+        "void sgd::(anonymous namespace)::gemm_dma<128, 128, true, true, 5, false, true, false, 2>(KArgs, SkArgs)") == \
+        "gemm_conv_dw_128x128"
+    assert bench.bench_kernel_name(
+        "void sgd::(anonymous namespace)::gemm_dma<64, 128, false, true, 3, false, false, false, 1>(KArgs, SkArgs)") \
+        == "gemm_dma_64x128_nn"
+    assert bench.bench_kernel_name(
+        "void sgd::(anonymous namespace)::gemm_dma<128, 128, false, false, 2, false, false, true, 2>(KArgs, SkArgs)") \
+        == "gemm_dma_128x128_nt"
     assert bench.bench_kernel_name("void sgd::(anonymous namespace)::dw_short<16, 2, 0>(KArgs, ShortArgs)") == \
         "gemm_dw_short_k32"
     assert bench.bench_kernel_name("sgd::(anonymous namespace)::dw_long_kernel(sgd::(anonymous namespace)::KArgs, "
