@@ -60,3 +60,23 @@ def test_bench_kernel_names():
         "void sgd::(anonymous namespace)::gemm_dma<128, 128, false, false, 2, false, false, false>(KArgs, SkArgs)") == \
         "gemm_dma_128x128_nt"
     assert bench.is_product("gemm_dw_short_k32") and not bench.is_product("softmax_ce")
+
+
+def test_committed_traffic_records_name_each_dominant_kernel():
+    """The committed counter record keys each kernel by the library's own name, so the bench line can
+    attach HBM traffic to the dominant kernel it times (an instance that the name mapping misses would
+    be filed under a bare template name)."""
+    import json
+    import os
+    recs = json.load(open(os.path.join(bench.ROOT, "profiles", "traffic.json")))
+    dominant = {"mlp5000": "gemm_dma_128x128_tn", "vgg16": "gemm_conv_dw_128x128",
+                "vgg_cifar": "gemm_conv_dw_128x128", "ps_adagrad": "apply_kernel<2, 8>"}
+    seen = set()
+    for r in recs:
+        kernels = r["kernels"]
+        assert not {"gemm_dma", "gemm_staged"} & set(kernels), f"unmapped instance names in {r['workload']}"
+        if r["workload"] in dominant:
+            assert dominant[r["workload"]] in kernels
+            assert kernels[dominant[r["workload"]]]["traffic_bytes"] > 0
+            seen.add(r["workload"])
+    assert seen == set(dominant)
